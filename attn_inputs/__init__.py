@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for exact attention, shared by the oracle and the HIP path.
+
+This module only *draws* data: it holds none of the attention arithmetic.  Both the
+CPU oracle (``oracle/``) and the GPU side (tests, ``bench.py``) take their inputs from
+here, so the two sides see bit-identical operands.
+
+Recipe (the workloads of the paged-decode and prefill benchmarks described on the
+mlx-mfa pages, "Performance" table, and the MXFlashAttn paged Split-KV decode page):
+
+* ``numpy.random.default_rng(seed)`` (PCG64).
+* Dense prefill: draw Q, K, V in that order as ``standard_normal(shape, float32)``
+  with Q ``[B, Hq, Nq, D]`` and K, V ``[B, Hkv, Nk, D]`` (the ``[B, H, N, D]``
+  row-major layout of the mlx-mfa "Supported Configurations" table).
+* Rounding to the storage type: fp16 by numpy's cast (round to nearest even);
+  bf16 by round-to-nearest-even on the float32 bit pattern.  Arrays are returned as
+  ``uint16`` bit patterns so that no later cast can perturb them.
+* Paged decode: draw order is ``seq_lens`` (uniform integers in ``[len_lo, len_hi]``),
+  then a permutation of the page pool, then q ``[B, Hq, D]``, then the K tokens and
+  the V tokens of every sequence in order (``[sum(L_b), Hkv, D]`` each).  The pool
+  holds ``P = sum(ceil(L_b / page_size))`` pages plus ``extra_pages`` unused ones;
+  the permutation is dealt to the sequences in order, so page ``j`` of sequence
+  ``b`` is ``block_table[b, j]``.  Token ``t`` of sequence ``b`` is stored at
+  ``(block_table[b, t // page_size], t % page_size)`` of the pool
+  ``[num_pages, page_size, Hkv, D]``.  Unused block-table entries are -1; tail slots
+  of each sequence's last page and every unused page hold NaN, so that a kernel
+  which reads them is caught.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+NAN_BITS = {F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0)}
+
+
+def round_f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a float32 array to fp16 or bf16 (nearest, ties to even); return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F16:
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        u = x.view(np.uint32)
+        # round-to-nearest-even on the upper 16 bits; NaNs are kept quiet NaNs
+        rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        out = ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+        nan = np.isnan(x)
+        if nan.any():
+            out[nan] = NAN_BITS[BF16]
+        return out
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _normal_bits(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return round_f32_to_bits(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+@dataclass
+class DenseInputs:
+    q: np.ndarray  # uint16 bits [B, Hq, Nq, D]
+    k: np.ndarray  # uint16 bits [B, Hkv, Nk, D]
+    v: np.ndarray  # uint16 bits [B, Hkv, Nk, D]
+    dtype: str
+
+
+def dense_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, dtype: str,
+                 seed: int) -> DenseInputs:
+    rng = np.random.default_rng(seed)
+    q = _normal_bits(rng, (B, Hq, Nq, D), dtype)
+    k = _normal_bits(rng, (B, Hkv, Nk, D), dtype)
+    v = _normal_bits(rng, (B, Hkv, Nk, D), dtype)
+    return DenseInputs(q, k, v, dtype)
+
+
+@dataclass
+class PagedInputs:
+    q: np.ndarray            # uint16 bits [B, Hq, D]
+    k_pages: np.ndarray      # uint16 bits [num_pages, page_size, Hkv, D]
+    v_pages: np.ndarray      # uint16 bits [num_pages, page_size, Hkv, D]
+    block_table: np.ndarray  # int32 [B, max_pages_per_seq], -1 where unused
+    seq_lens: np.ndarray     # int32 [B]
+    page_size: int
+    dtype: str
+    pages_used: int = field(default=0)
+
+
+def paged_inputs(B: int, Hq: int, Hkv: int, D: int, dtype: str, seed: int, *,
+                 len_lo: int, len_hi: int, page_size: int = 16,
+                 max_pages_per_seq: int | None = None, extra_pages: int = 0,
+                 seq_lens=None) -> PagedInputs:
+    """Paged KV pool with a seeded random page permutation (see module docstring).
+
+    ``seq_lens`` may be given explicitly (still consuming no random draws for them).
+    """
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        seq_lens = rng.integers(len_lo, len_hi, endpoint=True, size=B)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    assert seq_lens.shape == (B,)
+    pages_per_seq = [int(math.ceil(int(L) / page_size)) for L in seq_lens]
+    used = int(sum(pages_per_seq))
+    num_pages = used + int(extra_pages)
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, int(math.ceil(len_hi / page_size)))
+    if max(pages_per_seq, default=0) > max_pages_per_seq:
+        raise ValueError("max_pages_per_seq too small for the drawn sequence lengths")
+    perm = rng.permutation(num_pages).astype(np.int64)
+    q = _normal_bits(rng, (B, Hq, D), dtype)
+    total = int(seq_lens.sum())
+    k_tok = _normal_bits(rng, (total, Hkv, D), dtype)
+    v_tok = _normal_bits(rng, (total, Hkv, D), dtype)
+
+    block_table = np.full((B, max_pages_per_seq), -1, dtype=np.int32)
+    k_pages = np.full((num_pages, page_size, Hkv, D), NAN_BITS[dtype], dtype=np.uint16)
+    v_pages = np.full((num_pages, page_size, Hkv, D), NAN_BITS[dtype], dtype=np.uint16)
+    cursor = 0
+    tok0 = 0
+    for b in range(B):
+        n = pages_per_seq[b]
+        pages = perm[cursor:cursor + n]
+        cursor += n
+        block_table[b, :n] = pages
+        L = int(seq_lens[b])
+        # scatter the sequence's tokens page by page
+        for j in range(n):
+            t0 = j * page_size
+            t1 = min(L, t0 + page_size)
+            k_pages[pages[j], : t1 - t0] = k_tok[tok0 + t0: tok0 + t1]
+            v_pages[pages[j], : t1 - t0] = v_tok[tok0 + t0: tok0 + t1]
+        tok0 += L
+    return PagedInputs(q, k_pages, v_pages, block_table, seq_lens.astype(np.int32),
+                       page_size, dtype, used)
+
+
+# The five benchmark workloads.  Shapes follow the mlx-mfa "Performance" table
+# (B=2, H=8, f16, D=128, causal / window 512), its GQA statement (Hq a multiple of
+# Hkv), and the MXFlashAttn paged split-KV decode setting (pages of 16 tokens,
+# Hq=32, Hkv=8, D=128).
+CONFIGS = {
+    1: dict(name="tiny_dense", B=1, Hq=2, Hkv=2, Nq=128, Nk=128, D=64, dtype=F16,
+            causal=False, left=-1, right=-1, seed=101),
+    2: dict(name="dense_causal_prefill", B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128,
+            dtype=F16, causal=True, left=-1, right=-1, seed=102),
+    3: dict(name="gqa_causal_long_prefill", B=1, Hq=32, Hkv=8, Nq=16384, Nk=16384,
+            D=128, dtype=BF16, causal=True, left=-1, right=-1, seed=103),
+    4: dict(name="sliding_window_causal", B=2, Hq=8, Hkv=8, Nq=8192, Nk=8192, D=128,
+            dtype=F16, causal=True, left=512, right=0, seed=104),
+    5: dict(name="paged_splitkv_decode", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
+            page_size=16, len_lo=1024, len_hi=32768, seed=105),
+}
+
+
+def config(i: int) -> dict:
+    c = dict(CONFIGS[i])
+    c["scale"] = 1.0 / math.sqrt(c["D"])
+    return c
+
+
+def config_inputs(i: int):
+    c = config(i)
+    if i == 5:
+        return paged_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"],
+                            len_lo=c["len_lo"], len_hi=c["len_hi"],
+                            page_size=c["page_size"])
+    return dense_inputs(c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"], c["dtype"],
+                        c["seed"])

@@ -1,0 +1,235 @@
+"""Float64 reference for exact attention (test infrastructure; see ``oracle/__init__``).
+
+Notation follows the pages: Q ``[B, Hq, Nq, D]``, K/V ``[B, Hkv, Nk, D]``, grouped
+query heads ``g = Hq / Hkv`` with query head ``h`` reading KV head ``h // g``
+(mlx-bun forward shader, head mapping; mlx-mfa "Native GQA").
+
+Readings taken where the pages leave a point open (each is listed in the design doc):
+
+* Window ``(left, right)``, ``-1`` = unbounded (mlx-mfa "Sliding window" feature):
+  key ``j`` is visible to query ``i`` iff ``i+off-left <= j <= i+off+right``,
+  both ends inclusive.
+* Causal alignment is bottom-right: ``off = Nk - Nq``; key ``j`` is visible under
+  the causal mask iff ``j <= i + off``.  For ``Nq == Nk`` this is the mlx-bun
+  shader's ``kpos > q_row`` rule.
+* A row with no visible key returns ``O = 0`` and ``LSE = -inf``.
+* The LSE is the natural log of the sum of ``exp`` of the *scaled* scores.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_BF16 = "bf16"
+_F16 = "f16"
+
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of fp16 / bf16 storage given as uint16 bit patterns."""
+    bits = np.asarray(bits)
+    if bits.dtype != np.uint16:
+        raise TypeError("expected uint16 bit patterns")
+    if dtype == _F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == _BF16:
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def window_bounds(i, Nq: int, Nk: int, causal: bool, left: int, right: int):
+    """Inclusive visible key range ``[lo, hi]`` of query row(s) ``i`` (may be empty)."""
+    i = np.asarray(i, dtype=np.int64)
+    off = Nk - Nq
+    lo = np.zeros_like(i)
+    if left >= 0:
+        lo = np.maximum(lo, i + off - left)
+    hi = np.full_like(i, Nk - 1)
+    if causal:
+        hi = np.minimum(hi, i + off)
+    if right >= 0:
+        hi = np.minimum(hi, i + off + right)
+    return lo, hi
+
+
+def visible(i, j, Nq: int, Nk: int, causal: bool, left: int, right: int):
+    """Boolean visibility of key ``j`` to query ``i`` (broadcasting)."""
+    i, j = np.broadcast_arrays(np.asarray(i, dtype=np.int64), np.asarray(j, dtype=np.int64))
+    off = Nk - Nq
+    ok = (j >= 0) & (j < Nk)
+    if causal:
+        ok = ok & (j <= i + off)
+    if left >= 0:
+        ok = ok & (j >= i + off - left)
+    if right >= 0:
+        ok = ok & (j <= i + off + right)
+    return ok
+
+
+def _rows_attention(qr, kk, vv, scale, vis):
+    """Definition of attention for a block of rows.
+
+    qr ``[r, D]``, kk/vv ``[Nk, D]``, vis ``[r, Nk]`` bool.  Returns O ``[r, D]``,
+    LSE ``[r]``, P ``[r, Nk]``.
+    """
+    s = scale * (qr @ kk.T)
+    s = np.where(vis, s, -np.inf)
+    any_vis = vis.any(axis=1)
+    m = np.where(any_vis, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.exp(s - m[:, None])          # exp(-inf) = 0 at masked positions
+    z = e.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(any_vis[:, None], e / np.where(any_vis, z, 1.0)[:, None], 0.0)
+        lse = np.where(any_vis, m + np.log(np.where(any_vis, z, 1.0)), -np.inf)
+    o = p @ vv
+    return o, lse, p
+
+
+def attention(q, k, v, scale: float, causal: bool = False, left: int = -1,
+              right: int = -1, rows=None, row_block: int = 512):
+    """O = softmax(scale·QKᵀ + mask)·V and LSE, in float64.
+
+    q ``[B, Hq, Nq, D]``, k/v ``[B, Hkv, Nk, D]`` (float64 or anything numpy widens
+    exactly).  ``rows`` optionally restricts the computation to a list of
+    ``(b, h, i)`` triples; then the result is ``(O [n, D], LSE [n])`` in that order.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    cols = np.arange(Nk)
+    if rows is not None:
+        rows = list(rows)
+        O = np.zeros((len(rows), D))
+        L = np.zeros(len(rows))
+        for n, (b, h, i) in enumerate(rows):
+            kv = h // g
+            vis = visible(np.array([[i]]), cols[None, :], Nq, Nk, causal, left, right)
+            o, lse, _ = _rows_attention(q[b, h, i][None, :], k[b, kv], v[b, kv], scale, vis)
+            O[n] = o[0]
+            L[n] = lse[0]
+        return O, L
+    O = np.zeros((B, Hq, Nq, D))
+    L = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            for r0 in range(0, Nq, row_block):
+                r1 = min(Nq, r0 + row_block)
+                ii = np.arange(r0, r1)
+                vis = visible(ii[:, None], cols[None, :], Nq, Nk, causal, left, right)
+                o, lse, _ = _rows_attention(q[b, h, r0:r1], k[b, kv], v[b, kv], scale, vis)
+                O[b, h, r0:r1] = o
+                L[b, h, r0:r1] = lse
+    return O, L
+
+
+def attention_probs(q, k, scale: float, causal=False, left=-1, right=-1):
+    """The probability matrix P ``[B, Hq, Nq, Nk]`` (small sizes only)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    P = np.zeros((B, Hq, Nq, Nk))
+    ii = np.arange(Nq)[:, None]
+    jj = np.arange(Nk)[None, :]
+    vis = visible(ii, jj, Nq, Nk, causal, left, right)
+    for b in range(B):
+        for h in range(Hq):
+            _, _, p = _rows_attention(q[b, h], k[b, h // g], np.zeros((Nk, 1)), scale, vis)
+            P[b, h] = p
+    return P
+
+
+def gather_paged(pages: np.ndarray, block_table: np.ndarray, b: int, L: int,
+                 page_size: int) -> np.ndarray:
+    """The first ``L`` tokens of sequence ``b`` from a ``[P, page_size, Hkv, D]`` pool.
+
+    Token ``t`` sits at page ``block_table[b, t // page_size]``, slot
+    ``t % page_size`` (the paged-cache addressing of the MXFlashAttn decode page).
+    """
+    out = np.empty((L,) + pages.shape[2:], dtype=pages.dtype)
+    for t in range(L):
+        page = int(block_table[b, t // page_size])
+        if page < 0 or page >= pages.shape[0]:
+            raise IndexError(f"block_table[{b}, {t // page_size}] = {page} out of range")
+        out[t] = pages[page, t % page_size]
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float,
+                 page_size: int):
+    """Single-token decode over a paged KV cache, float64.
+
+    q ``[B, Hq, D]``; pools ``[P, page_size, Hkv, D]`` (float64 values); every cached
+    token of sequence ``b`` (``seq_lens[b]`` of them) is visible.  Returns O
+    ``[B, Hq, D]`` and LSE ``[B, Hq]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_pages.shape[2]
+    g = Hq // Hkv
+    O = np.zeros((B, Hq, D))
+    L = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        kb = gather_paged(k_pages, block_table, b, n, page_size)  # [n, Hkv, D]
+        vb = gather_paged(v_pages, block_table, b, n, page_size)
+        for h in range(Hq):
+            kv = h // g
+            vis = np.ones((1, n), dtype=bool)
+            o, lse, _ = _rows_attention(q[b, h][None, :], kb[:, kv], vb[:, kv], scale, vis)
+            O[b, h] = o[0]
+            L[b, h] = lse[0]
+    return O, L
+
+
+def lse_merge(parts):
+    """Combine partial results over a partition of the keys.
+
+    ``parts`` is a list of ``(O_s, LSE_s)`` where ``O_s`` is the normalised output of
+    attention restricted to key subset ``s`` and ``LSE_s`` its log-sum-exp (``-inf``
+    for an empty subset).  With ``M = max_s LSE_s`` and ``w_s = exp(LSE_s - M)``,
+    the full result is ``O = sum_s w_s O_s / sum_s w_s`` and
+    ``LSE = M + log(sum_s w_s)``.
+    """
+    lses = np.stack([np.asarray(p[1], dtype=np.float64) for p in parts])
+    outs = np.stack([np.asarray(p[0], dtype=np.float64) for p in parts])
+    M = lses.max(axis=0)
+    finite = np.isfinite(M)
+    Ms = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - Ms), 0.0)
+    W = w.sum(axis=0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        O = (w[..., None] * outs).sum(axis=0) / np.where(W > 0, W, 1.0)[..., None]
+        lse = np.where(W > 0, Ms + np.log(np.where(W > 0, W, 1.0)), -np.inf)
+    return np.where((W > 0)[..., None], O, 0.0), lse
+
+
+def visited_tiles(Nq: int, Nk: int, BM: int, BN: int, causal: bool, left: int,
+                  right: int):
+    """For each query tile, the sorted key-tile indices with >= 1 visible pair.
+
+    Brute force over every ``(i, j)`` with ``i < Nq`` and ``j < Nk``.
+    """
+    n_qt = math.ceil(Nq / BM)
+    n_kt = math.ceil(Nk / BN)
+    out = []
+    ii = np.arange(Nq)[:, None]
+    jj = np.arange(Nk)[None, :]
+    vis = visible(ii, jj, Nq, Nk, causal, left, right)
+    for qt in range(n_qt):
+        blk = vis[qt * BM: min(Nq, (qt + 1) * BM)]
+        cols = blk.any(axis=0)
+        tiles = [kt for kt in range(n_kt) if cols[kt * BN: min(Nk, (kt + 1) * BN)].any()]
+        out.append(tiles)
+    return out

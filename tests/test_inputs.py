@@ -1,0 +1,56 @@
+"""The seeded generator: determinism, rounding and the paged layout.  CPU only."""
+import numpy as np
+import pytest
+
+import attn_inputs as A
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [np.inf, -np.inf, 0.0, -0.0]
+    ours = A.round_f32_to_bits(x, "bf16")
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    assert A.round_f32_to_bits(np.array([np.nan], np.float32), "bf16")[0] == 0x7FC0
+
+
+def test_f16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 300
+    ours = A.round_f32_to_bits(x, "f16")
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_dense_deterministic():
+    a = A.dense_inputs(1, 2, 1, 5, 7, 8, "bf16", 3)
+    b = A.dense_inputs(1, 2, 1, 5, 7, 8, "bf16", 3)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)):
+        np.testing.assert_array_equal(x, y)
+    assert a.q.shape == (1, 2, 5, 8) and a.k.shape == (1, 1, 7, 8)
+
+
+def test_paged_layout():
+    p = A.paged_inputs(4, 4, 2, 16, "f16", 9, len_lo=1, len_hi=70, extra_pages=2)
+    assert p.block_table.dtype == np.int32 and p.seq_lens.dtype == np.int32
+    used = np.concatenate([p.block_table[b, : -(-int(L) // 16)] for b, L in enumerate(p.seq_lens)])
+    # every page is dealt to at most one sequence, all in range
+    assert len(set(used.tolist())) == len(used) and used.min() >= 0
+    assert used.max() < p.k_pages.shape[0]
+    for b, L in enumerate(p.seq_lens):
+        n = -(-int(L) // 16)
+        assert np.all(p.block_table[b, n:] == -1)
+        tail = int(L) - 16 * (n - 1)
+        last = p.block_table[b, n - 1]
+        assert np.all(p.k_pages[last, tail:] == A.NAN_BITS["f16"])
+        assert not np.any(p.k_pages[last, :tail] == A.NAN_BITS["f16"])
+    unused = sorted(set(range(p.k_pages.shape[0])) - set(used.tolist()))
+    assert len(unused) == 2
+    assert np.all(p.v_pages[unused] == A.NAN_BITS["f16"])
+
+
+def test_config5_shape():
+    c = A.config(5)
+    assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (16, 32, 8, 128, 16)
+    assert abs(c["scale"] - 128 ** -0.5) < 1e-15

@@ -1,0 +1,360 @@
+"""Pins for the CPU oracle: closed forms, invariants, an independent scalar
+implementation and PyTorch's float64 attention routine.  CPU only.
+
+Each ``pin_*`` function raises AssertionError on a mismatch; the tests call them on
+the real oracle, and ``test_planted_mistakes`` plants plausible mistakes into the
+oracle (on the CPU) to show that some pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import attn_inputs as A
+import oracle
+import oracle.reference as OA
+from oracle.scalar import attention_scalar, logsumexp_scalar
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _fsum_dot(a, b):
+    return math.fsum(float(x) * float(y) for x, y in zip(a, b))
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_golden():
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        q, k, v = (np.array(c[n], dtype=np.float64) for n in ("q", "k", "v"))
+        O, L = oracle.attention(q, k, v, c["scale"], c["causal"], c["left"], c["right"])
+        np.testing.assert_allclose(O, np.array(c["O"]), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L, np.array(c["LSE"]), rtol=0, atol=1e-14)
+
+
+def pin_single_key():
+    # Nk = 1: O = V[0] and LSE = scale * q.k0 (closed form), for every query row
+    q, k, v = _rand((2, 4, 3, 8), 1), _rand((2, 2, 1, 8), 2), _rand((2, 2, 1, 8), 3)
+    scale = 0.37
+    O, L = oracle.attention(q, k, v, scale, causal=False)
+    for b in range(2):
+        for h in range(4):
+            for i in range(3):
+                assert np.allclose(O[b, h, i], v[b, h // 2, 0], atol=1e-13)
+                assert abs(L[b, h, i] - scale * _fsum_dot(q[b, h, i], k[b, h // 2, 0])) < 1e-12
+
+
+def pin_identical_keys():
+    # all keys equal: every visible key has the same score s, so O is the plain mean of
+    # the visible V rows and LSE = s + log(n_visible).  With causal + window (left=3),
+    # row i sees keys max(0, i-3) .. i (inclusive reading): n = min(i, 3) + 1.
+    Nq = Nk = 10
+    q = _rand((1, 1, Nq, 4), 4)
+    k = np.broadcast_to(_rand((1, 1, 1, 4), 5), (1, 1, Nk, 4)).copy()
+    v = _rand((1, 1, Nk, 4), 6)
+    scale = 0.5
+    O, L = oracle.attention(q, k, v, scale, causal=True, left=3, right=0)
+    for i in range(Nq):
+        lo = max(0, i - 3)
+        n = i - lo + 1
+        s = scale * _fsum_dot(q[0, 0, i], k[0, 0, 0])
+        mean = [math.fsum(v[0, 0, j, d] for j in range(lo, i + 1)) / n for d in range(4)]
+        assert np.allclose(O[0, 0, i], mean, atol=1e-13), i
+        assert abs(L[0, 0, i] - (s + math.log(n))) < 1e-12, i
+
+
+def pin_causal_row0():
+    q, k, v = _rand((1, 2, 6, 8), 7), _rand((1, 2, 6, 8), 8), _rand((1, 2, 6, 8), 9)
+    O, L = oracle.attention(q, k, v, 0.3, causal=True)
+    for h in range(2):
+        assert np.allclose(O[0, h, 0], v[0, h, 0], atol=1e-14)
+        assert abs(L[0, h, 0] - 0.3 * _fsum_dot(q[0, h, 0], k[0, h, 0])) < 1e-12
+
+
+def pin_probs_sum_to_one():
+    q, k = _rand((1, 2, 7, 5), 10), _rand((1, 1, 9, 5), 11)
+    for causal, left, right in [(False, -1, -1), (True, -1, -1), (True, 2, 0), (False, 1, 1)]:
+        P = oracle.attention_probs(q, k, 0.7, causal, left, right)
+        s = P.sum(axis=-1)
+        assert np.all(np.abs(s - 1.0) < 1e-12)
+        assert np.all(P >= 0)
+
+
+def pin_lse_bruteforce():
+    # LSE against a pure-Python log-sum-exp of the visible scaled scores
+    q, k, v = _rand((1, 2, 5, 6), 12), _rand((1, 2, 8, 6), 13), _rand((1, 2, 8, 6), 14)
+    scale = 0.8
+    _, L = oracle.attention(q, k, v, scale, causal=True)
+    off = 8 - 5
+    for h in range(2):
+        for i in range(5):
+            vals = [scale * _fsum_dot(q[0, h, i], k[0, h, j]) for j in range(i + off + 1)]
+            assert abs(L[0, h, i] - logsumexp_scalar(vals)) < 1e-12
+
+
+def pin_scalar_oracle():
+    # independent pure-Python implementation on tiny inputs, GQA, Nq != Nk, all masks
+    q, k, v = _rand((2, 4, 5, 3), 15), _rand((2, 2, 7, 3), 16), _rand((2, 2, 7, 3), 17)
+    for causal, left, right in [(False, -1, -1), (True, -1, -1), (True, 2, 0), (False, 1, 2),
+                                (True, 0, 0), (False, -1, 1)]:
+        O, L = oracle.attention(q, k, v, 0.9, causal, left, right)
+        Os, Ls = attention_scalar(q.tolist(), k.tolist(), v.tolist(), 0.9, causal, left, right)
+        np.testing.assert_allclose(O, np.array(Os), atol=1e-13, rtol=0)
+        np.testing.assert_array_equal(np.isinf(L), np.isinf(np.array(Ls)))
+        fin = np.isfinite(L)
+        np.testing.assert_allclose(L[fin], np.array(Ls)[fin], atol=1e-13, rtol=0)
+
+
+def pin_wide_window_is_full():
+    q, k, v = _rand((1, 2, 9, 4), 18), _rand((1, 2, 9, 4), 19), _rand((1, 2, 9, 4), 20)
+    for causal in (False, True):
+        O0, L0 = oracle.attention(q, k, v, 0.5, causal)
+        O1, L1 = oracle.attention(q, k, v, 0.5, causal, left=9, right=9)
+        O2, L2 = oracle.attention(q, k, v, 0.5, causal, left=100, right=-1)
+        for O, L in ((O1, L1), (O2, L2)):
+            np.testing.assert_array_equal(O, O0)
+            np.testing.assert_array_equal(L, L0)
+
+
+def pin_zero_window_is_identity():
+    # (left=0, right=0): each row sees only key i+off -> O_i = V_{i+off}
+    q, k, v = _rand((1, 1, 4, 5), 21), _rand((1, 1, 6, 5), 22), _rand((1, 1, 6, 5), 23)
+    O, L = oracle.attention(q, k, v, 1.1, causal=False, left=0, right=0)
+    for i in range(4):
+        assert np.allclose(O[0, 0, i], v[0, 0, i + 2], atol=1e-14)
+        assert abs(L[0, 0, i] - 1.1 * _fsum_dot(q[0, 0, i], k[0, 0, i + 2])) < 1e-12
+
+
+def pin_gqa_is_repeated_mha():
+    q, k, v = _rand((2, 6, 5, 4), 24), _rand((2, 2, 7, 4), 25), _rand((2, 2, 7, 4), 26)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)  # head h reads kv h // 3
+    for causal in (False, True):
+        O0, L0 = oracle.attention(q, k, v, 0.6, causal)
+        O1, L1 = oracle.attention(q, kr, vr, 0.6, causal)
+        np.testing.assert_array_equal(O0, O1)
+        np.testing.assert_array_equal(L0, L1)
+
+
+def pin_affine_v():
+    q, k, v = _rand((1, 2, 6, 4), 27), _rand((1, 2, 6, 4), 28), _rand((1, 2, 6, 4), 29)
+    c = np.array([0.5, -1.0, 2.0, 3.0])
+    O0, L0 = oracle.attention(q, k, v, 0.4, True)
+    O1, L1 = oracle.attention(q, k, 2.5 * v + c, 0.4, True)
+    np.testing.assert_allclose(O1, 2.5 * O0 + c, atol=1e-12)
+    np.testing.assert_array_equal(L0, L1)
+
+
+def pin_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v = _rand((2, 3, 33, 16), 30), _rand((2, 3, 33, 16), 31), _rand((2, 3, 33, 16), 32)
+    for causal in (False, True):
+        O, _ = oracle.attention(q, k, v, 0.25, causal)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                             torch.from_numpy(v), is_causal=causal, scale=0.25)
+        np.testing.assert_allclose(O, ref.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_fully_masked_rows():
+    # causal with Nq > Nk: rows i < Nq - Nk see nothing -> O = 0, LSE = -inf
+    q, k, v = _rand((1, 1, 6, 3), 33), _rand((1, 1, 2, 3), 34), _rand((1, 1, 2, 3), 35)
+    O, L = oracle.attention(q, k, v, 1.0, causal=True)
+    assert np.all(O[0, 0, :4] == 0.0) and np.all(np.isneginf(L[0, 0, :4]))
+    assert np.allclose(O[0, 0, 4], v[0, 0, 0]) and np.all(np.isfinite(L[0, 0, 4:]))
+
+
+def pin_lse_merge_identity():
+    # merging attention over any partition of the keys equals the one-shot result
+    q, k, v = _rand((1, 2, 3, 5), 36), _rand((1, 2, 20, 5), 37), _rand((1, 2, 20, 5), 38)
+    O, L = oracle.attention(q, k, v, 0.7)
+    for cuts in ([0, 7, 20], [0, 1, 2, 3, 20], [0, 20], [0, 5, 5, 12, 20]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if a == b:
+                parts.append((np.zeros_like(O), np.full_like(L, -np.inf)))  # empty split
+            else:
+                parts.append(oracle.attention(q, k[:, :, a:b], v[:, :, a:b], 0.7))
+        Om, Lm = oracle.lse_merge(parts)
+        np.testing.assert_allclose(Om, O, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(Lm, L, atol=1e-12, rtol=0)
+
+
+def pin_decode_paged():
+    # paged decode equals (i) attention on the contiguous tokens and (ii) the last row
+    # of causal prefill over the same tokens; and is invariant to the page permutation
+    p = A.paged_inputs(3, 4, 2, 8, "f16", 40, len_lo=1, len_hi=50, extra_pages=3)
+    kp, vp, q = (oracle.widen(x, "f16") for x in (p.k_pages, p.v_pages, p.q))
+    O, L = oracle.decode_paged(q, kp, vp, p.block_table, p.seq_lens, 0.3, p.page_size)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    # rebuild the contiguous tokens from the generator's own draw order
+    rng = np.random.default_rng(40)
+    rng.integers(1, 50, endpoint=True, size=3)
+    total_pages = p.pages_used + 3
+    rng.permutation(total_pages)
+    A._normal_bits(rng, (3, 4, 8), "f16")
+    tot = int(p.seq_lens.sum())
+    kt = oracle.widen(A._normal_bits(rng, (tot, 2, 8), "f16"), "f16")
+    vt = oracle.widen(A._normal_bits(rng, (tot, 2, 8), "f16"), "f16")
+    t0 = 0
+    for b in range(3):
+        n = int(p.seq_lens[b])
+        kk = kt[t0:t0 + n].transpose(1, 0, 2)[None]
+        vv = vt[t0:t0 + n].transpose(1, 0, 2)[None]
+        t0 += n
+        O1, L1 = oracle.attention(q[b][None, :, None, :], kk, vv, 0.3)
+        np.testing.assert_allclose(O[b], O1[0, :, 0], atol=1e-13)
+        np.testing.assert_allclose(L[b], L1[0, :, 0], atol=1e-13)
+        # decode(L) == last row of causal prefill whose last query is q
+        qq = np.concatenate([_rand((1, 4, n - 1, 8), 41 + b), q[b][None, :, None, :]], axis=2)
+        O2, L2 = oracle.attention(qq, kk, vv, 0.3, causal=True)
+        np.testing.assert_allclose(O[b], O2[0, :, -1], atol=1e-13)
+        np.testing.assert_allclose(L[b], L2[0, :, -1], atol=1e-13)
+    # a different physical placement of the same pages gives the same result
+    perm = np.random.default_rng(7).permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    bt2 = np.where(p.block_table >= 0, inv[np.maximum(p.block_table, 0)], -1)
+    O3, L3 = oracle.decode_paged(q, kp[perm], vp[perm], bt2, p.seq_lens, 0.3, p.page_size)
+    np.testing.assert_array_equal(O3, O)
+    np.testing.assert_array_equal(L3, L)
+
+
+def pin_visited_tiles():
+    # closed-form tile counts: causal Nq=Nk=N with BM=2*BN visits 2(qt+1) tiles per
+    # q-tile; a window of left=W, right=0 visits at most ceil((BM + W) / BN) + 1.
+    t = oracle.visited_tiles(512, 512, 128, 64, True, -1, -1)
+    assert [len(x) for x in t] == [2, 4, 6, 8]
+    assert t[1] == [0, 1, 2, 3]
+    t = oracle.visited_tiles(100, 100, 32, 16, False, -1, -1)
+    assert all(x == list(range(7)) for x in t)
+    t = oracle.visited_tiles(1024, 1024, 128, 64, True, 128, 0)
+    assert t[0] == [0, 1] and t[3] == [4, 5, 6, 7]
+    for qt, tiles in enumerate(t):
+        q0, q1 = 128 * qt, 128 * qt + 127
+        lo, hi = max(0, q0 - 128), q1
+        assert tiles == list(range(lo // 64, hi // 64 + 1)), (qt, tiles)
+    # bottom-right alignment: Nq=1, Nk=1000 causal visits every key tile
+    assert oracle.visited_tiles(1, 1000, 128, 64, True, -1, -1) == [list(range(16))]
+    # Nq > Nk causal: the first query tile is entirely masked
+    assert oracle.visited_tiles(256, 64, 128, 64, True, -1, -1)[0] == []
+
+
+def pin_config4_pairs():
+    # config 4 (N=8192, causal, left=512, right=0): the inclusive reading gives
+    # min(i, 512) + 1 visible keys per row.
+    N, W = 8192, 512
+    i = np.arange(N)
+    lo, hi = oracle.window_bounds(i, N, N, True, W, 0)
+    n = hi - lo + 1
+    assert np.array_equal(n, np.minimum(i, W) + 1)
+    assert int(n.sum()) == 4_071_168
+
+
+PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
+        pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
+        pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
+        pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
+        pin_config4_pairs]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ------------------------------------------------------------- planted mistakes
+
+def _caught(monkeypatch_ctx, pins):
+    """True if at least one pin fails under the planted mistake."""
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            return True
+        except (ValueError, IndexError, FloatingPointError):
+            return True
+    return False
+
+
+def _mut_exclusive_window(i, j, Nq, Nk, causal, left, right):
+    # plausible mistake: exclusive left window end (P5-style "w keys" off by one)
+    ok = _ORIG_VISIBLE(i, j, Nq, Nk, causal, left, right)
+    if left >= 0:
+        ok = ok & (np.asarray(j) > np.asarray(i) + (Nk - Nq) - left)
+    return ok
+
+
+def _mut_top_left_causal(i, j, Nq, Nk, causal, left, right):
+    # plausible mistake: top-left causal alignment for Nq != Nk
+    return _ORIG_VISIBLE(i, j, Nk, Nk, causal, left, right)
+
+
+def _mut_rows_no_scale(qr, kk, vv, scale, vis):
+    return _ORIG_ROWS(qr, kk, vv, 1.0, vis)
+
+
+def _mut_rows_lse_no_max(qr, kk, vv, scale, vis):
+    o, lse, p = _ORIG_ROWS(qr, kk, vv, scale, vis)
+    s = scale * (qr @ kk.T)
+    m = np.where(vis, s, -np.inf).max(axis=1, initial=-np.inf)
+    return o, np.where(np.isfinite(lse), lse - np.where(np.isfinite(m), m, 0.0), lse), p
+
+
+def _mut_rows_transposed_v(qr, kk, vv, scale, vis):
+    # plausible mistake: contract P with V along the wrong axis when shapes allow it
+    o, lse, p = _ORIG_ROWS(qr, kk, vv, scale, vis)
+    if vv.shape[0] == vv.shape[1]:
+        o = p @ vv.T
+    return o, lse, p
+
+
+def _mut_rows_sign(qr, kk, vv, scale, vis):
+    return _ORIG_ROWS(qr, kk, vv, -scale, vis)
+
+
+def _mut_merge_unweighted(parts):
+    outs = [p[0] for p in parts]
+    O, L = _ORIG_MERGE(parts)
+    return np.mean(outs, axis=0), L
+
+
+_ORIG_VISIBLE = OA.visible
+_ORIG_ROWS = OA._rows_attention
+_ORIG_MERGE = OA.lse_merge
+
+
+def _gqa_mod_attention(q, k, v, scale, causal=False, left=-1, right=-1, rows=None, row_block=512):
+    # plausible mistake: head h reads KV head h % Hkv instead of h // g
+    Hq, Hkv = q.shape[1], k.shape[1]
+    idx = np.arange(Hq) % Hkv
+    return _ORIG_ATT(q, np.asarray(k)[:, idx], np.asarray(v)[:, idx], scale, causal, left, right,
+                     rows, row_block)
+
+
+_ORIG_ATT = OA.attention
+
+MUTATIONS = {
+    "exclusive_window": ("visible", _mut_exclusive_window),
+    "top_left_causal": ("visible", _mut_top_left_causal),
+    "dropped_scale": ("_rows_attention", _mut_rows_no_scale),
+    "lse_missing_max": ("_rows_attention", _mut_rows_lse_no_max),
+    "transposed_v": ("_rows_attention", _mut_rows_transposed_v),
+    "wrong_sign": ("_rows_attention", _mut_rows_sign),
+    "unweighted_merge": ("lse_merge", _mut_merge_unweighted),
+    "gqa_modulo": ("attention", _gqa_mod_attention),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _caught(monkeypatch, PINS), f"no pin catches the planted mistake {name!r}"
