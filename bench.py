@@ -1,0 +1,246 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One *step* is one ``mfa_fwd`` call over the dense causal prefill workload
+(B=2, H=8, Nq=Nk=4096, D=128, fp16, causal; seeded synthetic inputs resident in HBM
+before timing).  ``value`` is its throughput in TFLOP/s, counting 4*D FLOP per
+*visible* (query, key) pair.  In the same run the other workloads are timed the same
+way and reported under ``workloads``: the GQA long-context prefill (bf16, N=16384),
+the sliding-window prefill (window (512, 0)), and the paged split-KV decode (HBM
+GB/s over the algorithmic bytes: every cached K/V byte once, plus q, out, LSE, the
+block-table entries used and seq_lens).
+
+Timing: HIP events on the stream the kernels run on, W untimed warm-up steps, then
+K timed steps; ``torch.cuda.synchronize()`` on both sides of the timed region.
+``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
+same prefill workload, for about 10 s, and scales to TFLOP/s.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_inputs as A  # noqa: E402
+
+PEAK_MFMA_F16 = 2500.0   # TFLOP/s, MI355X dense fp16/bf16
+PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
+
+METRIC = "attn fwd TFLOP/s (D=128 causal fp16) + paged decode HBM GB/s, % roofline"
+
+
+def visible_pairs(Nq, Nk, causal, left, right) -> int:
+    """Number of visible (query, key) pairs of one head (inclusive window ends)."""
+    i = np.arange(Nq, dtype=np.int64)
+    off = Nk - Nq
+    lo = np.zeros(Nq, dtype=np.int64) if left < 0 else np.maximum(0, i + off - left)
+    hi = np.full(Nq, Nk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i + off)
+    if right >= 0:
+        hi = np.minimum(hi, i + off + right)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def to_dev(bits, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def time_calls(fn, steps, warmup):
+    """Per-call times (ms) measured with HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in zip(starts, ends):
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    times = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return times, wall
+
+
+def bench_prefill(i, steps, warmup):
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(i)
+    x = A.config_inputs(i)
+    q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    del x
+
+    def step():
+        ea.mfa_fwd(q, k, v, scale=c["scale"], causal=c["causal"], win_left=c["left"],
+                   win_right=c["right"], out=out, lse=lse)
+
+    times, wall = time_calls(step, steps, warmup)
+    info = ea.mfa_last_dispatch()
+    flop = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], c["left"], c["right"]) \
+        * c["B"] * c["Hq"]
+    ms = float(np.mean(times))
+    tf = flop / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['Nq']} D={c['D']} "
+                    f"{c['dtype']} causal={int(c['causal'])} window=({c['left']},{c['right']})",
+        "tflops": tf, "ms_mean": ms, "ms_median": float(np.median(times)),
+        "ms_min": float(np.min(times)), "wall_ms": wall, "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_MFMA_F16, "traffic": None},
+        "kernel": info["kernel"], "grid": info["grid"], "planned_tiles": info["planned"],
+        "dtype": c["dtype"],
+    }
+
+
+def decode_bytes(p, Hkv, D, Hq):
+    L = p.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * Hkv * D * 2 * 2
+    B = len(L)
+    qo = 2 * B * Hq * D * 2
+    lse = B * Hq * 4
+    bt = 4 * int(np.ceil(L / p.page_size).sum())
+    return kv + qo + lse + bt + 4 * B
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(5)
+    p = A.config_inputs(5)
+    q = to_dev(p.q, c["dtype"])
+    kp = to_dev(p.k_pages, c["dtype"])
+    vp = to_dev(p.v_pages, c["dtype"])
+    bt = torch.from_numpy(p.block_table).to("cuda")
+    sl = torch.from_numpy(p.seq_lens).to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    nbytes = ea.mfa_decode_workspace_bytes(c["B"], c["Hq"], c["D"], 16, bt.shape[1], 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        ea.mfa_decode_paged(q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse, workspace=ws)
+
+    times, wall = time_calls(step, steps, warmup)
+    info = ea.mfa_last_dispatch()
+    nb = decode_bytes(p, c["Hkv"], c["D"], c["Hq"])
+    ms = float(np.mean(times))
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} bf16 "
+                    f"page=16 seq_lens in [1024,32768] (sum={int(p.seq_lens.sum())})",
+        "gbs": gbs, "ms_mean": ms, "ms_median": float(np.median(times)),
+        "ms_min": float(np.min(times)), "wall_ms": wall, "bytes": nb,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM, "traffic": None},
+        "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
+        "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
+    }
+
+
+def cpu_baseline(budget_s=10.0):
+    """The float64 oracle on this host over whole heads of the dense causal prefill."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    c = A.config(2)
+    x = A.config_inputs(2)
+    q, k, v = (oracle.widen(t, c["dtype"]) for t in (x.q, x.k, x.v))
+    pairs = visible_pairs(c["Nq"], c["Nk"], True, -1, -1)
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(c["B"]):
+        for h in range(c["Hq"]):
+            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                             c["scale"], True)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flop = 4.0 * c["D"] * pairs * done
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of 16 (b,h) heads of the B=2 H=8 N=4096 D=128 causal workload, "
+                      f"float64 numpy oracle, {dt:.1f} s wall, BLAS threads={threads}, "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="2,3,4,5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_amd as ea
+    if not os.path.exists(ea.LIB_PATH):
+        from exact_attention_amd.build import build
+        build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ea.lib()
+
+    wl = [int(s) for s in args.workloads.split(",") if s]
+    res = {}
+    if 2 not in wl:
+        wl = [2] + wl
+    for i in wl:
+        if i == 5:
+            res[i] = bench_decode(args.steps, args.warmup)
+        else:
+            res[i] = bench_prefill(i, args.steps, args.warmup)
+        print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)
+
+    head = res[2]
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_mean"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {"workload": head["workload"], "global_batch": 2, "seq_len": 4096,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    line["workloads"] = {
+        str(i): {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+        for i, r in res.items()}
+    if 5 in res:
+        line["decode_gbs"] = round(res[5]["gbs"], 1)
+        line["decode_roofline"] = res[5]["roofline"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

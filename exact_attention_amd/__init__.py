@@ -1,0 +1,261 @@
+"""exact_attention_amd — MI355X (gfx950) fused exact attention.
+
+A thin ctypes binding over ``libmfa.so`` (C ABI in ``include/mfa.h``).  The functions
+keep the C names; they only marshal arguments: check tensor placement, dtype, shape and
+contiguity, allocate outputs with torch when the caller passes none, pass raw device
+pointers and the current HIP stream, and raise ``MfaError`` on a negative status.
+Every step of the computation runs in the library's HIP kernels; there is no other
+code path.  If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmfa.so")
+
+MFA_F16 = 0
+MFA_BF16 = 1
+
+STATUS = {
+    0: "MFA_OK", -1: "MFA_ERR_NULL", -2: "MFA_ERR_SHAPE", -3: "MFA_ERR_GQA",
+    -4: "MFA_ERR_HEAD_DIM", -5: "MFA_ERR_DTYPE", -6: "MFA_ERR_WINDOW", -7: "MFA_ERR_SCALE",
+    -8: "MFA_ERR_WORKSPACE", -9: "MFA_ERR_PAGED", -10: "MFA_ERR_OVERFLOW", -11: "MFA_ERR_HIP",
+    -12: "MFA_ERR_ALIGN", -13: "MFA_ERR_ARG",
+}
+
+
+class MfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({mfa_status_string(status)})")
+
+
+class mfa_plan(ctypes.Structure):
+    _fields_ = [("BM", ctypes.c_int), ("BN", ctypes.c_int), ("waves", ctypes.c_int),
+                ("n_q_tiles", ctypes.c_int), ("n_k_tiles", ctypes.c_int),
+                ("visited", ctypes.c_longlong), ("edge", ctypes.c_longlong)]
+
+
+class mfa_dispatch_info(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 96), ("op", ctypes.c_int), ("BM", ctypes.c_int),
+                ("BN", ctypes.c_int), ("waves", ctypes.c_int), ("grid", ctypes.c_int * 3),
+                ("block", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("chunk_tokens", ctypes.c_int), ("planned", ctypes.c_longlong),
+                ("n_launches", ctypes.c_int)]
+
+
+_LIB = None
+
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SIGS = {
+    "mfa_plan_fwd": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(mfa_plan), _VP, ctypes.c_longlong]),
+    "mfa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
+    "mfa_fwd_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
+                             _VP, _VP]),
+    "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "mfa_decode_num_splits": (_I, [_I, _I, _I]),
+    "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
+                              _I, _VP, ctypes.c_size_t, _I, _VP]),
+    "mfa_last_dispatch": (_I, [ctypes.POINTER(mfa_dispatch_info)]),
+    "mfa_status_string": (ctypes.c_char_p, [_I]),
+    "mfa_version": (_I, []),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """Load libmfa.so (built in-tree by ``exact_attention_amd.build``); raise if absent."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m exact_attention_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def mfa_status_string(status: int) -> str:
+    return lib().mfa_status_string(int(status)).decode()
+
+
+def mfa_version() -> int:
+    return int(lib().mfa_version())
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise MfaError(st, where)
+
+
+def mfa_plan_fwd(Nq: int, Nk: int, D: int, dtype: int = MFA_F16, causal: bool = False,
+                 win_left: int = -1, win_right: int = -1, with_ranges: bool = True):
+    """Host-only tile plan.  Returns (plan dict, list of (kt_lo, kt_hi) per query tile)."""
+    plan = mfa_plan()
+    probe = lib().mfa_plan_fwd(Nq, Nk, D, dtype, int(causal), win_left, win_right,
+                               ctypes.byref(plan), None, 0)
+    _check(probe, "mfa_plan_fwd")
+    ranges = None
+    if with_ranges:
+        buf = (ctypes.c_int32 * (2 * plan.n_q_tiles))()
+        _check(lib().mfa_plan_fwd(Nq, Nk, D, dtype, int(causal), win_left, win_right,
+                                  ctypes.byref(plan), ctypes.cast(buf, _VP), 2 * plan.n_q_tiles),
+               "mfa_plan_fwd")
+        ranges = [(buf[2 * t], buf[2 * t + 1]) for t in range(plan.n_q_tiles)]
+    d = {f: getattr(plan, f) for f, _ in mfa_plan._fields_}
+    return d, ranges
+
+
+def mfa_last_dispatch() -> dict:
+    info = mfa_dispatch_info()
+    _check(lib().mfa_last_dispatch(ctypes.byref(info)), "mfa_last_dispatch")
+    d = {f: getattr(info, f) for f, _ in mfa_dispatch_info._fields_}
+    d["kernel"] = info.kernel.decode()
+    d["grid"] = list(info.grid)
+    return d
+
+
+def mfa_decode_workspace_bytes(B: int, Hq: int, D: int, page_size: int, max_pages_per_seq: int,
+                               num_splits: int = 0) -> int:
+    return int(lib().mfa_decode_workspace_bytes(B, Hq, D, page_size, max_pages_per_seq, num_splits))
+
+
+def mfa_decode_num_splits(page_size: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
+    st = int(lib().mfa_decode_num_splits(page_size, max_pages_per_seq, num_splits))
+    if st < 0:
+        raise MfaError(st, "mfa_decode_num_splits")
+    return st
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return MFA_F16
+    if t.dtype == torch.bfloat16:
+        return MFA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 / bfloat16)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left: int = -1,
+            win_right: int = -1, out=None, lse=None, return_lse: bool = True, tile_log=None):
+    """Forward pass on torch tensors q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] (fp16 or bf16).
+
+    ``scale`` defaults to 1/sqrt(D) here (the C ABI applies no default).  Returns
+    ``(out, lse)``; ``lse`` is None when ``return_lse`` is False and none is given.
+    ``tile_log`` (int32 device tensor) selects ``mfa_fwd_tilelog``.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must match q")
+    args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else None,
+            B, Hq, Hkv, Nq, Nk, D, float(scale), int(bool(causal)), int(win_left),
+            int(win_right), dt, _stream(q)]
+    if tile_log is None:
+        _check(lib().mfa_fwd(*args), "mfa_fwd")
+    else:
+        if tile_log.dtype != torch.int32:
+            raise TypeError("tile_log must be int32")
+        _check(lib().mfa_fwd_tilelog(*args, _dev(tile_log, "tile_log")), "mfa_fwd_tilelog")
+    return out, lse
+
+
+def mfa_fwd_tilelog(q, k, v, tile_log, **kw):
+    return mfa_fwd(q, k, v, tile_log=tile_log, **kw)
+
+
+def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
+                     num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
+                     workspace=None):
+    """Paged split-KV decode on torch tensors.
+
+    q [B,Hq,D]; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
+    [B, max_pages_per_seq]; seq_lens int32 [B] (device).  Returns ``(out, lse)``.
+    ``workspace`` (any device tensor of enough bytes) is allocated here when absent.
+    """
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B, Hq, D] and the page pools [P, page, Hkv, D]")
+    B, Hq, D = q.shape
+    P, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError("head dimension mismatch")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share one dtype")
+    dt = _dtype_code(q)
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = mfa_decode_workspace_bytes(B, Hq, D, page_size, max_pages, num_splits)
+    if need == 0:
+        raise MfaError(-13, "mfa_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mfa_decode_paged(
+        _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None,
+        B, Hq, Hkv, D, page_size, P, max_pages, float(scale), int(num_splits),
+        _dev(workspace, "workspace"), wbytes, dt, _stream(q)), "mfa_decode_paged")
+    return out, lse
+
+
+__all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
+           "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
+           "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version"]

@@ -1,0 +1,216 @@
+// C ABI of libmfa: argument validation, tile planning, dispatch and the per-thread
+// dispatch record.  Every check runs before anything is enqueued; a failed check
+// returns a negative status and touches no memory (the "reject malformed input, never
+// fall back silently" contract of the MXFlashAttn 1.5.0 and mlx-mfa pages).
+#include <math.h>
+#include <string.h>
+
+#include "mfa_geometry.h"
+#include "mfa_internal.h"
+
+namespace {
+
+thread_local mfa_dispatch_info g_last;
+thread_local bool g_have_last = false;
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int dtype, int D) {
+    if (dtype != MFA_F16 && dtype != MFA_BF16) return MFA_ERR_DTYPE;
+    if (D != 64 && D != 128) return MFA_ERR_HEAD_DIM;
+    return MFA_OK;
+}
+
+int check_fwd(const void* q, const void* k, const void* v, void* out, const float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale, int causal,
+              int win_left, int win_right, int dtype) {
+    if (!q || !k || !v || !out) return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return MFA_ERR_SHAPE;
+    if (causal != 0 && causal != 1) return MFA_ERR_ARG;
+    if (Hq % Hkv != 0) return MFA_ERR_GQA;
+    if (win_left < -1 || win_right < -1) return MFA_ERR_WINDOW;
+    if (!isfinite(scale)) return MFA_ERR_SCALE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MFA_ERR_ALIGN;
+    const int64_t nqt = ((int64_t)Nq + mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (nqt * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
+    // element counts must fit comfortably in 64-bit offsets
+    const double qe = (double)B * Hq * Nq * D, ke = (double)B * Hkv * Nk * D;
+    if (qe > 4e18 || ke > 4e18) return MFA_ERR_OVERFLOW;
+    return MFA_OK;
+}
+
+void plan_fill(int Nq, int Nk, int D, int causal, int left, int right, mfa_plan* plan,
+               int32_t* kt_range) {
+    const int BM = mfa_fwd_bm(), BN = mfa_fwd_bn(D);
+    const MfaMask m = mfa_make_mask(Nq, Nk, causal, left, right);
+    plan->BM = BM;
+    plan->BN = BN;
+    plan->waves = 4;
+    plan->n_q_tiles = (Nq + BM - 1) / BM;
+    plan->n_k_tiles = (Nk + BN - 1) / BN;
+    long long visited = 0, edge = 0;
+    for (int qt = 0; qt < plan->n_q_tiles; ++qt) {
+        int lo, hi;
+        mfa_tile_range(m, Nq, BM, BN, qt, &lo, &hi);
+        visited += hi - lo;
+        for (int kt = lo; kt < hi; ++kt) edge += mfa_tile_full(m, BM, BN, qt, kt) ? 0 : 1;
+        if (kt_range) {
+            kt_range[2 * qt] = lo;
+            kt_range[2 * qt + 1] = hi;
+        }
+    }
+    plan->visited = visited;
+    plan->edge = edge;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int D, float scale, int causal, int win_left,
+               int win_right, int dtype, void* stream, int32_t* tile_log) {
+    int st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
+                       win_right, dtype);
+    if (st) return st;
+    MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, Nq, Nk, D, scale,
+                    causal, win_left, win_right, dtype};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = 1;
+    info.n_launches = 1;
+    st = mfa_fwd_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
+    mfa_plan plan;
+    plan_fill(Nq, Nk, D, causal, win_left, win_right, &plan, nullptr);
+    info.planned = plan.visited * (long long)B * Hq;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
+int decode_splits(int max_pages, int num_splits, int* chunk_pages) {
+    const int c = mfa_decode_chunk_pages(max_pages, num_splits);
+    if (chunk_pages) *chunk_pages = c;
+    return (max_pages + c - 1) / c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mfa_plan_fwd(int Nq, int Nk, int D, int dtype, int causal, int win_left, int win_right,
+                 mfa_plan* plan, int32_t* kt_range, long long kt_range_len) {
+    if (!plan) return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (Nq < 1 || Nk < 1) return MFA_ERR_SHAPE;
+    if (causal != 0 && causal != 1) return MFA_ERR_ARG;
+    if (win_left < -1 || win_right < -1) return MFA_ERR_WINDOW;
+    const long long nqt = ((long long)Nq + mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (kt_range && kt_range_len < 2 * nqt) {
+        plan_fill(Nq, Nk, D, causal, win_left, win_right, plan, nullptr);
+        return MFA_ERR_ARG;
+    }
+    plan_fill(Nq, Nk, D, causal, win_left, win_right, plan, kt_range);
+    return MFA_OK;
+}
+
+int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+            int Hkv, int Nq, int Nk, int D, float scale, int causal, int win_left,
+            int win_right, int dtype, void* stream) {
+    return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
+                      win_right, dtype, stream, nullptr);
+}
+
+int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int Hq, int Hkv, int Nq, int Nk, int D, float scale, int causal,
+                    int win_left, int win_right, int dtype, void* stream, int32_t* tile_log) {
+    if (!tile_log) return MFA_ERR_NULL;
+    if ((uintptr_t)tile_log & 3u) return MFA_ERR_ALIGN;
+    return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
+                      win_right, dtype, stream, tile_log);
+}
+
+int mfa_decode_num_splits(int page_size, int max_pages_per_seq, int num_splits) {
+    if (page_size != 16 || max_pages_per_seq < 1) return MFA_ERR_PAGED;
+    if (num_splits < 0) return MFA_ERR_ARG;
+    return decode_splits(max_pages_per_seq, num_splits, nullptr);
+}
+
+size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
+                                  int num_splits) {
+    if (B < 1 || Hq < 1 || (D != 64 && D != 128)) return 0;
+    const int S = mfa_decode_num_splits(page_size, max_pages_per_seq, num_splits);
+    if (S < 1) return 0;
+    return (size_t)B * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
+}
+
+int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                     int B, int Hq, int Hkv, int D, int page_size, int num_pages,
+                     int max_pages_per_seq, float scale, int num_splits, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (B < 1 || Hq < 1 || Hkv < 1) return MFA_ERR_SHAPE;
+    if (B > 65535 || Hq > 65535) return MFA_ERR_OVERFLOW;
+    if (Hq % Hkv != 0) return MFA_ERR_GQA;
+    if (page_size != 16 || num_pages < 1 || max_pages_per_seq < 1) return MFA_ERR_PAGED;
+    if (!isfinite(scale)) return MFA_ERR_SCALE;
+    if (num_splits < 0) return MFA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out) ||
+        ((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MFA_ERR_ALIGN;
+    if ((double)num_pages * page_size * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
+    int chunk_pages = 0;
+    const int S = decode_splits(max_pages_per_seq, num_splits, &chunk_pages);
+    const size_t need = (size_t)B * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return MFA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MFA_ERR_ALIGN;
+    MfaDecodeProblem p{q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, D,
+                       num_pages, max_pages_per_seq, scale, S, chunk_pages, workspace, dtype};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = 2;
+    st = mfa_decode_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
+int mfa_last_dispatch(mfa_dispatch_info* out) {
+    if (!out) return MFA_ERR_NULL;
+    if (!g_have_last) return MFA_ERR_ARG;
+    *out = g_last;
+    return MFA_OK;
+}
+
+const char* mfa_status_string(int status) {
+    switch (status) {
+        case MFA_OK: return "ok";
+        case MFA_ERR_NULL: return "a required pointer is NULL";
+        case MFA_ERR_SHAPE: return "a size is smaller than 1";
+        case MFA_ERR_GQA: return "Hq is not a multiple of Hkv";
+        case MFA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+        case MFA_ERR_DTYPE: return "dtype must be MFA_F16 or MFA_BF16";
+        case MFA_ERR_WINDOW: return "window bounds must be >= -1 (-1 = unbounded)";
+        case MFA_ERR_SCALE: return "scale is not finite";
+        case MFA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+        case MFA_ERR_PAGED: return "page_size must be 16 and num_pages, max_pages_per_seq >= 1";
+        case MFA_ERR_OVERFLOW: return "sizes exceed the addressing or launch-grid limits";
+        case MFA_ERR_HIP: return "the HIP runtime reported an error at launch";
+        case MFA_ERR_ALIGN: return "a tensor pointer is not suitably aligned (16 bytes)";
+        case MFA_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int mfa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers for gfx950 (CDNA4): MFMA wrappers, 16-bit conversions, lane exchange.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 mfa_f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mfa_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mfa_f32x16 __attribute__((ext_vector_type(16)));
+typedef float mfa_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mfa_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mfa_u32x2 __attribute__((ext_vector_type(2)));
+
+#define MFA_DT_F16 0
+#define MFA_DT_BF16 1
+
+#define MFA_INF __builtin_inff()
+#define MFA_LN2 0.69314718055994530942f
+
+// D(32x32, fp32) += A(32x16) * B(16x32).  Operands: 8 16-bit values per lane; lane l
+// holds row (A) / column (B) l % 32 and the k-group l / 32.
+template <int DT>
+__device__ __forceinline__ mfa_f32x16 mfa_mfma32(mfa_u32x4 a, mfa_u32x4 b, mfa_f32x16 c) {
+    if constexpr (DT == MFA_DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mfa_f16x8, a),
+                                                       __builtin_bit_cast(mfa_f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(mfa_bf16x8, a),
+                                                        __builtin_bit_cast(mfa_bf16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x32) * B(32x16).  Lane l holds row/column l % 16, k-group l / 16.
+template <int DT>
+__device__ __forceinline__ mfa_f32x4 mfa_mfma16(mfa_u32x4 a, mfa_u32x4 b, mfa_f32x4 c) {
+    if constexpr (DT == MFA_DT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mfa_f16x8, a),
+                                                       __builtin_bit_cast(mfa_f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfa_bf16x8, a),
+                                                        __builtin_bit_cast(mfa_bf16x8, b), c, 0, 0, 0);
+}
+
+// Round two fp32 values to the 16-bit type (nearest, ties to even) and pack lo | hi<<16.
+template <int DT>
+__device__ __forceinline__ uint32_t mfa_pack2(float lo, float hi) {
+    if constexpr (DT == MFA_DT_F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        h2 r = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, r);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        b2 r = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+}
+
+// Widen the low / high 16-bit half of a packed word to fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float mfa_lo(uint32_t w) {
+    if constexpr (DT == MFA_DT_F16)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    else
+        return __builtin_bit_cast(float, w << 16);
+}
+template <int DT>
+__device__ __forceinline__ float mfa_hi(uint32_t w) {
+    if constexpr (DT == MFA_DT_F16)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    else
+        return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+__device__ __forceinline__ float mfa_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float mfa_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x held by lane (lane ^ 32).
+__device__ __forceinline__ float mfa_swap_halves(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+// Value of x held by lane src (any lane of the wave).
+__device__ __forceinline__ float mfa_lane(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r + 15); every lane of the
+// row receives the result.
+__device__ __forceinline__ float mfa_dpp_f(float x, int ctrl_sel) {
+    int v = __builtin_bit_cast(int, x);
+    int r;
+    switch (ctrl_sel) {
+        case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false); break;  // row_ror:8
+        case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false); break;  // row_ror:4
+        case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false); break;   // quad_perm 2,3,0,1
+        default: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false); break;  // quad_perm 1,0,3,2
+    }
+    return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float mfa_row16_sum(float x) {
+    x += mfa_dpp_f(x, 0);
+    x += mfa_dpp_f(x, 1);
+    x += mfa_dpp_f(x, 2);
+    x += mfa_dpp_f(x, 3);
+    return x;
+}
+__device__ __forceinline__ float mfa_row16_max(float x) {
+    x = fmaxf(x, mfa_dpp_f(x, 0));
+    x = fmaxf(x, mfa_dpp_f(x, 1));
+    x = fmaxf(x, mfa_dpp_f(x, 2));
+    x = fmaxf(x, mfa_dpp_f(x, 3));
+    return x;
+}

@@ -1,0 +1,44 @@
+// Internal interface between the C ABI layer (mfa_api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "mfa.h"
+
+struct MfaFwdProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int32_t* tile_log;   // nullable: per-tile visit record
+    int B, Hq, Hkv, Nq, Nk, D;
+    float scale;
+    int causal, left, right;
+    int dtype;
+};
+
+struct MfaDecodeProblem {
+    const void* q;
+    const void* k_pages;
+    const void* v_pages;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, D;
+    int num_pages, max_pages_per_seq;
+    float scale;
+    int num_splits;      // resolved (> 0)
+    int chunk_pages;     // pages per split
+    void* workspace;
+    int dtype;
+};
+
+int mfa_fwd_bm();
+int mfa_fwd_bn(int D);
+int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
+
+int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits);
+int mfa_decode_launch(const MfaDecodeProblem& p, hipStream_t stream, mfa_dispatch_info* info);

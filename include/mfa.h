@@ -1,0 +1,184 @@
+/*
+ * mfa.h — C ABI of the MI355X (gfx950) fused exact-attention library, libmfa.so.
+ *
+ * Two operations, both exact attention O = softmax(scale * Q K^T + mask) V with an
+ * fp32 online softmax that never materialises the score matrix:
+ *
+ *   mfa_fwd           tiled forward (prefill) with causal / sliding-window key-tile
+ *                     skipping and grouped-query head mapping; writes O and the row
+ *                     log-sum-exp.  Defined by the FlashAttention-2 forward shader of
+ *                     the mlx-bun flash-attention.ts page (online softmax with running
+ *                     max m and sum l in fp32, O = o / l, LSE = m + log l) and the
+ *                     mlx-mfa 2.5.2 page's feature list ("Causal tile-skip",
+ *                     "Sliding window", "Native GQA").
+ *   mfa_decode_paged  single-query decode over a paged KV cache, split across
+ *                     workgroups along the keys, with partial (O, LSE) pairs merged in
+ *                     a second pass.  Defined by the mlx-mfa 2.5.2 page ("Flash Decode
+ *                     — two-phase split-KV", "Paged KV — page-pool KV cache with
+ *                     block_table") and the MXFlashAttn 1.5.0 page (M1 paged Split-KV
+ *                     decode; the per-split (m, l) slot race section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are caller-owned, contiguous, 16-byte aligned device memory.  The
+ *   library allocates no device memory; the decode workspace is passed in.
+ * - Element type: 16-bit storage, MFA_F16 (IEEE half) or MFA_BF16 (bfloat16), the
+ *   same for Q, K, V and O.  LSE is float32.  All arithmetic accumulates in fp32.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *   call returns without synchronising.
+ * - Arguments are validated before anything is launched; on failure a negative
+ *   mfa_status is returned and nothing is written.  There is no fallback path.
+ * - Visibility (mlx-mfa "Sliding window" feature, window_size=(left, right), -1 =
+ *   unbounded; causal mask of the mlx-bun forward shader), with off = Nk - Nq
+ *   (bottom-right alignment) and both window ends inclusive: key j is visible to
+ *   query i iff
+ *       (!causal || j <= i + off) && (left < 0 || j >= i + off - left)
+ *                                 && (right < 0 || j <= i + off + right).
+ *   A row with no visible key gets O = 0 and LSE = -inf.
+ * - Grouped-query attention: query head h reads KV head h / (Hq / Hkv) (mlx-bun
+ *   forward shader head mapping); Hq must be a multiple of Hkv.
+ * - Thread safety: calls may be made from several host threads; the dispatch record
+ *   returned by mfa_last_dispatch is per host thread.
+ */
+#ifndef MFA_H
+#define MFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MFA_F16 = 0, MFA_BF16 = 1 } mfa_dtype;
+
+typedef enum {
+    MFA_OK = 0,
+    MFA_ERR_NULL = -1,      /* a required pointer is NULL */
+    MFA_ERR_SHAPE = -2,     /* a size is < 1 (or inconsistent) */
+    MFA_ERR_GQA = -3,       /* Hq is not a multiple of Hkv */
+    MFA_ERR_HEAD_DIM = -4,  /* D not in {64, 128} */
+    MFA_ERR_DTYPE = -5,     /* dtype not MFA_F16 / MFA_BF16 */
+    MFA_ERR_WINDOW = -6,    /* win_left or win_right < -1 */
+    MFA_ERR_SCALE = -7,     /* scale is not finite */
+    MFA_ERR_WORKSPACE = -8, /* decode workspace NULL or too small */
+    MFA_ERR_PAGED = -9,     /* page_size != 16, num_pages or max_pages_per_seq < 1 */
+    MFA_ERR_OVERFLOW = -10, /* sizes exceed the 64-bit element / launch-grid limits */
+    MFA_ERR_HIP = -11,      /* the HIP runtime reported an error at launch */
+    MFA_ERR_ALIGN = -12,    /* a tensor pointer is not 16-byte aligned */
+    MFA_ERR_ARG = -13       /* other invalid argument (e.g. num_splits < 0) */
+} mfa_status;
+
+/* Tile plan of the forward kernel for one (batch, head): host-only, launches nothing.
+ * Defined by the causal tile-skip and sliding-window features of the mlx-mfa 2.5.2
+ * page: only key tiles holding at least one visible (query, key) pair are visited,
+ * and only tiles crossing the mask boundary are masked element-wise. */
+typedef struct {
+    int BM;               /* query rows per workgroup (one query tile) */
+    int BN;               /* keys per key tile */
+    int waves;            /* wavefronts (64 lanes) per workgroup */
+    int n_q_tiles;        /* ceil(Nq / BM) */
+    int n_k_tiles;        /* ceil(Nk / BN) */
+    long long visited;    /* key tiles visited, summed over the query tiles */
+    long long edge;       /* of which are masked element-wise */
+} mfa_plan;
+
+/* Fill *plan for the given problem.  If kt_range is not NULL it must hold
+ * 2 * n_q_tiles ints (pass its capacity in kt_range_len); on return kt_range[2t] and
+ * kt_range[2t+1] are the half-open key-tile range [lo, hi) visited by query tile t
+ * (lo == hi when the tile sees no key).  Returns MFA_OK or a validation error; if
+ * kt_range_len is too small, MFA_ERR_ARG with *plan still filled. */
+int mfa_plan_fwd(int Nq, int Nk, int D, int dtype, int causal, int win_left, int win_right,
+                 mfa_plan* plan, int32_t* kt_range, long long kt_range_len);
+
+/* Forward pass.
+ *   q    [B, Hq,  Nq, D]  dtype          k, v  [B, Hkv, Nk, D]  dtype
+ *   out  [B, Hq,  Nq, D]  dtype (written, rounded to nearest even from fp32)
+ *   lse  [B, Hq,  Nq]     float32, natural log of the sum of exp of the scaled
+ *                         visible scores; may be NULL
+ *   scale multiplies Q K^T before masking (finite; no default is applied)
+ *   causal (0/1), win_left / win_right >= -1 (-1 = unbounded)
+ * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE, _GQA, _WINDOW, _SCALE, _ALIGN,
+ * _OVERFLOW, _HIP. */
+int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+            int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+            int causal, int win_left, int win_right, int dtype, void* stream);
+
+/* Same as mfa_fwd, and additionally records, for every (b, h, query tile), four int32
+ * values in tile_log[((b * Hq + h) * n_q_tiles + t) * 4 + {0,1,2,3}]:
+ *   first key tile visited (or -1), number of key tiles visited, number of those
+ *   masked element-wise, one past the last key tile visited (or -1).
+ * tile_log is device memory of B * Hq * n_q_tiles * 4 int32 (n_q_tiles from
+ * mfa_plan_fwd).  Used to check that the kernel visits exactly the planned tiles. */
+int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+                    int causal, int win_left, int win_right, int dtype, void* stream,
+                    int32_t* tile_log);
+
+/* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).
+ * Returns 0 if the arguments are invalid. */
+size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
+                                  int num_splits);
+
+/* Number of key splits mfa_decode_paged will use (num_splits 0 = auto), or a negative
+ * status if the arguments are invalid. */
+int mfa_decode_num_splits(int page_size, int max_pages_per_seq, int num_splits);
+
+/* Paged split-KV decode: one new query token per sequence.
+ *   q            [B, Hq, D]                          dtype
+ *   k_pages      [num_pages, page_size, Hkv, D]      dtype   (pool of KV pages)
+ *   v_pages      [num_pages, page_size, Hkv, D]      dtype
+ *   block_table  [B, max_pages_per_seq] int32: token t of sequence b lives in page
+ *                block_table[b, t / page_size], slot t % page_size
+ *   seq_lens     [B] int32, device memory: cached tokens of each sequence, all visible
+ *   out          [B, Hq, D] dtype;  lse [B, Hq] float32 or NULL
+ *   page_size must be 16.  num_splits: 0 = auto, else an upper bound on the number of
+ *   key splits; splits are contiguous ranges of logical token positions, so the result
+ *   does not depend on where the pages sit in the pool.
+ *   workspace: device memory of at least mfa_decode_workspace_bytes(...) bytes, holding
+ *   the per-split partial (O, LSE); its contents on entry do not matter.
+ * Device-side contract (seq_lens stays on the device and is not checked on the host):
+ *   0 <= seq_lens[b] <= max_pages_per_seq * page_size and the first
+ *   ceil(seq_lens[b] / page_size) entries of row b of block_table are valid page
+ *   indices.  Out of contract, the kernels stay in bounds (lengths are clamped to the
+ *   capacity and invalid page indices are skipped) but the result is unspecified.
+ *   Tokens past seq_lens[b] are never used, whatever they hold.  seq_lens[b] == 0
+ *   gives O = 0 and LSE = -inf.
+ * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE, _GQA, _PAGED, _SCALE, _ALIGN,
+ * _WORKSPACE, _ARG, _OVERFLOW, _HIP. */
+int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     void* out, float* lse,
+                     int B, int Hq, int Hkv, int D, int page_size, int num_pages,
+                     int max_pages_per_seq, float scale, int num_splits,
+                     void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
+ * record: backend, operation, selection and split fields). */
+typedef struct {
+    char kernel[96];      /* kernel name of the main launch */
+    int op;               /* 1 = forward, 2 = paged decode */
+    int BM, BN, waves;    /* forward tile configuration */
+    int grid[3];          /* main launch grid */
+    int block;            /* threads per workgroup */
+    int num_splits;       /* decode: key splits (grid.x of the split kernel) */
+    int chunk_tokens;     /* decode: logical tokens per split */
+    long long planned;    /* forward: key tiles visited over all (b, h); decode: 0 */
+    int n_launches;       /* kernels enqueued by the call */
+} mfa_dispatch_info;
+
+/* Copy the calling thread's last dispatch record; MFA_ERR_NULL if out is NULL,
+ * MFA_ERR_ARG if this thread has launched nothing yet. */
+int mfa_last_dispatch(mfa_dispatch_info* out);
+
+/* Static description of a status code. */
+const char* mfa_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int mfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_H */

@@ -1,0 +1,45 @@
+"""Helpers shared by the GPU tests (no attention arithmetic here)."""
+import numpy as np
+
+TOL_O = {"f16": 2e-3, "bf16": 1.5e-2}   # max-abs on O (fp32 accumulation)
+TOL_LSE = 1e-3                          # absolute, on LSE
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float16 if dtype == "f16" else torch.bfloat16
+
+
+def to_dev(bits: np.ndarray, dtype: str):
+    """uint16 bit patterns -> device tensor of the 16-bit float type (bit-identical)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch_dtype(dtype))
+
+
+def to_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_f64(t, dtype) -> np.ndarray:
+    import oracle
+    return oracle.widen(to_bits(t), dtype)
+
+
+def assert_close_o(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    assert err <= TOL_O[dtype], f"{what}: max |dO| = {err:.3e} > {TOL_O[dtype]}"
+    return err
+
+
+def assert_close_lse(got: np.ndarray, ref: np.ndarray, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(got[fin]))
+    err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+    assert err <= TOL_LSE, f"{what}: max |dLSE| = {err:.3e} > {TOL_LSE}"
+    return err

@@ -1,0 +1,178 @@
+"""Host side of the C ABI, without a GPU: the library loads and exports every
+declared entry point; the tile plan equals the oracle's brute-force visited-tile set;
+malformed arguments get their documented status before anything is launched."""
+import math
+import os
+import re
+import threading
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfa.h")
+
+ea = pytest.importorskip("exact_attention_amd")
+if not os.path.exists(ea.LIB_PATH):
+    pytest.skip("libmfa.so not built", allow_module_level=True)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(mfa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    L = ea.lib()
+    for n in names:
+        assert hasattr(L, n), f"libmfa.so does not export {n}"
+    assert set(names) == set(ea.EXPORTS), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    assert ea.mfa_version() >= 100
+    for code in range(-13, 1):
+        s = ea.mfa_status_string(code)
+        assert s and s != "unknown status"
+    assert ea.mfa_status_string(5) == "unknown status"
+
+
+def _plan_vs_oracle(Nq, Nk, D, causal, left, right):
+    plan, ranges = ea.mfa_plan_fwd(Nq, Nk, D, ea.MFA_F16, causal, left, right)
+    ref = oracle.visited_tiles(Nq, Nk, plan["BM"], plan["BN"], causal, left, right)
+    assert len(ranges) == len(ref) == math.ceil(Nq / plan["BM"])
+    for t, ((lo, hi), tiles) in enumerate(zip(ranges, ref)):
+        assert list(range(lo, hi)) == tiles, (Nq, Nk, D, causal, left, right, t)
+    assert plan["visited"] == sum(len(t) for t in ref)
+    assert 0 <= plan["edge"] <= plan["visited"]
+    return plan
+
+
+@pytest.mark.parametrize("case", [
+    (128, 128, 64, False, -1, -1), (128, 128, 64, True, -1, -1), (4096, 4096, 128, True, -1, -1),
+    (8192, 8192, 128, True, 512, 0), (1, 1, 128, True, -1, -1), (1, 5000, 128, True, -1, -1),
+    (300, 100, 64, True, -1, -1), (1000, 1000, 128, False, 3, 7), (777, 1234, 128, False, 0, 0),
+    (513, 513, 64, True, 0, -1), (200, 4000, 128, False, -1, 0), (4000, 200, 128, False, 50, -1),
+])
+def test_plan_matches_oracle(case):
+    _plan_vs_oracle(*case)
+
+
+def test_plan_random():
+    rng = np.random.default_rng(0)
+    for _ in range(60):
+        Nq, Nk = (int(x) for x in rng.integers(1, 700, size=2))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        left = int(rng.choice([-1, 0, 1, 17, 130, 1000]))
+        right = int(rng.choice([-1, 0, 1, 33, 300]))
+        _plan_vs_oracle(Nq, Nk, D, causal, left, right)
+
+
+def test_plan_headline_counts():
+    # causal N=4096 with 128x64 tiles: query tile t visits 2(t+1) tiles -> 1056 of 2048
+    plan, _ = ea.mfa_plan_fwd(4096, 4096, 128, ea.MFA_F16, True)
+    assert (plan["BM"], plan["BN"]) == (128, 64)
+    assert plan["visited"] == 1056 and plan["n_k_tiles"] * plan["n_q_tiles"] == 2048
+    # the diagonal of a 128-row tile crosses two 64-key tiles: both are masked
+    assert plan["edge"] == 64
+    # window (512, 0): query tile t visits key tiles max(0, 2t-8) .. 2t+1 -> 620 in all
+    plan, _ = ea.mfa_plan_fwd(8192, 8192, 128, ea.MFA_F16, True, 512, 0)
+    assert plan["visited"] == sum(min(2 * t + 2, 10) for t in range(64)) == 620
+
+
+def test_plan_errors():
+    P = ea.mfa_plan
+    import ctypes
+    p = P()
+    L = ea.lib()
+    assert L.mfa_plan_fwd(10, 10, 96, 0, 0, -1, -1, ctypes.byref(p), None, 0) == -4
+    assert L.mfa_plan_fwd(10, 10, 64, 3, 0, -1, -1, ctypes.byref(p), None, 0) == -5
+    assert L.mfa_plan_fwd(0, 10, 64, 0, 0, -1, -1, ctypes.byref(p), None, 0) == -2
+    assert L.mfa_plan_fwd(10, 10, 64, 0, 0, -2, -1, ctypes.byref(p), None, 0) == -6
+    assert L.mfa_plan_fwd(10, 10, 64, 0, 0, -1, -1, None, None, 0) == -1
+    buf = (ctypes.c_int32 * 1)()
+    assert L.mfa_plan_fwd(1000, 10, 64, 0, 0, -1, -1, ctypes.byref(p), ctypes.cast(buf, ctypes.c_void_p), 1) == -13
+
+
+# fake, aligned device addresses: every case below must fail validation before any
+# HIP call, so they are never dereferenced
+A1, A2, A3, A4, A5 = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def fwd(**kw):
+    a = dict(q=A1, k=A2, v=A3, out=A4, lse=A5, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, D=128, scale=0.1,
+             causal=0, left=-1, right=-1, dtype=0, stream=None)
+    a.update(kw)
+    return ea.lib().mfa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["D"], a["scale"], a["causal"], a["left"], a["right"],
+                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1),
+    (dict(dtype=2), -5), (dict(dtype=-1), -5), (dict(D=96), -4), (dict(D=256), -4),
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2),
+    (dict(Hq=3, Hkv=2), -3), (dict(left=-2), -6), (dict(right=-5), -6),
+    (dict(scale=float("nan")), -7), (dict(scale=float("inf")), -7),
+    (dict(q=A1 + 2), -12), (dict(out=A4 + 8), -12), (dict(lse=A5 + 2), -12),
+    (dict(causal=2), -13), (dict(B=65536, Hq=65536, Hkv=1, Nq=128), -10),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+def dec(**kw):
+    a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, out=0x60000, lse=0x70000, B=2, Hq=8, Hkv=2, D=128,
+             page_size=16, num_pages=10, max_pages=4, scale=0.1, num_splits=0, ws=0x80000,
+             ws_bytes=1 << 30, dtype=1, stream=None)
+    a.update(kw)
+    return ea.lib().mfa_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["out"], a["lse"],
+                                     a["B"], a["Hq"], a["Hkv"], a["D"], a["page_size"],
+                                     a["num_pages"], a["max_pages"], a["scale"], a["num_splits"],
+                                     a["ws"], a["ws_bytes"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(bt=None), -1), (dict(sl=None), -1), (dict(out=None), -1),
+    (dict(dtype=5), -5), (dict(D=80), -4), (dict(B=0), -2), (dict(Hkv=3), -3),
+    (dict(page_size=32), -9), (dict(num_pages=0), -9), (dict(max_pages=0), -9),
+    (dict(scale=float("-inf")), -7), (dict(num_splits=-1), -13), (dict(ws=None), -8),
+    (dict(ws_bytes=16), -8), (dict(q=A1 + 4), -12), (dict(bt=A4 + 2), -12),
+])
+def test_decode_validation(kw, code):
+    assert dec(**kw) == code
+
+
+def test_workspace_and_splits():
+    for max_pages, ns in [(2048, 0), (64, 0), (4, 0), (2048, 1), (2048, 7), (100, 3), (9, 1000)]:
+        S = ea.mfa_decode_num_splits(16, max_pages, ns)
+        assert 1 <= S <= max_pages
+        if ns > 0:
+            assert S <= ns
+        assert ea.mfa_decode_workspace_bytes(16, 32, 128, 16, max_pages, ns) == 16 * 32 * S * 129 * 4
+    assert ea.mfa_decode_num_splits(16, 2048, 0) == 64
+    assert ea.mfa_decode_workspace_bytes(16, 32, 128, 8, 2048, 0) == 0
+    with pytest.raises(ea.MfaError):
+        ea.mfa_decode_num_splits(16, 0, 0)
+
+
+def test_last_dispatch_is_per_thread():
+    out = {}
+
+    def run():
+        try:
+            ea.mfa_last_dispatch()
+            out["r"] = "ok"
+        except ea.MfaError as e:
+            out["r"] = e.status
+
+    t = threading.Thread(target=run)
+    t.start()
+    t.join()
+    assert out["r"] == -13
