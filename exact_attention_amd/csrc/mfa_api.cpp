@@ -42,6 +42,9 @@ int check_fwd(const void* q, const void* k, const void* v, void* out, const floa
     // element counts must fit comfortably in 64-bit offsets
     const double qe = (double)B * Hq * Nq * D, ke = (double)B * Hkv * Nk * D;
     if (qe > 4e18 || ke > 4e18) return MFA_ERR_OVERFLOW;
+    // one head's rows are addressed with 32-bit byte offsets
+    if ((int64_t)Nq * D * 2 > 0x7fffffffLL || (int64_t)Nk * D * 2 > 0x7fffffffLL)
+        return MFA_ERR_OVERFLOW;
     return MFA_OK;
 }
 
@@ -98,6 +101,19 @@ int decode_splits(int max_pages, int num_splits, int* chunk_pages) {
 }
 
 }  // namespace
+
+int mfa_num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 extern "C" {
 

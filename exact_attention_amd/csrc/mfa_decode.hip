@@ -13,18 +13,22 @@
 // the slots of its own heads (the per-split slot race described on the MXFlashAttn
 // page came from lanes of invalid query heads writing into a neighbour's slot).
 //
-// Inside a workgroup (4 waves, each a contiguous run of pages of the chunk):
-//   lane = (G = lane / 16, t = lane % 16).  Page slot t is token t of the page.
-//   S = Q K^T on a 16x16x32 MFMA: the A operand holds the workgroup's query heads,
-//   replicated over the 16 rows, so that every lane's accumulator holds the scores of
-//   all those heads for token t; the B operand is read straight from the page (16-byte
-//   loads, lane group G reads one 64-byte quarter of each K row).
-//   Each lane then keeps its own running (m, l, o) per head for the tokens in slot t
-//   of its pages (o over the D/4 columns it loaded from V) — an online softmax per
-//   lane, so no cross-lane reduction is needed inside the loop.  At the end the 16
-//   slots are merged with DPP row reductions, and the 4 waves through LDS.
+// Inside a workgroup (4 waves, each a contiguous run of pages of the chunk), per page:
+//   S^T = K Q^T on a 16x16x32 MFMA, read straight from the page: the A operand holds
+//   the page's 16 token rows (lane % 16 = token, lane / 16 = 64-byte quarter of the
+//   row), the B operand the workgroup's HPW query heads replicated over the 16
+//   columns.  Lane (G = lane / 16, c = lane % 16) then holds the scores of tokens
+//   4G .. 4G+3 for head c % HPW; the other heads' scores come from the lanes of the
+//   same quad through DPP.
+//   The same lane loads one 16-byte column chunk (c) of V for those 4 tokens and keeps
+//   its own online softmax state (m, l) and output slice o[head][8] per head — so the
+//   output accumulator is 8 * HPW registers and no reduction is needed in the loop.
+//   At the end the partial states of the 4 token groups of every wave are merged in
+//   LDS (same max-rescale rule as the combine pass).
 // Tokens at or past seq_lens[b] (tail slots of the last page, which may hold any bit
-// pattern) are neither loaded nor counted: their scores are -inf and their V rows 0.
+// pattern) are never read: each page is addressed through a buffer resource whose
+// range ends at the last valid token, so such loads return zeros, and their scores
+// are set to -inf.
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -33,7 +37,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kPage = 16;
-constexpr int kPG = 2;   // pages per online-softmax step of a lane
+constexpr int kPG = 2;   // pages per online-softmax step
+constexpr float kLazy = 8.0f;
 
 struct DecArgs {
     const uint16_t* q;
@@ -56,10 +61,18 @@ __device__ __forceinline__ int clamp_len(int L, int max_pages) {
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Value of x held by the lane of this quad whose index within the quad is SRC.
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float x) {
+    constexpr int ctrl = SRC | (SRC << 2) | (SRC << 4) | (SRC << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+
 template <int D, int DT, int HPW>
-__global__ __launch_bounds__(kThreads) void mfa_decode_split_kernel(DecArgs a) {
-    constexpr int NKB = D / 32;     // 16-byte chunks per lane per K/V row
-    constexpr int NO = NKB * 8;     // output columns per lane
+__global__ __launch_bounds__(kThreads, 3) void mfa_decode_split_kernel(DecArgs a) {
+    constexpr int NKB = D / 32;       // k-steps (16-byte chunks per lane per K row)
+    constexpr int NCH = D / 8;        // 16-byte chunks per V row
+    constexpr int NT = D / 32;        // tokens per lane per page (4 for D=128, 2 for D=64)
     const int s = blockIdx.x;
     const int hg = blockIdx.y;
     const int b = blockIdx.z;
@@ -74,131 +87,171 @@ __global__ __launch_bounds__(kThreads) void mfa_decode_split_kernel(DecArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4;
-    const int t16 = lane & 15;
+    const int c = lane & 15;
     const int ppw = a.chunk_pages / kWaves;
     const int w_begin = page_begin + wave * ppw;
     const int w_end = min(w_begin + ppw, page_end);
 
-    // A operand: head (t16 % HPW) of the group, k-chunks 4*kb + G
-    mfa_u32x4 qa[NKB];
+    // B operand: query head (c % HPW) of the group, k-chunks 4*kb + G
+    mfa_u32x4 qb[NKB];
     {
-        const uint16_t* qp = a.q + ((size_t)b * a.Hq + h0 + (t16 % HPW)) * D;
+        const uint16_t* qp = a.q + ((size_t)b * a.Hq + h0 + (c % HPW)) * D;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qa[kb] = *(const mfa_u32x4*)(qp + (4 * kb + G) * 8);
+        for (int kb = 0; kb < NKB; ++kb) qb[kb] = *(const mfa_u32x4*)(qp + (4 * kb + G) * 8);
     }
 
-    float m[HPW], l[HPW], o[HPW][NO];
+    // this lane's V slice: chunk vch of tokens vt0 .. vt0 + NT - 1 of each page
+    const int vch = c % NCH;
+    const int vt0 = 4 * G + NT * (c / NCH);
+    const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
+    const uint32_t k_off = (uint32_t)(c * a.Hkv * D) * 2;            // A row = token c
+    const uint32_t v_off = (uint32_t)(vt0 * a.Hkv * D + vch * 8) * 2;
+
+    float m[HPW], l[HPW], o[HPW][8];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
         m[hh] = -MFA_INF;
         l[hh] = 0.f;
 #pragma unroll
-        for (int i = 0; i < NO; ++i) o[hh][i] = 0.f;
+        for (int i = 0; i < 8; ++i) o[hh][i] = 0.f;
     }
 
-    const size_t tok_stride = (size_t)a.Hkv * D;
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+    const size_t page_elems = (size_t)kPage * a.Hkv * D;
 
     for (int pg = w_begin; pg < w_end; pg += kPG) {
-        mfa_u32x4 kr[kPG][NKB], vr[kPG][NKB];
-        bool tv[kPG];
+        mfa_u32x4 kr[kPG][NKB], vr[kPG][NT];
+        int nv[kPG];
 #pragma unroll
         for (int j = 0; j < kPG; ++j) {
             const int pi = pg + j;
-            int pid = pi < w_end ? bt[pi] : -1;
+            const int pid = pi < w_end ? __builtin_amdgcn_readfirstlane(bt[pi]) : -1;
             const bool pvalid = pid >= 0 && pid < a.num_pages;
-            tv[j] = pvalid && (pi * kPage + t16) < L;
-            const size_t base = ((size_t)(pvalid ? pid : 0) * kPage + t16) * tok_stride + (size_t)kvh * D;
+            // valid tokens of this page (0 if the page index is out of range)
+            nv[j] = pvalid ? min(kPage, L - pi * kPage) : 0;
+            const uint16_t* base = (pvalid ? pid : 0) * page_elems + (size_t)kvh * D + a.kp;
+            const uint16_t* vbase = (pvalid ? pid : 0) * page_elems + (size_t)kvh * D + a.vp;
+            const uint32_t bytes = (uint32_t)nv[j] * tok_bytes;
+            const auto rk = mfa_rsrc(base, bytes);
+            const auto rv = mfa_rsrc(vbase, bytes);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                kr[j][kb] = tv[j] ? *(const mfa_u32x4*)(a.kp + base + (4 * kb + G) * 8) : mfa_u32x4{0, 0, 0, 0};
-                vr[j][kb] = tv[j] ? *(const mfa_u32x4*)(a.vp + base + (4 * kb + G) * 8) : mfa_u32x4{0, 0, 0, 0};
-            }
+            for (int kb = 0; kb < NKB; ++kb) kr[j][kb] = mfa_load16(rk, k_off + (4 * kb + G) * 16);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) vr[j][t] = mfa_load16(rv, v_off + t * tok_bytes);
         }
-        float sc[kPG][HPW];
+        // scores: sc[j][hh][i] for token 4G + i (i < 4) of page j, head hh
+        float sc[kPG][HPW][4];
 #pragma unroll
         for (int j = 0; j < kPG; ++j) {
             mfa_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) acc = mfa_mfma16<DT>(qa[kb], kr[j][kb], acc);
+            for (int kb = 0; kb < NKB; ++kb) acc = mfa_mfma16<DT>(kr[j][kb], qb[kb], acc);
 #pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) sc[j][hh] = tv[j] ? acc[hh] * a.scale_log2 : -MFA_INF;
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = 4 * G + i < nv[j];
+                const float x = acc[i] * a.scale_log2;
+                // head hh's score lives in the quad lane with index hh (HPW = 4),
+                // hh + 2*(k/2) (HPW = 2), or in every lane (HPW = 1)
+                if constexpr (HPW == 4) {
+                    sc[j][0][i] = valid ? quad_bcast<0>(x) : -MFA_INF;
+                    sc[j][1][i] = valid ? quad_bcast<1>(x) : -MFA_INF;
+                    sc[j][2][i] = valid ? quad_bcast<2>(x) : -MFA_INF;
+                    sc[j][3][i] = valid ? quad_bcast<3>(x) : -MFA_INF;
+                } else if constexpr (HPW == 2) {
+                    const float x0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                        __builtin_bit_cast(int, x), 0xA0, 0xf, 0xf, false));   // quad_perm 0,0,2,2
+                    const float x1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                        __builtin_bit_cast(int, x), 0xF5, 0xf, 0xf, false));   // quad_perm 1,1,3,3
+                    sc[j][0][i] = valid ? x0 : -MFA_INF;
+                    sc[j][1][i] = valid ? x1 : -MFA_INF;
+                } else {
+                    sc[j][0][i] = valid ? x : -MFA_INF;
+                }
+            }
+        }
+        // this lane's own tokens: i = NT * (c / NCH) + t (a select, not a dynamic index)
+        const bool upper = (NCH < 16) && (c >= NCH);
+        auto own = [&](int j, int hh, int t) -> float {
+            if constexpr (NCH == 16) return sc[j][hh][t];
+            else return upper ? sc[j][hh][NT + t] : sc[j][hh][t];
+        };
+        // online softmax over this lane's tokens; the offset is raised lazily
+        float mb[HPW];
+        bool raise_any = false;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            float t = -MFA_INF;
+#pragma unroll
+            for (int j = 0; j < kPG; ++j)
+#pragma unroll
+                for (int i = 0; i < NT; ++i) t = fmaxf(t, own(j, hh, i));
+            mb[hh] = t;
+            raise_any |= t > m[hh] + kLazy;
+        }
+        if (__builtin_amdgcn_ballot_w64(raise_any) != 0) {
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const bool r = mb[hh] > m[hh] + kLazy;
+                const float m_new = r ? mb[hh] : m[hh];
+                const float alpha = (m[hh] == -MFA_INF) ? 0.f : mfa_exp2(m[hh] - m_new);
+                l[hh] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[hh][i] *= alpha;
+                m[hh] = m_new;
+            }
         }
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
-            float mb = sc[0][hh];
-#pragma unroll
-            for (int j = 1; j < kPG; ++j) mb = fmaxf(mb, sc[j][hh]);
-            const float m_new = fmaxf(m[hh], mb);
-            const float m_use = (m_new == -MFA_INF) ? 0.f : m_new;
-            const float alpha = mfa_exp2(m[hh] - m_use);
-            float p[kPG];
-            float ps = 0.f;
+            const float mu = (m[hh] == -MFA_INF) ? 0.f : m[hh];
 #pragma unroll
             for (int j = 0; j < kPG; ++j) {
-                p[j] = mfa_exp2(sc[j][hh] - m_use);
-                ps += p[j];
-            }
-            l[hh] = l[hh] * alpha + ps;
-            m[hh] = m_new;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                for (int t = 0; t < NT; ++t) {
+                    const float x = own(j, hh, t);
+                    const float p = (x == -MFA_INF) ? 0.f : mfa_exp2(x - mu);
+                    l[hh] += p;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float x0 = o[hh][kb * 8 + 2 * e2] * alpha;
-                    float x1 = o[hh][kb * 8 + 2 * e2 + 1] * alpha;
-#pragma unroll
-                    for (int j = 0; j < kPG; ++j) {
-                        x0 += p[j] * mfa_lo<DT>(vr[j][kb][e2]);
-                        x1 += p[j] * mfa_hi<DT>(vr[j][kb][e2]);
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        o[hh][2 * e2] += p * mfa_lo<DT>(vr[j][t][e2]);
+                        o[hh][2 * e2 + 1] += p * mfa_hi<DT>(vr[j][t][e2]);
                     }
-                    o[hh][kb * 8 + 2 * e2] = x0;
-                    o[hh][kb * 8 + 2 * e2 + 1] = x1;
                 }
             }
         }
     }
 
-    // merge the 16 token slots of each DPP row (same columns, different tokens)
-    __shared__ float sm_m[kWaves][HPW];
-    __shared__ float sm_l[kWaves][HPW];
-    __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HPW][D];
+    // merge the partial states in LDS: for each head, NP partials of (m, l, o[D])
+    constexpr int GROUPS = 4 * (16 / NCH);           // token groups per wave
+    constexpr int NP = kWaves * GROUPS;               // partials per head
+    __shared__ float sm_m[HPW][NP];
+    __shared__ float sm_l[HPW][NP];
+    __shared__ __attribute__((aligned(16))) float sm_o[HPW][NP][D];
+    const int part = wave * GROUPS + G * (16 / NCH) + c / NCH;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-        const float M = mfa_row16_max(m[hh]);
-        const float f = (m[hh] == -MFA_INF) ? 0.f : mfa_exp2(m[hh] - M);
-        const float lr = mfa_row16_sum(l[hh] * f);
-#pragma unroll
-        for (int i = 0; i < NO; ++i) o[hh][i] = mfa_row16_sum(o[hh][i] * f);
-        if (t16 == 0) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float* dst = &sm_o[wave][hh][(4 * kb + G) * 8];
-                *(mfa_f32x4*)dst = mfa_f32x4{o[hh][kb * 8 + 0], o[hh][kb * 8 + 1], o[hh][kb * 8 + 2], o[hh][kb * 8 + 3]};
-                *(mfa_f32x4*)(dst + 4) = mfa_f32x4{o[hh][kb * 8 + 4], o[hh][kb * 8 + 5], o[hh][kb * 8 + 6], o[hh][kb * 8 + 7]};
-            }
-            if (G == 0) {
-                sm_m[wave][hh] = M;
-                sm_l[wave][hh] = lr;
-            }
+        float* dst = &sm_o[hh][part][vch * 8];
+        *(mfa_f32x4*)dst = mfa_f32x4{o[hh][0], o[hh][1], o[hh][2], o[hh][3]};
+        *(mfa_f32x4*)(dst + 4) = mfa_f32x4{o[hh][4], o[hh][5], o[hh][6], o[hh][7]};
+        if (vch == 0) {
+            sm_m[hh][part] = m[hh];
+            sm_l[hh][part] = l[hh];
         }
     }
     __syncthreads();
 
-    // merge the waves and write this split's partial (O_s, LSE_s) per head
     for (int idx = tid; idx < HPW * D; idx += kThreads) {
         const int hh = idx / D, d = idx - hh * D;
         float M = -MFA_INF;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
+        for (int p = 0; p < NP; ++p) M = fmaxf(M, sm_m[hh][p]);
         float lt = 0.f, ot = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = (sm_m[w][hh] == -MFA_INF) ? 0.f : mfa_exp2(sm_m[w][hh] - M);
-            lt += f * sm_l[w][hh];
-            ot += f * sm_o[w][hh][d];
+        for (int p = 0; p < NP; ++p) {
+            const float f = (sm_m[hh][p] == -MFA_INF) ? 0.f : mfa_exp2(sm_m[hh][p] - M);
+            lt += f * sm_l[hh][p];
+            ot += f * sm_o[hh][p][d];
         }
         const size_t slot = ((size_t)b * a.Hq + h0 + hh) * a.S + s;
         a.ws_o[slot * D + d] = lt > 0.f ? ot / lt : 0.f;
@@ -206,18 +259,24 @@ __global__ __launch_bounds__(kThreads) void mfa_decode_split_kernel(DecArgs a) {
     }
 }
 
+// One workgroup of 4 waves per (sequence, head).  Wave w merges the splits
+// s = w, w + 4, ...: lane s % 64 holds a split's LSE, the weights are broadcast with
+// readlane and every lane accumulates D/64 columns; the 4 waves are then merged in LDS.
 template <int D, int DT>
-__global__ __launch_bounds__(64) void mfa_decode_combine_kernel(DecArgs a) {
+__global__ __launch_bounds__(256) void mfa_decode_combine_kernel(DecArgs a) {
     constexpr int PER = D / 64;
+    constexpr int NW = 4;
     const int bh = blockIdx.x;
     const int b = bh / a.Hq;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int L = clamp_len(a.seq_lens[b], a.max_pages);
     const int n_pages_b = (L + kPage - 1) / kPage;
     const int n_used = (n_pages_b + a.chunk_pages - 1) / a.chunk_pages;
     const float* lse_s = a.ws_lse + (size_t)bh * a.S;
     const float* o_s = a.ws_o + (size_t)bh * a.S * D;
 
+    // global max of the split LSEs (every wave computes it)
     float M = -MFA_INF;
     for (int s = lane; s < n_used; s += 64) M = fmaxf(M, lse_s[s]);
 #pragma unroll
@@ -228,22 +287,55 @@ __global__ __launch_bounds__(64) void mfa_decode_combine_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
     float W = 0.f;
-    for (int s = 0; s < n_used; ++s) {
-        const float ls = lse_s[s];
+    // wave w takes splits w, w + NW, ...; 64 of them per pass
+    for (int base = wave; base < n_used; base += 64 * NW) {
+        const int s = base + NW * lane;
+        const float ls = s < n_used ? lse_s[s] : -MFA_INF;
         const float w = (ls == -MFA_INF) ? 0.f : mfa_exp2(ls - M_use);
-        W += w;
+        float wsum = w;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += w * o_s[(size_t)s * D + lane * PER + i];
+        for (int x = 32; x >= 1; x >>= 1) wsum += __shfl_xor(wsum, x, 64);
+        W += wsum;
+        const int n = min(64, (n_used - base + NW - 1) / NW);
+#pragma unroll 8
+        for (int k = 0; k < n; ++k) {
+            const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+            const float* src = o_s + (size_t)(base + NW * k) * D + lane * PER;
+            if constexpr (PER == 2) {
+                const float2 v = *(const float2*)src;
+                acc[0] += wk * v.x;
+                acc[1] += wk * v.y;
+            } else {
+                acc[0] += wk * src[0];
+            }
+        }
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
+    __shared__ float sm_acc[NW][D];
+    __shared__ float sm_w[NW];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sm_acc[wave][lane * PER + i] = acc[i];
+    if (lane == 0) sm_w[wave] = W;
+    __syncthreads();
+    if (wave != 0) return;
+    float Wt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Wt += sm_w[w];
+    float o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        o[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) o[i] += sm_acc[w][lane * PER + i];
+    }
+    const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
     uint16_t* op = a.out + (size_t)bh * D + lane * PER;
     if constexpr (PER == 2) {
-        *(uint32_t*)op = mfa_pack2<DT>(acc[0] * inv, acc[1] * inv);
+        *(uint32_t*)op = mfa_pack2<DT>(o[0] * inv, o[1] * inv);
     } else {
-        const uint32_t w2 = mfa_pack2<DT>(acc[0] * inv, 0.f);
+        const uint32_t w2 = mfa_pack2<DT>(o[0] * inv, 0.f);
         *op = (uint16_t)(w2 & 0xffffu);
     }
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = W > 0.f ? (M_use + mfa_log2(W)) * MFA_LN2 : -MFA_INF;
+    if (a.lse != nullptr && lane == 0) a.lse[bh] = Wt > 0.f ? (M_use + mfa_log2(Wt)) * MFA_LN2 : -MFA_INF;
 }
 
 template <int D, int DT, int HPW>
@@ -251,7 +343,7 @@ int launch(const DecArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
     const dim3 grid1((unsigned)a.S, (unsigned)(a.Hq / HPW), (unsigned)a.B);
     hipLaunchKernelGGL((mfa_decode_split_kernel<D, DT, HPW>), grid1, dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
-    hipLaunchKernelGGL((mfa_decode_combine_kernel<D, DT>), dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_combine_kernel<D, DT>), dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     snprintf(info->kernel, sizeof(info->kernel), "mfa_decode_split_kernel<D=%d,%s,HPW=%d>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", HPW);

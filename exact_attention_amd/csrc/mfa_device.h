@@ -70,6 +70,35 @@ __device__ __forceinline__ float mfa_hi(uint32_t w) {
 }
 
 __device__ __forceinline__ float mfa_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum of the two 16-bit values of a packed word, accumulated into c in fp32.
+template <int DT>
+__device__ __forceinline__ float mfa_sum2(uint32_t w, float c) {
+    if constexpr (DT == MFA_DT_F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), one, c, false);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), one, c, false);
+    }
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero, with no
+// branch and a 32-bit per-lane offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mfa_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ mfa_u32x4 mfa_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(mfa_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t mfa_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ mfa_u32x2 mfa_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(mfa_u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ float mfa_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Value of x held by lane (lane ^ 32).

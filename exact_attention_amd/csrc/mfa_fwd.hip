@@ -12,26 +12,37 @@
 //   One workgroup = 4 waves = one query tile of BM = 128 rows of one (batch, head).
 //   Each wave owns 32 query rows.  Key tiles of BN keys are streamed through LDS,
 //   double-buffered: the global loads of tile j+1 are in flight while tile j is
-//   consumed, and one barrier per tile separates the buffers.
+//   consumed, and one barrier per tile separates the buffers.  Global loads go
+//   through buffer resources, whose range check returns zeros past the last key row.
 //
 // Per wave and key tile (32x32x16 MFMA, fp32 accumulate):
 //   S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T held in registers for the whole
 //     kernel.  The accumulator puts one query row in each lane (lane % 32) and 16 of
 //     the 32 keys of a block in its registers, so the row max needs one exchange with
 //     lane ^ 32 and the row sum none until the end.
-//   The K rows fed to the A operand are permuted (pi below) so that accumulator
+//   The K rows fed to the A operand are permuted (key_perm) so that accumulator
 //   register r of lane half g holds key 16*(r/8) + 8*g + r%8: each lane then owns runs
 //   of 8 consecutive keys, which is exactly the B operand layout of the next product.
 //   O^T += V^T P^T: A = V^T from LDS (V is transposed while it is written to LDS),
 //     B = P^T straight from the softmax registers (rounded to the input type).  The
-//     O^T accumulator again has one query row per lane, so the rescale by alpha is a
-//     per-lane scalar multiply.
+//     O^T accumulator again has one query row per lane, so rescaling is a per-lane
+//     scalar multiply.
+//
+// Softmax details (all in the log2 domain; scale * log2(e) is folded into one FMA that
+// feeds the exponential):
+//   * The running max used as the exponent offset is only raised when a row's new
+//     maximum exceeds it by more than 2^8 (kLazy), so P <= 256 and O, l are rescaled
+//     only on those (rare) tiles; the result is the same up to rounding because the
+//     offset cancels in O = o / l and enters LSE as m + log2 l.
+//   * For fp16, l accumulates the P values after rounding to fp16 (one dot2 per pair),
+//     i.e. exactly the weights the P V product uses; for bf16, whose rounding is 8x
+//     coarser, l sums the fp32 values so that the LSE keeps fp32 accuracy.
 //
 // Masking and skipping (mlx-mfa 2.5.2 features "Causal tile-skip", "Sliding window";
 // mlx-bun forward shader's fully-masked-tile guard): the workgroup visits only the key
 // tiles of mfa_tile_range; element masks are applied only on tiles that
-// mfa_tile_full rejects; a row whose running max is still -inf uses 0 as the
-// subtrahend so exp never sees (-inf) - (-inf).
+// mfa_tile_full rejects; a row whose offset is still -inf uses 0 in its place so exp
+// never sees (-inf) - (-inf), and masked scores get P = 0 explicitly.
 #include "mfa_device.h"
 #include "mfa_geometry.h"
 #include "mfa_internal.h"
@@ -40,6 +51,7 @@ namespace {
 
 constexpr int kBM = 128;
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;
 
 struct FwdArgs {
     const uint16_t* q;
@@ -52,7 +64,8 @@ struct FwdArgs {
     int n_q_tiles;
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
-    float scale_log2;
+    int snake;       // 1: pair heavy and light query tiles (grid fits in one pass)
+    float scale_log2_abs;  // |scale| * log2(e)
     MfaMask mask;
 };
 
@@ -65,28 +78,25 @@ template <int D, int BN>
 struct Tile {
     static constexpr int KCH = D / 8;              // 16-byte chunks per K row
     static constexpr int VCH = BN / 8;             // 16-byte chunks per V^T row
-    static constexpr int K_ELEMS = BN * D;         // 16-bit elements per K tile
-    static constexpr int V_ELEMS = D * BN;
+    // Rows are padded by 16 bytes: 16 consecutive rows read at one column then fall
+    // into 16 distinct 16-byte bank groups (conflict-free MFMA operand reads), and
+    // every operand address is a per-lane base plus a compile-time offset.
+    static constexpr int KP = D + 8;               // K row pitch (elements)
+    static constexpr int VP = BN + 8;              // V^T row pitch (elements)
+    static constexpr int K_ELEMS = BN * KP;        // 16-bit elements per K buffer
+    static constexpr int V_ELEMS = D * VP;
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
     static constexpr int K_LOADS = BN * KCH / kThreads;   // 16-byte K loads per thread
-    static constexpr int QUADS = D / 4;                   // 4-element column groups of V
+    static constexpr int VW = D * BN / (8 * kThreads);    // V columns per thread (8 keys each)
+    static constexpr int VGROUPS = D / VW;                // column groups of V
     static_assert(BN * KCH % kThreads == 0, "K tile must split evenly");
-    static_assert(QUADS * (BN / 8) == kThreads, "V tile: one 8x4 block per thread");
+    static_assert(VW == 2 || VW == 4, "V tile: one 8-key x VW-column block per thread");
 
-    // XOR swizzles on 16-byte chunks keep the MFMA operand reads free of LDS bank
-    // conflicts: 16 consecutive rows at one logical chunk land in 16 distinct
-    // 16-byte bank groups.
-    __device__ static __forceinline__ int k_off(int row, int ch) {
-        int phys = (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
-        return row * D + phys * 8;
-    }
-    __device__ static __forceinline__ int v_off(int d, int ch) {
-        int phys = (VCH == 16) ? (ch ^ (d & 15)) : (ch ^ ((d >> 1) & 7));
-        return K_ELEMS + d * BN + phys * 8;
-    }
+    __device__ static __forceinline__ int k_off(int row, int ch) { return row * KP + ch * 8; }
+    __device__ static __forceinline__ int v_off(int d, int ch) { return K_ELEMS + d * VP + ch * 8; }
 };
 
-template <int D, int DT, int BN, bool TILELOG>
+template <int D, int DT, int BN, bool TILELOG, bool NEG>
 __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     using T = Tile<D, BN>;
     constexpr int NKB = D / 16;   // k-steps of S^T = K Q^T
@@ -101,11 +111,19 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
 
-    // ---- which (query tile, batch, head): longest causal tiles first -------------
+    // ---- which (query tile, batch, head) -------------------------------------------
     const int id = blockIdx.x;
     const int round = id / a.HB;
     const int w = id - round * a.HB;
-    const int qt = a.n_q_tiles - 1 - round;
+    int qt;
+    if (a.snake) {
+        // first half of the grid: heaviest tiles downwards; second half: lightest
+        // upwards, so the two workgroups sharing a CU carry complementary work
+        const int half = (a.n_q_tiles + 1) >> 1;
+        qt = round < half ? a.n_q_tiles - 1 - round : round - half;
+    } else {
+        qt = a.n_q_tiles - 1 - round;   // longest first
+    }
     int b, h;
     if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
@@ -126,19 +144,19 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
 
     const size_t head_q = (size_t)(b * a.Hq + h) * (size_t)a.Nq;
     const size_t head_kv = (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk;
-    const uint16_t* __restrict__ kg = a.k + head_kv * D;
-    const uint16_t* __restrict__ vg = a.v + head_kv * D;
+    const uint16_t* kg = a.k + head_kv * D;
+    const uint16_t* vg = a.v + head_kv * D;
 
     const int qrow = q0 + wave * 32 + l32;
     const bool qvalid = qrow < a.Nq;
 
-    // ---- Q^T operand in registers ------------------------------------------------
+    // ---- Q^T operand in registers (rows past Nq read as zero) --------------------
     mfa_u32x4 qreg[NKB];
     {
-        const uint16_t* qp = a.q + (head_q + (size_t)(qvalid ? qrow : 0)) * D + g32 * 8;
+        const auto rq = mfa_rsrc(a.q + head_q * D, (uint32_t)a.Nq * D * 2);
+        const uint32_t off = ((uint32_t)qrow * D + g32 * 8) * 2;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-            qreg[kb] = qvalid ? *(const mfa_u32x4*)(qp + kb * 16) : mfa_u32x4{0, 0, 0, 0};
+        for (int kb = 0; kb < NKB; ++kb) qreg[kb] = mfa_load16(rq, off + kb * 32);
     }
 
     // per-row visible key bounds (inclusive), clamped into int range
@@ -150,31 +168,39 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     mfa_f32x16 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = mfa_f32x16{};
-    float m_run = -MFA_INF;
-    float l_run = 0.f;
+    float m_run = -MFA_INF;   // exponent offset (log2 domain, scaled)
+    float l_run = 0.f;        // this lane's half of the row sum
 
     // ---- loader mapping ----------------------------------------------------------
-    // K: 16-byte chunks; V: an 8-key x 4-column block per thread, transposed into V^T.
-    const int v_c4 = tid % T::QUADS;
-    const int v_a = tid / T::QUADS;
+    // K: 16-byte chunks; V: an 8-key x VW-column block per thread, transposed into V^T.
+    constexpr int VW = T::VW;
+    const int v_c = tid % T::VGROUPS;
+    const int v_a = tid / T::VGROUPS;
+    uint32_t k_voff[T::K_LOADS];
+#pragma unroll
+    for (int p = 0; p < T::K_LOADS; ++p) {
+        const int c = p * kThreads + tid;
+        k_voff[p] = (uint32_t)((c / T::KCH) * D + (c % T::KCH) * 8) * 2;
+    }
+    const uint32_t v_voff = (uint32_t)(v_a * 8 * D + v_c * VW) * 2;
     mfa_u32x4 kreg[T::K_LOADS];
-    mfa_u32x2 vreg[8];
+    mfa_u32x2 vreg[8];   // VW == 2 uses the first word only
 
     auto load_tile = [&](int kt) {
         const int k0 = kt * BN;
+        const uint32_t bytes = (uint32_t)(a.Nk - k0) * D * 2;
+        const auto rk = mfa_rsrc(kg + (size_t)k0 * D, bytes);
+        const auto rv = mfa_rsrc(vg + (size_t)k0 * D, bytes);
 #pragma unroll
-        for (int p = 0; p < T::K_LOADS; ++p) {
-            const int c = p * kThreads + tid;
-            const int row = c / T::KCH, ch = c % T::KCH;
-            const int key = k0 + row;
-            kreg[p] = key < a.Nk ? *(const mfa_u32x4*)(kg + (size_t)key * D + ch * 8)
-                                 : mfa_u32x4{0, 0, 0, 0};
-        }
+        for (int p = 0; p < T::K_LOADS; ++p) kreg[p] = mfa_load16(rk, k_voff[p]);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int key = k0 + v_a * 8 + r;
-            vreg[r] = key < a.Nk ? *(const mfa_u32x2*)(vg + (size_t)key * D + v_c4 * 4)
-                                 : mfa_u32x2{0, 0};
+            if constexpr (VW == 4) {
+                vreg[r] = mfa_load8(rv, v_voff + r * D * 2);
+            } else {
+                vreg[r][0] = mfa_load4(rv, v_voff + r * D * 2);
+                vreg[r][1] = 0;
+            }
         }
     };
     auto store_tile = [&](int buf) {
@@ -182,20 +208,20 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int p = 0; p < T::K_LOADS; ++p) {
             const int c = p * kThreads + tid;
-            const int row = c / T::KCH, ch = c % T::KCH;
-            *(mfa_u32x4*)(s + T::k_off(row, ch)) = kreg[p];
+            *(mfa_u32x4*)(s + T::k_off(c / T::KCH, c % T::KCH)) = kreg[p];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < VW; ++e) {
             const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
             mfa_u32x4 col;
 #pragma unroll
             for (int m2 = 0; m2 < 4; ++m2)
                 col[m2] = __builtin_amdgcn_perm(vreg[2 * m2 + 1][e >> 1], vreg[2 * m2][e >> 1], sel);
-            *(mfa_u32x4*)(s + T::v_off(v_c4 * 4 + e, v_a)) = col;
+            *(mfa_u32x4*)(s + T::v_off(v_c * VW + e, v_a)) = col;
         }
     };
 
+    const float sl2 = a.scale_log2_abs;
     int n_visit = 0, n_edge = 0;
     if (kt_lo < kt_hi) {
         load_tile(kt_lo);
@@ -209,41 +235,59 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
         if (has_next) load_tile(kt + 1);
         const uint16_t* s = smem + cur * T::BUF_ELEMS;
 
-        // S^T = K Q^T for the NNB 32-key blocks of the tile
+        // S^T = K Q^T for the NNB 32-key blocks of the tile (independent chains)
         mfa_f32x16 sacc[NNB];
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) {
-            sacc[nb] = mfa_f32x16{};
-            const int krow = nb * 32 + key_perm(l32);
+        for (int nb = 0; nb < NNB; ++nb) sacc[nb] = mfa_f32x16{};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                const int krow = nb * 32 + key_perm(l32);
                 const mfa_u32x4 kop = *(const mfa_u32x4*)(s + T::k_off(krow, 2 * kb + g32));
                 sacc[nb] = mfa_mfma32<DT>(kop, qreg[kb], sacc[nb]);
             }
         }
 
-        // scale into the log2 domain, mask edge tiles, online softmax
+        // signed raw scores (the sign of scale folded in), masked on edge tiles
         const bool edge = !mfa_tile_full(a.mask, kBM, BN, qt, kt);
         const int k0 = kt * BN;
         float tmax = -MFA_INF;
+        if (edge) {
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) {
+            for (int nb = 0; nb < NNB; ++nb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[nb][r] * a.scale_log2;
-                if (edge) {
+                for (int r = 0; r < 16; ++r) {
                     const int key = k0 + nb * 32 + 16 * (r >> 3) + 8 * g32 + (r & 7);
-                    x = (key >= row_lo && key <= row_hi) ? x : -MFA_INF;
+                    const float x = NEG ? -sacc[nb][r] : sacc[nb][r];
+                    sacc[nb][r] = (key >= row_lo && key <= row_hi) ? x : -MFA_INF;
+                    tmax = fmaxf(tmax, sacc[nb][r]);
                 }
-                sacc[nb][r] = x;
-                tmax = fmaxf(tmax, x);
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (NEG) sacc[nb][r] = -sacc[nb][r];
+                    tmax = fmaxf(tmax, sacc[nb][r]);
+                }
             }
         }
         tmax = fmaxf(tmax, mfa_swap_halves(tmax));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -MFA_INF) ? 0.f : m_new;
-        const float alpha = mfa_exp2(m_run - m_use);
-        float psum = 0.f;
+        // raise the offset only when the row max outgrows it by more than kLazy
+        const float tmax_s = (tmax == -MFA_INF) ? -MFA_INF : tmax * sl2;
+        const bool raise = tmax_s > m_run + kLazy;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float m_new = raise ? tmax_s : m_run;
+            const float alpha = (m_run == -MFA_INF) ? 0.f : mfa_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -MFA_INF) ? 0.f : m_run;
+
         mfa_u32x4 pop[NNB][2];
 #pragma unroll
         for (int nb = 0; nb < NNB; ++nb) {
@@ -251,29 +295,37 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
-                    const float p0 = mfa_exp2(sacc[nb][8 * hh + 2 * e2] - m_use);
-                    const float p1 = mfa_exp2(sacc[nb][8 * hh + 2 * e2 + 1] - m_use);
-                    psum += p0 + p1;
-                    pop[nb][hh][e2] = mfa_pack2<DT>(p0, p1);
+                    const float x0 = sacc[nb][8 * hh + 2 * e2];
+                    const float x1 = sacc[nb][8 * hh + 2 * e2 + 1];
+                    float p0 = mfa_exp2(__builtin_fmaf(x0, sl2, -m_use));
+                    float p1 = mfa_exp2(__builtin_fmaf(x1, sl2, -m_use));
+                    if (edge) {
+                        p0 = (x0 == -MFA_INF) ? 0.f : p0;
+                        p1 = (x1 == -MFA_INF) ? 0.f : p1;
+                    }
+                    const uint32_t pk = mfa_pack2<DT>(p0, p1);
+                    pop[nb][hh][e2] = pk;
+                    // f16: sum the rounded weights with one dot2 (rounding 2^-12);
+                    // bf16 rounds too coarsely (2^-9) for the LSE, so sum in fp32
+                    if constexpr (DT == MFA_DT_F16)
+                        l_run = mfa_sum2<DT>(pk, l_run);
+                    else
+                        l_run += p0 + p1;
                 }
             }
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T (the NDB accumulators are independent chains)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + l32;
+        for (int nb = 0; nb < NNB; ++nb) {
 #pragma unroll
-            for (int nb = 0; nb < NNB; ++nb) {
+            for (int hh = 0; hh < 2; ++hh) {
+                mfa_u32x4 vop[NDB];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const mfa_u32x4 vop = *(const mfa_u32x4*)(s + T::v_off(d, 4 * nb + 2 * hh + g32));
-                    oacc[db] = mfa_mfma32<DT>(vop, pop[nb][hh], oacc[db]);
-                }
+                for (int db = 0; db < NDB; ++db)
+                    vop[db] = *(const mfa_u32x4*)(s + T::v_off(db * 32 + l32, 4 * nb + 2 * hh + g32));
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] = mfa_mfma32<DT>(vop[db], pop[nb][hh], oacc[db]);
             }
         }
 
@@ -312,16 +364,25 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     }
 }
 
+template <int D, int DT, int BN, bool TL>
+void launch_sign(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t stream, bool neg) {
+    if (neg)
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, TL, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, TL, false>), grid, block, 0, stream, a);
+}
+
 template <int D, int DT, int BN>
-int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, mfa_dispatch_info* info) {
+int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, bool neg, mfa_dispatch_info* info) {
     const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
     const dim3 block(kThreads);
     if (tilelog)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, true>), grid, block, 0, stream, a);
+        launch_sign<D, DT, BN, true>(a, grid, block, stream, neg);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, false>), grid, block, 0, stream, a);
-    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, BN, tilelog ? ",tilelog" : "");
+        launch_sign<D, DT, BN, false>(a, grid, block, stream, neg);
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d%s%s>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, BN, tilelog ? ",tilelog" : "",
+             neg ? ",neg" : "");
     info->BM = kBM;
     info->BN = BN;
     info->waves = kThreads / 64;
@@ -334,7 +395,7 @@ int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, mfa_dispatch_info
 
 }  // namespace
 
-int mfa_fwd_bn(int D) { return D == 128 ? 64 : 128; }
+int mfa_fwd_bn(int) { return 64; }
 int mfa_fwd_bm() { return kBM; }
 
 int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_info* info) {
@@ -354,13 +415,16 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.n_q_tiles = (pr.Nq + kBM - 1) / kBM;
     a.HB = pr.B * pr.Hq;
     a.xcd_group = ((pr.B * pr.Hkv) % 8 == 0) ? 1 : 0;
-    a.scale_log2 = pr.scale * 1.4426950408889634f;
+    // heavy/light pairing helps when every workgroup is resident at once (2 per CU)
+    a.snake = (pr.causal && (long long)a.n_q_tiles * a.HB <= 2LL * mfa_num_cus()) ? 1 : 0;
+    a.scale_log2_abs = fabsf(pr.scale) * 1.4426950408889634f;
     a.mask = mfa_make_mask(pr.Nq, pr.Nk, pr.causal, pr.left, pr.right);
     const bool tl = pr.tile_log != nullptr;
+    const bool neg = pr.scale < 0.f;
     if (pr.D == 128) {
-        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, 64>(a, stream, tl, info)
-                                   : launch<128, MFA_DT_BF16, 64>(a, stream, tl, info);
+        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, 64>(a, stream, tl, neg, info)
+                                   : launch<128, MFA_DT_BF16, 64>(a, stream, tl, neg, info);
     }
-    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, 128>(a, stream, tl, info)
-                               : launch<64, MFA_DT_BF16, 128>(a, stream, tl, info);
+    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, 64>(a, stream, tl, neg, info)
+                               : launch<64, MFA_DT_BF16, 64>(a, stream, tl, neg, info);
 }

@@ -36,6 +36,9 @@ struct MfaDecodeProblem {
     int dtype;
 };
 
+// Compute units of the current device (cached per device).
+int mfa_num_cus();
+
 int mfa_fwd_bm();
 int mfa_fwd_bn(int D);
 int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
