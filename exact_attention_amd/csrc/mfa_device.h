@@ -93,6 +93,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mfa_rsrc(const void* base, uin
 __device__ __forceinline__ mfa_u32x4 mfa_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(mfa_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void mfa_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// names 4 consecutive 16-bit values (row i/4, columns 4*(i%4) .. +3 of a 4 x 16 block)
+// and receives column i of the block (rows 0..3), packed low to high.
+__device__ __forceinline__ mfa_u32x2 mfa_lds_read_tr16(const void* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(mfa_u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<void*>(p))));
+}
+
 __device__ __forceinline__ uint32_t mfa_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

@@ -6,14 +6,13 @@
 // per key tile, m' = max(m, rowmax S); alpha = exp(m - m'); P = exp(S - m');
 // l = alpha * l + rowsum P; O = alpha * O + P V; at the end O / l and m + log l.
 // That shader runs one thread per query row with scalar dot products; here both
-// contractions run on the CDNA4 matrix cores instead.
+// contractions run on the CDNA4 matrix cores and the loop is software-pipelined.
 //
 // Work decomposition
-//   One workgroup = 4 waves = one query tile of BM = 128 rows of one (batch, head).
-//   Each wave owns 32 query rows.  Key tiles of BN keys are streamed through LDS,
-//   double-buffered: the global loads of tile j+1 are in flight while tile j is
-//   consumed, and one barrier per tile separates the buffers.  Global loads go
-//   through buffer resources, whose range check returns zeros past the last key row.
+//   One workgroup = 4 waves = one query tile of BM = 128 rows of one (batch, head);
+//   each wave owns 32 query rows.  Key tiles of BN = 64 keys stream through LDS:
+//   K and V tiles are copied global -> LDS directly (buffer loads with the LDS bit;
+//   the range check returns zeros past the last key row), double-buffered.
 //
 // Per wave and key tile (32x32x16 MFMA, fp32 accumulate):
 //   S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T held in registers for the whole
@@ -23,17 +22,23 @@
 //   The K rows fed to the A operand are permuted (key_perm) so that accumulator
 //   register r of lane half g holds key 16*(r/8) + 8*g + r%8: each lane then owns runs
 //   of 8 consecutive keys, which is exactly the B operand layout of the next product.
-//   O^T += V^T P^T: A = V^T from LDS (V is transposed while it is written to LDS),
-//     B = P^T straight from the softmax registers (rounded to the input type).  The
-//     O^T accumulator again has one query row per lane, so rescaling is a per-lane
-//     scalar multiply.
+//   O^T += V^T P^T: A = V^T read from the row-major V tile with the gfx950 transposing
+//     LDS read (ds_read_b64_tr_b16: 16 lanes read a 4-key x 16-column block and each
+//     receives one column), B = P^T straight from the softmax registers (rounded to
+//     the input type).  The O^T accumulator again has one query row per lane.
 //
-// Softmax details (all in the log2 domain; scale * log2(e) is folded into one FMA that
-// feeds the exponential):
-//   * The running max used as the exponent offset is only raised when a row's new
-//     maximum exceeds it by more than 2^8 (kLazy), so P <= 256 and O, l are rescaled
-//     only on those (rare) tiles; the result is the same up to rounding because the
-//     offset cancels in O = o / l and enters LSE as m + log2 l.
+// Pipeline (iteration j, with S(j) already computed):
+//   issue the direct loads of K(j+2) and V(j+1);
+//   row max of S(j) (raise the exponent offset if needed, rescale O and l);
+//   the 16 MFMAs of S(j+1) = K(j+1) Q^T interleaved with the exponentials of S(j);
+//   the 16 MFMAs of O += V(j)^T P(j)^T;  wait for the loads;  one barrier.
+//   So the matrix cores work on tile j+1 while the vector ALUs finish tile j.
+//
+// Softmax details (log2 domain; scale * log2(e) is folded into one FMA that feeds
+// the exponential):
+//   * The exponent offset is only raised when a row's new maximum exceeds it by more
+//     than 2^8 (kLazy), so P <= 256 and O, l are rescaled only on those (rare) tiles;
+//     the offset cancels in O = o / l and enters LSE as m + log2 l.
 //   * For fp16, l accumulates the P values after rounding to fp16 (one dot2 per pair),
 //     i.e. exactly the weights the P V product uses; for bf16, whose rounding is 8x
 //     coarser, l sums the fp32 values so that the LSE keeps fp32 accuracy.
@@ -41,8 +46,9 @@
 // Masking and skipping (mlx-mfa 2.5.2 features "Causal tile-skip", "Sliding window";
 // mlx-bun forward shader's fully-masked-tile guard): the workgroup visits only the key
 // tiles of mfa_tile_range; element masks are applied only on tiles that
-// mfa_tile_full rejects; a row whose offset is still -inf uses 0 in its place so exp
-// never sees (-inf) - (-inf), and masked scores get P = 0 explicitly.
+// mfa_tile_full rejects (the invisible scores become -inf, so exp2 gives P = 0); a
+// row whose offset is still -inf uses 0 in its place so exp never sees
+// (-inf) - (-inf).
 #include "mfa_device.h"
 #include "mfa_geometry.h"
 #include "mfa_internal.h"
@@ -50,6 +56,7 @@
 namespace {
 
 constexpr int kBM = 128;
+constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.0f;
 
@@ -69,45 +76,47 @@ struct FwdArgs {
     MfaMask mask;
 };
 
+template <int N>
+struct MfaInt {
+    static constexpr int value = N;
+};
+
 // K row (within a 32-key block) fed to A-operand row i.
 __device__ __forceinline__ int key_perm(int i) {
     return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
 }
 
-template <int D, int BN>
+template <int D>
 struct Tile {
-    static constexpr int KCH = D / 8;              // 16-byte chunks per K row
-    static constexpr int VCH = BN / 8;             // 16-byte chunks per V^T row
-    // Rows are padded by 16 bytes: 16 consecutive rows read at one column then fall
-    // into 16 distinct 16-byte bank groups (conflict-free MFMA operand reads), and
-    // every operand address is a per-lane base plus a compile-time offset.
-    static constexpr int KP = D + 8;               // K row pitch (elements)
-    static constexpr int VP = BN + 8;              // V^T row pitch (elements)
-    static constexpr int K_ELEMS = BN * KP;        // 16-bit elements per K buffer
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int K_LOADS = BN * KCH / kThreads;   // 16-byte K loads per thread
-    static constexpr int VW = D * BN / (8 * kThreads);    // V columns per thread (8 keys each)
-    static constexpr int VGROUPS = D / VW;                // column groups of V
-    static_assert(BN * KCH % kThreads == 0, "K tile must split evenly");
-    static_assert(VW == 2 || VW == 4, "V tile: one 8-key x VW-column block per thread");
-
-    __device__ static __forceinline__ int k_off(int row, int ch) { return row * KP + ch * 8; }
-    __device__ static __forceinline__ int v_off(int d, int ch) { return K_ELEMS + d * VP + ch * 8; }
+    static constexpr int KCH = D / 8;                   // 16-byte chunks per row
+    static constexpr int ELEMS = kBN * D;               // 16-bit elements per K or V tile
+    static constexpr int LOADS = kBN * KCH / kThreads;  // 16-byte direct loads per thread
+    // XOR swizzles on 16-byte chunks (rows are unpadded so that a wave's direct load
+    // fills 1 KiB of consecutive LDS).  K: the 16 rows one MFMA operand read touches at
+    // a logical chunk land in 16 distinct bank groups.  V: the 4 rows x 32 bytes of a
+    // transposing read land in distinct banks.
+    __device__ static __forceinline__ int k_phys(int row, int ch) {
+        return (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
+    }
+    __device__ static __forceinline__ int v_phys(int row, int ch) {
+        return (KCH == 16) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
+    }
 };
 
-template <int D, int DT, int BN, bool TILELOG, bool NEG>
+template <int D, int DT, bool TILELOG, bool NEG>
 __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
-    using T = Tile<D, BN>;
+    using T = Tile<D>;
+    constexpr int BN = kBN;
     constexpr int NKB = D / 16;   // k-steps of S^T = K Q^T
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NNB = BN / 32;  // 32-key blocks of a tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
+    // K buffers 0, 1 then V buffers 0, 1
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T::ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
 
@@ -141,6 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
 
     int kt_lo, kt_hi;
     mfa_tile_range(a.mask, a.Nq, kBM, BN, qt, &kt_lo, &kt_hi);
+    const int n = kt_hi - kt_lo;
 
     const size_t head_q = (size_t)(b * a.Hq + h) * (size_t)a.Nq;
     const size_t head_kv = (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk;
@@ -171,111 +181,136 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     float m_run = -MFA_INF;   // exponent offset (log2 domain, scaled)
     float l_run = 0.f;        // this lane's half of the row sum
 
-    // ---- loader mapping ----------------------------------------------------------
-    // K: 16-byte chunks; V: an 8-key x VW-column block per thread, transposed into V^T.
-    constexpr int VW = T::VW;
-    const int v_c = tid % T::VGROUPS;
-    const int v_a = tid / T::VGROUPS;
-    uint32_t k_voff[T::K_LOADS];
-#pragma unroll
-    for (int p = 0; p < T::K_LOADS; ++p) {
-        const int c = p * kThreads + tid;
-        k_voff[p] = (uint32_t)((c / T::KCH) * D + (c % T::KCH) * 8) * 2;
+    // ---- direct global -> LDS tile loads ------------------------------------------
+    // Load i of wave w fills the 1 KiB block b = 4*i + w of the tile (rows
+    // b*RPB .. b*RPB + RPB - 1, RPB = 64 / KCH rows per block); lane l writes 16 bytes at
+    // LDS slot b*64 + l, i.e. (row, physical chunk), fetching the logical chunk the
+    // swizzle maps there.  Blocks of one wave are 256 / KCH rows apart, which leaves the
+    // swizzle unchanged, so one per-lane offset serves every load of the thread and each
+    // load only moves the buffer base (scalar).
+    constexpr int RPB = 64 / T::KCH;
+    uint32_t kld_off, vld_off;
+    {
+        const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
+        kld_off = (uint32_t)(row * D + T::k_phys(row, phys) * 8) * 2;
+        vld_off = (uint32_t)(row * D + T::v_phys(row, phys) * 8) * 2;
     }
-    const uint32_t v_voff = (uint32_t)(v_a * 8 * D + v_c * VW) * 2;
-    mfa_u32x4 kreg[T::K_LOADS];
-    mfa_u32x2 vreg[8];   // VW == 2 uses the first word only
-
-    auto load_tile = [&](int kt) {
+    auto issue_k = [&](int kt, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const int k0 = kt * BN;
-        const uint32_t bytes = (uint32_t)(a.Nk - k0) * D * 2;
-        const auto rk = mfa_rsrc(kg + (size_t)k0 * D, bytes);
-        const auto rv = mfa_rsrc(vg + (size_t)k0 * D, bytes);
 #pragma unroll
-        for (int p = 0; p < T::K_LOADS; ++p) kreg[p] = mfa_load16(rk, k_voff[p]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if constexpr (VW == 4) {
-                vreg[r] = mfa_load8(rv, v_voff + r * D * 2);
-            } else {
-                vreg[r][0] = mfa_load4(rv, v_voff + r * D * 2);
-                vreg[r][1] = 0;
-            }
+        for (int i = 0; i < T::LOADS; ++i) {
+            const int r0 = k0 + i * 4 * RPB;   // first key row covered by load i
+            const auto r = mfa_rsrc(kg + (size_t)r0 * D, (uint32_t)max(a.Nk - r0, 0) * D * 2);
+            mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off);
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t* s = smem + buf * T::BUF_ELEMS;
+    auto issue_v = [&](int kt, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
+        const int k0 = kt * BN;
 #pragma unroll
-        for (int p = 0; p < T::K_LOADS; ++p) {
-            const int c = p * kThreads + tid;
-            *(mfa_u32x4*)(s + T::k_off(c / T::KCH, c % T::KCH)) = kreg[p];
-        }
-#pragma unroll
-        for (int e = 0; e < VW; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            mfa_u32x4 col;
-#pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2)
-                col[m2] = __builtin_amdgcn_perm(vreg[2 * m2 + 1][e >> 1], vreg[2 * m2][e >> 1], sel);
-            *(mfa_u32x4*)(s + T::v_off(v_c * VW + e, v_a)) = col;
+        for (int i = 0; i < T::LOADS; ++i) {
+            const int r0 = k0 + i * 4 * RPB;
+            const auto r = mfa_rsrc(vg + (size_t)r0 * D, (uint32_t)max(a.Nk - r0, 0) * D * 2);
+            mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off);
         }
     };
+
+    // ---- per-lane LDS operand addresses (elements; buffer and block offsets are
+    // compile-time immediates) --------------------------------------------------------
+    // K (S^T A operand): row key_perm(l32) (+32 per key block), chunk 2*kb + g32.
+    int k_rd[NKB];
+    {
+        const int row = key_perm(l32);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) k_rd[kb] = row * D + T::k_phys(row, 2 * kb + g32) * 8;
+    }
+    // V^T (PV A operand) via transposing reads: lane group qg = lane / 16 covers
+    // columns 16*(qg%2) .. +15 of a 32-column block and keys 8*(qg/2) .. +3 (+4 for the
+    // second read); lane i of the group addresses row i/4, columns 4*(i%4) .. +3.
+    int v_rd[NDB];
+    {
+        const int qg = lane >> 4, i = lane & 15;
+        const int row = 8 * (qg >> 1) + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
+            v_rd[db] = row * D + T::v_phys(row, col >> 3) * 8 + (col & 7);
+        }
+    }
 
     const float sl2 = a.scale_log2_abs;
-    int n_visit = 0, n_edge = 0;
-    if (kt_lo < kt_hi) {
-        load_tile(kt_lo);
-        store_tile(0);
-        __syncthreads();
-    }
+    int n_edge = 0;
 
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int cur = (kt - kt_lo) & 1;
-        const bool has_next = kt + 1 < kt_hi;
-        if (has_next) load_tile(kt + 1);
-        const uint16_t* s = smem + cur * T::BUF_ELEMS;
-
-        // S^T = K Q^T for the NNB 32-key blocks of the tile (independent chains)
-        mfa_f32x16 sacc[NNB];
+    // S^T = K Q^T for the key tile in K buffer KBUF into s
+    auto qk_mfma = [&](auto kb_c, mfa_f32x16(&s)[NNB]) {
+        constexpr int kbuf = decltype(kb_c)::value;
+        const uint16_t* base = smem + kbuf * T::ELEMS;
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) sacc[nb] = mfa_f32x16{};
+        for (int nb = 0; nb < NNB; ++nb) s[nb] = mfa_f32x16{};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
-                const int krow = nb * 32 + key_perm(l32);
-                const mfa_u32x4 kop = *(const mfa_u32x4*)(s + T::k_off(krow, 2 * kb + g32));
-                sacc[nb] = mfa_mfma32<DT>(kop, qreg[kb], sacc[nb]);
+                const mfa_u32x4 kop = *(const mfa_u32x4*)(base + k_rd[kb] + nb * 32 * D);
+                s[nb] = mfa_mfma32<DT>(kop, qreg[kb], s[nb]);
             }
         }
+    };
 
-        // signed raw scores (the sign of scale folded in), masked on edge tiles
-        const bool edge = !mfa_tile_full(a.mask, kBM, BN, qt, kt);
-        const int k0 = kt * BN;
-        float tmax = -MFA_INF;
-        if (edge) {
+    // O^T += V^T P^T with V from V buffer VBUF
+    auto pv_mfma = [&](auto vb_c, const mfa_u32x4(&pop)[NNB][2]) {
+        constexpr int vbuf = decltype(vb_c)::value;
+        const uint16_t* base = smem + (2 + vbuf) * T::ELEMS;
 #pragma unroll
-            for (int nb = 0; nb < NNB; ++nb) {
+        for (int nb = 0; nb < NNB; ++nb) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int kofs = (nb * 32 + hh * 16) * D;
+                mfa_u32x4 vop[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const mfa_u32x2 l2 = mfa_lds_read_tr16(base + v_rd[db] + kofs);
+                    const mfa_u32x2 h2 = mfa_lds_read_tr16(base + v_rd[db] + kofs + 4 * D);
+                    vop[db] = mfa_u32x4{l2[0], l2[1], h2[0], h2[1]};
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] = mfa_mfma32<DT>(vop[db], pop[nb][hh], oacc[db]);
+            }
+        }
+    };
+
+    // One pipeline stage; P = parity of j (selects the LDS buffers and which S register
+    // set is current).  The stage always issues S(j+1): on the last tile that product
+    // reads a stale buffer and is never used, which keeps the common path free of
+    // branches.  On edge tiles the invisible scores of S(j) are first overwritten with
+    // -inf (after the sign of scale), so the rest of the stage is the same code.
+    auto stage = [&](const int j, auto p_c, mfa_f32x16(&s_cur)[NNB], mfa_f32x16(&s_next)[NNB]) {
+        constexpr int P = decltype(p_c)::value;
+        const int kt = kt_lo + j;
+        if (j + 2 < n) issue_k(kt + 2, MfaInt<P>{});
+        if (j + 1 < n) issue_v(kt + 1, MfaInt<P ^ 1>{});
+
+        if (!mfa_tile_full(a.mask, kBM, BN, qt, kt)) {
+            const int k0 = kt * BN;
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + nb * 32 + 16 * (r >> 3) + 8 * g32 + (r & 7);
-                    const float x = NEG ? -sacc[nb][r] : sacc[nb][r];
-                    sacc[nb][r] = (key >= row_lo && key <= row_hi) ? x : -MFA_INF;
-                    tmax = fmaxf(tmax, sacc[nb][r]);
+                    const bool vis = key >= row_lo && key <= row_hi;
+                    s_cur[nb][r] = vis ? s_cur[nb][r] : (NEG ? MFA_INF : -MFA_INF);
                 }
-            }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < NNB; ++nb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if (NEG) sacc[nb][r] = -sacc[nb][r];
-                    tmax = fmaxf(tmax, sacc[nb][r]);
-                }
-            }
+            if (TILELOG) ++n_edge;
         }
+
+        // row max of S(j) (signed); lazy offset raise
+        float tmax = -MFA_INF;
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, NEG ? -s_cur[nb][r] : s_cur[nb][r]);
         tmax = fmaxf(tmax, mfa_swap_halves(tmax));
-        // raise the offset only when the row max outgrows it by more than kLazy
         const float tmax_s = (tmax == -MFA_INF) ? -MFA_INF : tmax * sl2;
         const bool raise = tmax_s > m_run + kLazy;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -288,53 +323,68 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
         }
         const float m_use = (m_run == -MFA_INF) ? 0.f : m_run;
 
+        // S(j+1) on the matrix cores, interleaved (in program order) with the
+        // exponentials of S(j), in two phases: phase 0 computes key block 0 of S(j+1)
+        // while exponentiating block 1 of S(j); phase 1 computes block 1 of S(j+1)
+        // (in the registers block 1 of S(j) just freed) while exponentiating block 0.
+        // The K operands of step t+1 are read from LDS while step t computes.
+        static_assert(NNB == 2, "two key blocks per tile");
         mfa_u32x4 pop[NNB][2];
+        const uint16_t* kbase = smem + (P ^ 1) * T::ELEMS;
+        constexpr int PAIRS = 8 / NKB;   // score pairs exponentiated per MFMA step
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) {
+        for (int ph = 0; ph < 2; ++ph) {
+            const int nbm = ph;          // key block of S(j+1) on the matrix cores
+            const int nbe = 1 - ph;      // key block of S(j) on the vector ALUs
+            mfa_f32x16 acc = mfa_f32x16{};
+            mfa_u32x4 kop[2];
+            kop[0] = *(const mfa_u32x4*)(kbase + k_rd[0] + nbm * 32 * D);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int step = 0; step < NKB; ++step) {
+                if (step + 1 < NKB)
+                    kop[(step + 1) & 1] = *(const mfa_u32x4*)(kbase + k_rd[step + 1] + nbm * 32 * D);
+                acc = mfa_mfma32<DT>(kop[step & 1], qreg[step], acc);
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float x0 = sacc[nb][8 * hh + 2 * e2];
-                    const float x1 = sacc[nb][8 * hh + 2 * e2 + 1];
-                    float p0 = mfa_exp2(__builtin_fmaf(x0, sl2, -m_use));
-                    float p1 = mfa_exp2(__builtin_fmaf(x1, sl2, -m_use));
-                    if (edge) {
-                        p0 = (x0 == -MFA_INF) ? 0.f : p0;
-                        p1 = (x1 == -MFA_INF) ? 0.f : p1;
-                    }
+                for (int e = 0; e < PAIRS; ++e) {
+                    const int pr = step * PAIRS + e;   // pair index 0..7 within block nbe
+                    const int hh = pr >> 2, e2 = pr & 3;
+                    const int r0 = 8 * hh + 2 * e2, r1 = r0 + 1;
+                    const float x0 = NEG ? -s_cur[nbe][r0] : s_cur[nbe][r0];
+                    const float x1 = NEG ? -s_cur[nbe][r1] : s_cur[nbe][r1];
+                    // masked scores are -inf here and give exp2(-inf) = 0
+                    const float p0 = mfa_exp2(__builtin_fmaf(x0, sl2, -m_use));
+                    const float p1 = mfa_exp2(__builtin_fmaf(x1, sl2, -m_use));
                     const uint32_t pk = mfa_pack2<DT>(p0, p1);
-                    pop[nb][hh][e2] = pk;
-                    // f16: sum the rounded weights with one dot2 (rounding 2^-12);
-                    // bf16 rounds too coarsely (2^-9) for the LSE, so sum in fp32
+                    pop[nbe][hh][e2] = pk;
                     if constexpr (DT == MFA_DT_F16)
                         l_run = mfa_sum2<DT>(pk, l_run);
                     else
                         l_run += p0 + p1;
                 }
             }
+            s_next[nbm] = acc;
         }
 
-        // O^T += V^T P^T (the NDB accumulators are independent chains)
-#pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                mfa_u32x4 vop[NDB];
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    vop[db] = *(const mfa_u32x4*)(s + T::v_off(db * 32 + l32, 4 * nb + 2 * hh + g32));
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] = mfa_mfma32<DT>(vop[db], pop[nb][hh], oacc[db]);
-            }
-        }
+        // O += V(j)^T P(j)^T
+        pv_mfma(MfaInt<P>{}, pop);
 
-        if (has_next) store_tile(cur ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's direct loads landed
         __syncthreads();
-        if (TILELOG) {
-            ++n_visit;
-            n_edge += edge ? 1 : 0;
-        }
+    };
+
+    mfa_f32x16 sA[NNB], sB[NNB];
+    if (n > 0) {
+        issue_k(kt_lo, MfaInt<0>{});
+        issue_v(kt_lo, MfaInt<0>{});
+        if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        qk_mfma(MfaInt<0>{}, sA);
+        __syncthreads();   // S(0)'s K reads are done before K buffer 0 is refilled
+    }
+    for (int j = 0; j < n; j += 2) {
+        stage(j, MfaInt<0>{}, sA, sB);
+        if (j + 1 < n) stage(j + 1, MfaInt<1>{}, sB, sA);
     }
 
     // ---- epilogue: O = o / l, LSE = (m + log2 l) * ln 2 --------------------------
@@ -357,34 +407,34 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     }
     if (TILELOG && tid == 0) {
         int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
-        t[0] = n_visit ? kt_lo : -1;
-        t[1] = n_visit;
+        t[0] = n ? kt_lo : -1;
+        t[1] = n;
         t[2] = n_edge;
-        t[3] = n_visit ? kt_lo + n_visit : -1;
+        t[3] = n ? kt_hi : -1;
     }
 }
 
-template <int D, int DT, int BN, bool TL>
+template <int D, int DT, bool TL>
 void launch_sign(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t stream, bool neg) {
     if (neg)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, TL, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, TL, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, BN, TL, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, TL, false>), grid, block, 0, stream, a);
 }
 
-template <int D, int DT, int BN>
+template <int D, int DT>
 int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, bool neg, mfa_dispatch_info* info) {
     const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
     const dim3 block(kThreads);
     if (tilelog)
-        launch_sign<D, DT, BN, true>(a, grid, block, stream, neg);
+        launch_sign<D, DT, true>(a, grid, block, stream, neg);
     else
-        launch_sign<D, DT, BN, false>(a, grid, block, stream, neg);
+        launch_sign<D, DT, false>(a, grid, block, stream, neg);
     snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d%s%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, BN, tilelog ? ",tilelog" : "",
+             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, tilelog ? ",tilelog" : "",
              neg ? ",neg" : "");
     info->BM = kBM;
-    info->BN = BN;
+    info->BN = kBN;
     info->waves = kThreads / 64;
     info->grid[0] = (int)grid.x;
     info->grid[1] = 1;
@@ -395,7 +445,7 @@ int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, bool neg, mfa_dis
 
 }  // namespace
 
-int mfa_fwd_bn(int) { return 64; }
+int mfa_fwd_bn(int) { return kBN; }
 int mfa_fwd_bm() { return kBM; }
 
 int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_info* info) {
@@ -417,14 +467,16 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.xcd_group = ((pr.B * pr.Hkv) % 8 == 0) ? 1 : 0;
     // heavy/light pairing helps when every workgroup is resident at once (2 per CU)
     a.snake = (pr.causal && (long long)a.n_q_tiles * a.HB <= 2LL * mfa_num_cus()) ? 1 : 0;
-    a.scale_log2_abs = fabsf(pr.scale) * 1.4426950408889634f;
+    // |scale| * log2(e), kept >= 1e-30 so that a masked (-inf) score times it stays
+    // -inf; for scale = 0 the visible scores then all scale to ~0, i.e. the same
+    // uniform weights up to fp32 rounding
+    a.scale_log2_abs = fmaxf(fabsf(pr.scale) * 1.4426950408889634f, 1e-30f);
     a.mask = mfa_make_mask(pr.Nq, pr.Nk, pr.causal, pr.left, pr.right);
     const bool tl = pr.tile_log != nullptr;
     const bool neg = pr.scale < 0.f;
-    if (pr.D == 128) {
-        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, 64>(a, stream, tl, neg, info)
-                                   : launch<128, MFA_DT_BF16, 64>(a, stream, tl, neg, info);
-    }
-    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, 64>(a, stream, tl, neg, info)
-                               : launch<64, MFA_DT_BF16, 64>(a, stream, tl, neg, info);
+    if (pr.D == 128)
+        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, tl, neg, info)
+                                   : launch<128, MFA_DT_BF16>(a, stream, tl, neg, info);
+    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, tl, neg, info)
+                               : launch<64, MFA_DT_BF16>(a, stream, tl, neg, info);
 }
