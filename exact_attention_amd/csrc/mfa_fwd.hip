@@ -9,10 +9,15 @@
 // contractions run on the CDNA4 matrix cores and the loop is software-pipelined.
 //
 // Work decomposition
-//   One workgroup = 4 waves = one query tile of BM = 128 rows of one (batch, head);
-//   each wave owns 32 query rows.  Key tiles of BN = 64 keys stream through LDS:
-//   K and V tiles are copied global -> LDS directly (buffer loads with the LDS bit;
-//   the range check returns zeros past the last key row), double-buffered.
+//   One workgroup = 8 waves = one query tile of BM = 128 rows of one (batch, head).
+//   The waves form two groups of 4; in each group a wave owns 32 query rows, and the
+//   two groups split the tile's visited key range in halves, run concurrently (two
+//   waves per SIMD) and merge their (O, m, l) through LDS at the end.  Every
+//   workgroup thus finishes its query tile in about half the serial time, and with
+//   one workgroup per CU and longest tiles dispatched first, short causal tiles fill
+//   the CUs that free up early.  Key tiles of BN = 64 keys stream through LDS: K and
+//   V tiles are copied global -> LDS directly (buffer loads with the LDS bit; the
+//   range check returns zeros past the last key row), double-buffered per group.
 //
 // Per wave and key tile (32x32x16 MFMA, fp32 accumulate):
 //   S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T held in registers for the whole
@@ -57,7 +62,7 @@ namespace {
 
 constexpr int kBM = 128;
 constexpr int kBN = 64;
-constexpr int kThreads = 256;
+constexpr int kGroupThreads = 256;   // one wave group: 4 waves x 32 query rows
 constexpr float kLazy = 8.0f;
 
 struct FwdArgs {
@@ -71,7 +76,6 @@ struct FwdArgs {
     int n_q_tiles;
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
-    int snake;       // 1: pair heavy and light query tiles (grid fits in one pass)
     float scale_log2_abs;  // |scale| * log2(e)
     MfaMask mask;
 };
@@ -90,7 +94,7 @@ template <int D>
 struct Tile {
     static constexpr int KCH = D / 8;                   // 16-byte chunks per row
     static constexpr int ELEMS = kBN * D;               // 16-bit elements per K or V tile
-    static constexpr int LOADS = kBN * KCH / kThreads;  // 16-byte direct loads per thread
+    static constexpr int LOADS = kBN * KCH / kGroupThreads;  // 16-byte direct loads per thread
     // XOR swizzles on 16-byte chunks (rows are unpadded so that a wave's direct load
     // fills 1 KiB of consecutive LDS).  K: the 16 rows one MFMA operand read touches at
     // a logical chunk land in 16 distinct bank groups.  V: the 4 rows x 32 bytes of a
@@ -103,20 +107,22 @@ struct Tile {
     }
 };
 
-template <int D, int DT, bool TILELOG, bool NEG>
-__global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
+template <int D, int DT, int GROUPS, bool TILELOG, bool NEG>
+__global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     using T = Tile<D>;
     constexpr int BN = kBN;
     constexpr int NKB = D / 16;   // k-steps of S^T = K Q^T
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NNB = BN / 32;  // 32-key blocks of a tile
 
-    // K buffers 0, 1 then V buffers 0, 1
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T::ELEMS];
+    // per wave group: K buffers 0, 1 then V buffers 0, 1
+    __shared__ __attribute__((aligned(1024))) uint16_t smem_all[GROUPS * 4 * T::ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = GROUPS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);   // wave group
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);    // wave within its group
+    uint16_t* smem = smem_all + grp * 4 * T::ELEMS;
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
 
@@ -124,15 +130,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     const int id = blockIdx.x;
     const int round = id / a.HB;
     const int w = id - round * a.HB;
-    int qt;
-    if (a.snake) {
-        // first half of the grid: heaviest tiles downwards; second half: lightest
-        // upwards, so the two workgroups sharing a CU carry complementary work
-        const int half = (a.n_q_tiles + 1) >> 1;
-        qt = round < half ? a.n_q_tiles - 1 - round : round - half;
-    } else {
-        qt = a.n_q_tiles - 1 - round;   // longest first
-    }
+    // longest query tiles first: with one workgroup per CU, dynamic dispatch then
+    // hands the short tiles to the CUs that finish early
+    const int qt = a.n_q_tiles - 1 - round;
     int b, h;
     if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
@@ -148,9 +148,14 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     const int kvh = h / a.g;
     const int q0 = qt * kBM;
 
-    int kt_lo, kt_hi;
-    mfa_tile_range(a.mask, a.Nq, kBM, BN, qt, &kt_lo, &kt_hi);
-    const int n = kt_hi - kt_lo;
+    // with two wave groups the visited key tiles [t_lo, t_hi) are split between them:
+    // group 0 takes the first ceil(n/2), group 1 the rest
+    int t_lo, t_hi;
+    mfa_tile_range(a.mask, a.Nq, kBM, BN, qt, &t_lo, &t_hi);
+    const int n_all = t_hi - t_lo;
+    const int n0 = GROUPS == 1 ? n_all : (n_all + 1) >> 1;
+    const int kt_lo = grp == 0 ? t_lo : t_lo + n0;
+    const int n = grp == 0 ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
 
     const size_t head_q = (size_t)(b * a.Hq + h) * (size_t)a.Nq;
     const size_t head_kv = (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk;
@@ -372,19 +377,65 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
         __syncthreads();
     };
 
+    // Barriers are workgroup-wide, so both groups run n0 stages; a group with fewer
+    // tiles passes its spare stage with the barrier only.
     mfa_f32x16 sA[NNB], sB[NNB];
-    if (n > 0) {
-        issue_k(kt_lo, MfaInt<0>{});
-        issue_v(kt_lo, MfaInt<0>{});
-        if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+    if (n0 > 0) {
+        if (n > 0) {
+            issue_k(kt_lo, MfaInt<0>{});
+            issue_v(kt_lo, MfaInt<0>{});
+            if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+        }
         __syncthreads();
-        qk_mfma(MfaInt<0>{}, sA);
+        if (n > 0) qk_mfma(MfaInt<0>{}, sA);
         __syncthreads();   // S(0)'s K reads are done before K buffer 0 is refilled
     }
-    for (int j = 0; j < n; j += 2) {
-        stage(j, MfaInt<0>{}, sA, sB);
-        if (j + 1 < n) stage(j + 1, MfaInt<1>{}, sB, sA);
+    for (int j = 0; j < n0; j += 2) {
+        if (j < n)
+            stage(j, MfaInt<0>{}, sA, sB);
+        else
+            __syncthreads();
+        if (j + 1 < n0) {
+            if (j + 1 < n)
+                stage(j + 1, MfaInt<1>{}, sB, sA);
+            else
+                __syncthreads();
+        }
+    }
+
+    // ---- merge the two groups' partial states (same rows, disjoint keys) ---------
+    // Group 1 leaves (m, l, o) of each lane in LDS (struct-of-arrays, conflict-free);
+    // group 0 combines them with its own: M = max(m0, m1), f_i = exp2(m_i - M).
+    if constexpr (GROUPS == 2) {
+        constexpr int NC = NDB * 16 + 2;   // o values, m, l per lane
+        float* xch = reinterpret_cast<float*>(smem_all);
+        __shared__ int edge_cnt;
+        const int slot = wave * 64 + lane;
+        if (grp == 1) {
+            xch[0 * 256 + slot] = m_run;
+            xch[1 * 256 + slot] = l_run;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(2 + db * 16 + r) * 256 + slot] = oacc[db][r];
+            if (TILELOG && tid == 256) edge_cnt = n_edge;
+        }
+        static_assert(NC * 256 * 4 <= GROUPS * 4 * T::ELEMS * 2, "exchange fits in the tile buffers");
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = xch[0 * 256 + slot];
+        const float l1 = xch[1 * 256 + slot];
+        const float M = fmaxf(m_run, m1);
+        const float f0 = (m_run == -MFA_INF) ? 0.f : mfa_exp2(m_run - M);
+        const float f1 = (m1 == -MFA_INF) ? 0.f : mfa_exp2(m1 - M);
+        l_run = f0 * l_run + f1 * l1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = f0 * oacc[db][r] + f1 * xch[(2 + db * 16 + r) * 256 + slot];
+        m_run = M;
+        if (TILELOG) n_edge += edge_cnt;
     }
 
     // ---- epilogue: O = o / l, LSE = (m + log2 l) * ln 2 --------------------------
@@ -407,45 +458,59 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     }
     if (TILELOG && tid == 0) {
         int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
-        t[0] = n ? kt_lo : -1;
-        t[1] = n;
+        t[0] = n_all ? t_lo : -1;
+        t[1] = n_all;
         t[2] = n_edge;
-        t[3] = n ? kt_hi : -1;
+        t[3] = n_all ? t_hi : -1;
     }
 }
 
-template <int D, int DT, bool TL>
-void launch_sign(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t stream, bool neg) {
+template <int D, int DT, int G, bool TL>
+void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
+    const dim3 block(G * kGroupThreads);
     if (neg)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, TL, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, TL, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false>), grid, block, 0, stream, a);
 }
 
 template <int D, int DT>
-int launch(const FwdArgs& a, hipStream_t stream, bool tilelog, bool neg, mfa_dispatch_info* info) {
+int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
+           mfa_dispatch_info* info) {
     const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
-    const dim3 block(kThreads);
-    if (tilelog)
-        launch_sign<D, DT, true>(a, grid, block, stream, neg);
-    else
-        launch_sign<D, DT, false>(a, grid, block, stream, neg);
-    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d%s%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, tilelog ? ",tilelog" : "",
+    if (groups == 2) {
+        if (tilelog) launch_sign<D, DT, 2, true>(a, grid, stream, neg);
+        else launch_sign<D, DT, 2, false>(a, grid, stream, neg);
+    } else {
+        if (tilelog) launch_sign<D, DT, 1, true>(a, grid, stream, neg);
+        else launch_sign<D, DT, 1, false>(a, grid, stream, neg);
+    }
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups, tilelog ? ",tilelog" : "",
              neg ? ",neg" : "");
     info->BM = kBM;
     info->BN = kBN;
-    info->waves = kThreads / 64;
+    info->waves = groups * kGroupThreads / 64;
     info->grid[0] = (int)grid.x;
     info->grid[1] = 1;
     info->grid[2] = 1;
-    info->block = kThreads;
+    info->block = groups * kGroupThreads;
     return hipGetLastError() == hipSuccess ? MFA_OK : MFA_ERR_HIP;
 }
 
 }  // namespace
 
 int mfa_fwd_bn(int) { return kBN; }
+
+// Wave groups per workgroup.  Two workgroups of one group share a CU and overlap
+// each other's prologue and epilogue, which is best when the grid has many query
+// tiles.  A small grid (at most two workgroups per CU: every workgroup resident at
+// once, so the longest query tile bounds the run) instead gets one 8-wave workgroup
+// per CU whose two groups split the key range of the query tile.
+int mfa_fwd_groups(int B, int Hq, int Nq, int num_cus) {
+    const long long wgs = (long long)((Nq + kBM - 1) / kBM) * B * Hq;
+    return wgs <= 2LL * num_cus ? 2 : 1;
+}
 int mfa_fwd_bm() { return kBM; }
 
 int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_info* info) {
@@ -465,8 +530,6 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.n_q_tiles = (pr.Nq + kBM - 1) / kBM;
     a.HB = pr.B * pr.Hq;
     a.xcd_group = ((pr.B * pr.Hkv) % 8 == 0) ? 1 : 0;
-    // heavy/light pairing helps when every workgroup is resident at once (2 per CU)
-    a.snake = (pr.causal && (long long)a.n_q_tiles * a.HB <= 2LL * mfa_num_cus()) ? 1 : 0;
     // |scale| * log2(e), kept >= 1e-30 so that a masked (-inf) score times it stays
     // -inf; for scale = 0 the visible scores then all scale to ~0, i.e. the same
     // uniform weights up to fp32 rounding
@@ -474,9 +537,10 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.mask = mfa_make_mask(pr.Nq, pr.Nk, pr.causal, pr.left, pr.right);
     const bool tl = pr.tile_log != nullptr;
     const bool neg = pr.scale < 0.f;
+    const int groups = mfa_fwd_groups(pr.B, pr.Hq, pr.Nq, mfa_num_cus());
     if (pr.D == 128)
-        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, tl, neg, info)
-                                   : launch<128, MFA_DT_BF16>(a, stream, tl, neg, info);
-    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, tl, neg, info)
-                               : launch<64, MFA_DT_BF16>(a, stream, tl, neg, info);
+        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, groups, tl, neg, info)
+                                   : launch<128, MFA_DT_BF16>(a, stream, groups, tl, neg, info);
+    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, groups, tl, neg, info)
+                               : launch<64, MFA_DT_BF16>(a, stream, groups, tl, neg, info);
 }

@@ -41,6 +41,7 @@ int mfa_num_cus();
 
 int mfa_fwd_bm();
 int mfa_fwd_bn(int D);
+int mfa_fwd_groups(int B, int Hq, int Nq, int num_cus);
 int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
 
 int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits);
