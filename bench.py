@@ -37,6 +37,37 @@ PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 
 METRIC = "attn fwd TFLOP/s (D=128 causal fp16) + paged decode HBM GB/s, % roofline"
 
+# HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE / WRITE_SIZE,
+# scaled by a plain copy kernel of known size) is kept in profiles/traffic.json
+# together with a hash of the kernel sources it was measured on; it is reported only
+# while the sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "fwd": ["mfa_fwd.hip", "mfa_device.h", "mfa_geometry.h"],
+    "decode": ["mfa_decode.hip", "mfa_device.h"],
+}
+
+
+def sources_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "exact_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key, kind):
+    """Bytes per launch recorded for `key`, or None if absent or measured on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha256") != sources_hash(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
 
 def visible_pairs(Nq, Nk, causal, left, right) -> int:
     """Number of visible (query, key) pairs of one head (inclusive window ends)."""
@@ -104,7 +135,8 @@ def bench_prefill(i, steps, warmup):
                     f"{c['dtype']} causal={int(c['causal'])} window=({c['left']},{c['right']})",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": None},
+                     "frac": tf / PEAK_MFMA_F16,
+                     "traffic": measured_traffic(f"fwd_config{i}", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "planned_tiles": info["planned"],
         "dtype": c["dtype"],
     }
@@ -147,7 +179,7 @@ def bench_decode(steps, warmup):
                     f"page=16 seq_lens in [1024,32768] (sum={int(p.seq_lens.sum())})",
         "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM, "traffic": None},
+                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("decode_config5", "decode")},
         "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
         "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
     }
