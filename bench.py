@@ -9,8 +9,9 @@ the sliding-window prefill (window (512, 0)), and the paged split-KV decode (HBM
 GB/s over the algorithmic bytes: every cached K/V byte once, plus q, out, LSE, the
 block-table entries used and seq_lens).
 
-Timing: HIP events on the stream the kernels run on, W untimed warm-up steps, then
-K timed steps; ``torch.cuda.synchronize()`` on both sides of the timed region.
+Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
+workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
+sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
@@ -88,7 +89,7 @@ def to_dev(bits, dtype):
     return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
 
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps):
     """Time `steps` back-to-back calls as one block.
 
     HIP events are recorded on the current stream (the one the library launches on)
@@ -96,8 +97,6 @@ def time_calls(fn, steps, warmup):
     both sides.  Returns (ms per call, wall ms of the block).
     """
     import torch
-    for _ in range(warmup):
-        fn()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -111,7 +110,8 @@ def time_calls(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def bench_prefill(i, steps, warmup):
+def setup_prefill(i):
+    """Device inputs and one step (one mfa_fwd call) of prefill workload i."""
     import torch
     import exact_attention_amd as ea
     c = A.config(i)
@@ -125,7 +125,13 @@ def bench_prefill(i, steps, warmup):
         ea.mfa_fwd(q, k, v, scale=c["scale"], causal=c["causal"], win_left=c["left"],
                    win_right=c["right"], out=out, lse=lse)
 
-    ms, wall = time_calls(step, steps, warmup)
+    return step
+
+
+def bench_prefill(i, step, steps):
+    import exact_attention_amd as ea
+    c = A.config(i)
+    ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     flop = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], c["left"], c["right"]) \
         * c["B"] * c["Hq"]
@@ -152,7 +158,8 @@ def decode_bytes(p, Hkv, D, Hq):
     return kv + qo + lse + bt + 4 * B
 
 
-def bench_decode(steps, warmup):
+def setup_decode():
+    """Device inputs and one step (one mfa_decode_paged call) of the paged decode workload."""
     import torch
     import exact_attention_amd as ea
     c = A.config(5)
@@ -170,13 +177,21 @@ def bench_decode(steps, warmup):
     def step():
         ea.mfa_decode_paged(q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse, workspace=ws)
 
-    ms, wall = time_calls(step, steps, warmup)
+    step.seq_lens = p.seq_lens
+    step.page_size = p.page_size
+    return step
+
+
+def bench_decode(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(5)
+    ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
-    nb = decode_bytes(p, c["Hkv"], c["D"], c["Hq"])
+    nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"])
     gbs = nb / (ms * 1e-3) / 1e9
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} bf16 "
-                    f"page=16 seq_lens in [1024,32768] (sum={int(p.seq_lens.sum())})",
+                    f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
         "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM, "traffic": measured_traffic("decode_config5", "decode")},
@@ -235,14 +250,18 @@ def main():
     ea.lib()
 
     wl = [int(s) for s in args.workloads.split(",") if s]
-    res = {}
     if 2 not in wl:
         wl = [2] + wl
+    steps = {i: (setup_decode() if i == 5 else setup_prefill(i)) for i in wl}
+    # the W untimed warm-up steps of every workload run first, so that the first timed
+    # workload does not meet a GPU still ramping its clocks
     for i in wl:
-        if i == 5:
-            res[i] = bench_decode(args.steps, args.warmup)
-        else:
-            res[i] = bench_prefill(i, args.steps, args.warmup)
+        for _ in range(args.warmup):
+            steps[i]()
+    torch.cuda.synchronize()
+    res = {}
+    for i in wl:
+        res[i] = bench_decode(steps[i], args.steps) if i == 5 else bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)
 
     head = res[2]

@@ -25,6 +25,10 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Wall", "-Wno-unused-function"]
 
 
+# Per-source extra flags (none at present).
+SOURCE_FLAGS: dict = {}
+
+
 def hipcc() -> str:
     cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(cand):
@@ -40,7 +44,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [cc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+        cmd = [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE,
+               "-I", CSRC, *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

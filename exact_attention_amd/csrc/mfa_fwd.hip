@@ -107,6 +107,31 @@ struct Tile {
     }
 };
 
+// Workgroup barrier of the tile pipeline.  __syncthreads() also fences memory, which
+// waits for every outstanding load, including direct-to-LDS copies meant to stay in
+// flight; here each wave has already waited for the copies the next stage reads
+// (vmcnt), waits for its own LDS reads to return (lgkmcnt(0): no buffer is refilled
+// while a read of it is pending) and then meets the others.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS operand reads of the key loop.  The restrict-qualified parameter gives each read
+// an alias scope of its own; without one the compiler orders every LDS read after all
+// direct-to-LDS copies still in flight (a vmcnt(0) before the read), which the tile
+// pipeline already orders itself with vmcnt waits and barriers.
+__device__ __forceinline__ mfa_u32x4 lds_read16(const uint16_t* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const mfa_u32x4 lds_u32x4;
+    return *(lds_u32x4*)p;
+}
+__device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
+    return mfa_lds_read_tr16(p);
+}
+
 template <int D, int DT, int GROUPS, bool TILELOG, bool NEG>
 __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     using T = Tile<D>;
@@ -172,6 +197,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         const uint32_t off = ((uint32_t)qrow * D + g32 * 8) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) qreg[kb] = mfa_load16(rq, off + kb * 32);
+        // complete here, so that no wait for them is left to the key loop (vmcnt is one
+        // counter, which the loop's own direct loads keep busy)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
     }
 
     // per-row visible key bounds (inclusive), clamped into int range
@@ -257,7 +285,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) {
-                const mfa_u32x4 kop = *(const mfa_u32x4*)(base + k_rd[kb] + nb * 32 * D);
+                const mfa_u32x4 kop = lds_read16(base + k_rd[kb] + nb * 32 * D);
                 s[nb] = mfa_mfma32<DT>(kop, qreg[kb], s[nb]);
             }
         }
@@ -275,8 +303,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
                 mfa_u32x4 vop[NDB];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const mfa_u32x2 l2 = mfa_lds_read_tr16(base + v_rd[db] + kofs);
-                    const mfa_u32x2 h2 = mfa_lds_read_tr16(base + v_rd[db] + kofs + 4 * D);
+                    const mfa_u32x2 l2 = lds_read_tr(base + v_rd[db] + kofs);
+                    const mfa_u32x2 h2 = lds_read_tr(base + v_rd[db] + kofs + 4 * D);
                     vop[db] = mfa_u32x4{l2[0], l2[1], h2[0], h2[1]};
                 }
 #pragma unroll
@@ -343,11 +371,11 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             const int nbe = 1 - ph;      // key block of S(j) on the vector ALUs
             mfa_f32x16 acc = mfa_f32x16{};
             mfa_u32x4 kop[2];
-            kop[0] = *(const mfa_u32x4*)(kbase + k_rd[0] + nbm * 32 * D);
+            kop[0] = lds_read16(kbase + k_rd[0] + nbm * 32 * D);
 #pragma unroll
             for (int step = 0; step < NKB; ++step) {
                 if (step + 1 < NKB)
-                    kop[(step + 1) & 1] = *(const mfa_u32x4*)(kbase + k_rd[step + 1] + nbm * 32 * D);
+                    kop[(step + 1) & 1] = lds_read16(kbase + k_rd[step + 1] + nbm * 32 * D);
                 acc = mfa_mfma32<DT>(kop[step & 1], qreg[step], acc);
 #pragma unroll
                 for (int e = 0; e < PAIRS; ++e) {
@@ -374,7 +402,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         pv_mfma(MfaInt<P>{}, pop);
 
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's direct loads landed
-        __syncthreads();
+        block_barrier();
     };
 
     // Barriers are workgroup-wide, so both groups run n0 stages; a group with fewer
@@ -387,20 +415,20 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
             __builtin_amdgcn_s_waitcnt(0x0f70);
         }
-        __syncthreads();
+        block_barrier();
         if (n > 0) qk_mfma(MfaInt<0>{}, sA);
-        __syncthreads();   // S(0)'s K reads are done before K buffer 0 is refilled
+        block_barrier();   // S(0)'s K reads are done before K buffer 0 is refilled
     }
     for (int j = 0; j < n0; j += 2) {
         if (j < n)
             stage(j, MfaInt<0>{}, sA, sB);
         else
-            __syncthreads();
+            block_barrier();
         if (j + 1 < n0) {
             if (j + 1 < n)
                 stage(j + 1, MfaInt<1>{}, sB, sA);
             else
-                __syncthreads();
+                block_barrier();
         }
     }
 

@@ -68,6 +68,28 @@ def test_edge_shapes(case):
     dense_case(B, Hq, Hkv, Nq, Nk, D, dtype, 1000 + Nq + Nk, causal, left, right)
 
 
+@pytest.mark.parametrize("case", [
+    (500, 128, "f16", True, 37, 0),      # row windows starting in the upper lane half of a block
+    (500, 64, "bf16", False, 20, 45),
+    (333, 128, "bf16", True, -1, -1),
+])
+def test_both_workgroup_layouts(case):
+    # a small grid takes two key-splitting wave groups per workgroup, a large one a single
+    # group; both must agree with the oracle (first and last head checked)
+    N, D, dtype, causal, left, right = case
+    for H, groups in ((2, 2), (240, 1)):
+        x = A.dense_inputs(1, H, H, N, N, D, dtype, 31 + H)
+        q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+        O, L = run(q, k, v, 1 / math.sqrt(D), causal, left, right)
+        info = ea.mfa_last_dispatch()
+        assert f"groups={groups}" in info["kernel"], info["kernel"]
+        for h in (0, H - 1):
+            qf, kf, vf = (oracle.widen(t[:, h:h + 1], dtype) for t in (x.q, x.k, x.v))
+            Or, Lr = oracle.attention(qf, kf, vf, 1 / math.sqrt(D), causal, left, right)
+            assert_close_o(to_f64(O[:, h:h + 1], dtype), Or, dtype, f"O H={H} h={h}")
+            assert_close_lse(L[:, h:h + 1].cpu().numpy(), Lr, f"LSE H={H} h={h}")
+
+
 def test_fully_masked_rows_exact():
     import torch
     x = A.dense_inputs(1, 2, 2, 300, 90, 128, "f16", 5)
