@@ -121,13 +121,22 @@ __global__ __launch_bounds__(kThreads, 3) void mfa_decode_split_kernel(DecArgs a
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
     const size_t page_elems = (size_t)kPage * a.Hkv * D;
 
+    // Page ids are read one step ahead (right after the step's own loads are issued), so
+    // a step's K/V loads never wait for a block-table read.
+    int pid_next[kPG];
+#pragma unroll
+    for (int j = 0; j < kPG; ++j) pid_next[j] = w_begin + j < w_end ? bt[w_begin + j] : -1;
+
     for (int pg = w_begin; pg < w_end; pg += kPG) {
         mfa_u32x4 kr[kPG][NKB], vr[kPG][NT];
         int nv[kPG];
+        int pid_cur[kPG];
+#pragma unroll
+        for (int j = 0; j < kPG; ++j) pid_cur[j] = __builtin_amdgcn_readfirstlane(pid_next[j]);
 #pragma unroll
         for (int j = 0; j < kPG; ++j) {
             const int pi = pg + j;
-            const int pid = pi < w_end ? __builtin_amdgcn_readfirstlane(bt[pi]) : -1;
+            const int pid = pid_cur[j];
             const bool pvalid = pid >= 0 && pid < a.num_pages;
             // valid tokens of this page (0 if the page index is out of range)
             nv[j] = pvalid ? min(kPage, L - pi * kPage) : 0;
@@ -141,6 +150,10 @@ __global__ __launch_bounds__(kThreads, 3) void mfa_decode_split_kernel(DecArgs a
 #pragma unroll
             for (int t = 0; t < NT; ++t) vr[j][t] = mfa_load16(rv, v_off + t * tok_bytes);
         }
+#pragma unroll
+        for (int j = 0; j < kPG; ++j) pid_next[j] = pg + kPG + j < w_end ? bt[pg + kPG + j] : -1;
+        // every load of the step is issued before the first use of its data
+        __builtin_amdgcn_sched_barrier(0);
         // scores: sc[j][hh][i] for token 4G + i (i < 4) of page j, head hh
         float sc[kPG][HPW][4];
 #pragma unroll

@@ -33,7 +33,7 @@
 //     the input type).  The O^T accumulator again has one query row per lane.
 //
 // Pipeline (iteration j, with S(j) already computed):
-//   issue the direct loads of K(j+2) and V(j+1);
+//   the direct loads of K(j+2) and V(j+1), spread over the stage;
 //   row max of S(j) (raise the exponent offset if needed, rescale O and l);
 //   the 16 MFMAs of S(j+1) = K(j+1) Q^T interleaved with the exponentials of S(j);
 //   the 16 MFMAs of O += V(j)^T P(j)^T;  wait for the loads;  one barrier.
@@ -228,25 +228,30 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         kld_off = (uint32_t)(row * D + T::k_phys(row, phys) * 8) * 2;
         vld_off = (uint32_t)(row * D + T::v_phys(row, phys) * 8) * 2;
     }
-    auto issue_k = [&](int kt, auto buf_c) {
+    // One buffer range per tile: rows from k0 on (an empty range when the tile is not
+    // needed, which makes the copies zero-filling no-ops into a free buffer); copy i of a
+    // thread is at a fixed offset from the tile start.
+    auto tile_rsrc = [&](const uint16_t* src, int kt, bool need) {
+        const int k0 = need ? kt * BN : 0;
+        return mfa_rsrc(src + (size_t)k0 * D, need ? (uint32_t)max(a.Nk - k0, 0) * D * 2 : 0u);
+    };
+    auto copy_k = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
         constexpr int buf = decltype(buf_c)::value;
-        const int k0 = kt * BN;
+        mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * (4 * RPB * D * 2));
+    };
+    auto copy_v = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
+        constexpr int buf = decltype(buf_c)::value;
+        mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * (4 * RPB * D * 2));
+    };
+    auto issue_k = [&](int kt, auto buf_c) {
+        const auto r = tile_rsrc(kg, kt, true);
 #pragma unroll
-        for (int i = 0; i < T::LOADS; ++i) {
-            const int r0 = k0 + i * 4 * RPB;   // first key row covered by load i
-            const auto r = mfa_rsrc(kg + (size_t)r0 * D, (uint32_t)max(a.Nk - r0, 0) * D * 2);
-            mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off);
-        }
+        for (int i = 0; i < T::LOADS; ++i) copy_k(r, buf_c, i);
     };
     auto issue_v = [&](int kt, auto buf_c) {
-        constexpr int buf = decltype(buf_c)::value;
-        const int k0 = kt * BN;
+        const auto r = tile_rsrc(vg, kt, true);
 #pragma unroll
-        for (int i = 0; i < T::LOADS; ++i) {
-            const int r0 = k0 + i * 4 * RPB;
-            const auto r = mfa_rsrc(vg + (size_t)r0 * D, (uint32_t)max(a.Nk - r0, 0) * D * 2);
-            mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off);
-        }
+        for (int i = 0; i < T::LOADS; ++i) copy_v(r, buf_c, i);
     };
 
     // ---- per-lane LDS operand addresses (elements; buffer and block offsets are
@@ -292,13 +297,14 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     };
 
     // O^T += V^T P^T with V from V buffer VBUF
-    auto pv_mfma = [&](auto vb_c, const mfa_u32x4(&pop)[NNB][2]) {
+    auto pv_mfma = [&](auto vb_c, const mfa_u32x4(&pop)[NNB][2], auto copy_v_part) {
         constexpr int vbuf = decltype(vb_c)::value;
         const uint16_t* base = smem + (2 + vbuf) * T::ELEMS;
 #pragma unroll
         for (int nb = 0; nb < NNB; ++nb) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
+                copy_v_part(2 * nb + hh);
                 const int kofs = (nb * 32 + hh * 16) * D;
                 mfa_u32x4 vop[NDB];
 #pragma unroll
@@ -321,8 +327,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     auto stage = [&](const int j, auto p_c, mfa_f32x16(&s_cur)[NNB], mfa_f32x16(&s_next)[NNB]) {
         constexpr int P = decltype(p_c)::value;
         const int kt = kt_lo + j;
-        if (j + 2 < n) issue_k(kt + 2, MfaInt<P>{});
-        if (j + 1 < n) issue_v(kt + 1, MfaInt<P ^ 1>{});
+        // copies of K(j+2) and V(j+1), spread over the stage (a burst of copies at the
+        // start would queue every wave behind the CU's address path)
+        const auto rk = tile_rsrc(kg, kt + 2, j + 2 < n);
+        const auto rv = tile_rsrc(vg, kt + 1, j + 1 < n);
 
         if (!mfa_tile_full(a.mask, kBM, BN, qt, kt)) {
             const int k0 = kt * BN;
@@ -374,6 +382,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             kop[0] = lds_read16(kbase + k_rd[0] + nbm * 32 * D);
 #pragma unroll
             for (int step = 0; step < NKB; ++step) {
+                // K copies: LOADS per stage, LOADS / 2 per phase, at evenly spaced steps
+                if ((step % (2 * NKB / T::LOADS)) == 1)
+                    copy_k(rk, MfaInt<P>{}, ph * (T::LOADS / 2) + step / (2 * NKB / T::LOADS));
                 if (step + 1 < NKB)
                     kop[(step + 1) & 1] = lds_read16(kbase + k_rd[step + 1] + nbm * 32 * D);
                 acc = mfa_mfma32<DT>(kop[step & 1], qreg[step], acc);
@@ -399,7 +410,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         }
 
         // O += V(j)^T P(j)^T
-        pv_mfma(MfaInt<P>{}, pop);
+        pv_mfma(MfaInt<P>{}, pop, [&](int q) {
+            // V copies: LOADS per stage over the 2 * NNB PV steps
+            if (q % (2 * NNB / T::LOADS) == 0) copy_v(rv, MfaInt<P ^ 1>{}, q / (2 * NNB / T::LOADS));
+        });
 
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's direct loads landed
         block_barrier();
