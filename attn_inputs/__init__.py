@@ -136,7 +136,49 @@ def paged_inputs(B: int, Hq: int, Hkv: int, D: int, dtype: str, seed: int, *,
                        page_size, dtype, used)
 
 
-# The five benchmark workloads.  Shapes follow the mlx-mfa "Performance" table
+@dataclass
+class VarlenInputs:
+    q: np.ndarray             # uint16 bits [total_q, Hq, D]
+    k: np.ndarray             # uint16 bits [total_k, Hkv, D]
+    v: np.ndarray             # uint16 bits [total_k, Hkv, D]
+    cu_seqlens_q: np.ndarray  # int32 [B + 1]
+    cu_seqlens_k: np.ndarray  # int32 [B + 1]
+    dtype: str
+
+
+def varlen_inputs(Hq: int, Hkv: int, D: int, dtype: str, seed: int, *, B: int | None = None,
+                  len_lo: int | None = None, len_hi: int | None = None, seqlens_q=None,
+                  seqlens_k=None, pad_q: int = 0, pad_k: int = 0) -> VarlenInputs:
+    """Packed variable-length sequences (token-major ``[total, H, D]``).
+
+    Draw order: the query lengths (uniform integers in ``[len_lo, len_hi]``, unless
+    ``seqlens_q`` is given), then Q, K, V.  ``seqlens_k`` defaults to the query lengths
+    (self-attention packing); giving longer key lengths models chunked prefill, where each
+    sequence's new queries follow ``Lk_b - Lq_b`` earlier keys.  ``pad_q`` / ``pad_k`` extra
+    tokens after the last sequence belong to no sequence and hold NaN.
+    """
+    rng = np.random.default_rng(seed)
+    if seqlens_q is None:
+        seqlens_q = rng.integers(len_lo, len_hi, endpoint=True, size=B)
+    seqlens_q = np.asarray(seqlens_q, dtype=np.int64)
+    seqlens_k = seqlens_q if seqlens_k is None else np.asarray(seqlens_k, dtype=np.int64)
+    if seqlens_k.shape != seqlens_q.shape:
+        raise ValueError("seqlens_q and seqlens_k differ in length")
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = _normal_bits(rng, (tq, Hq, D), dtype)
+    k = _normal_bits(rng, (tk, Hkv, D), dtype)
+    v = _normal_bits(rng, (tk, Hkv, D), dtype)
+    if pad_q:
+        q = np.concatenate([q, np.full((pad_q, Hq, D), NAN_BITS[dtype], np.uint16)])
+    if pad_k:
+        k = np.concatenate([k, np.full((pad_k, Hkv, D), NAN_BITS[dtype], np.uint16)])
+        v = np.concatenate([v, np.full((pad_k, Hkv, D), NAN_BITS[dtype], np.uint16)])
+    return VarlenInputs(q, k, v, cu_q, cu_k, dtype)
+
+
+# The benchmark workloads.  Shapes follow the mlx-mfa "Performance" table
 # (B=2, H=8, f16, D=128, causal / window 512), its GQA statement (Hq a multiple of
 # Hkv), and the MXFlashAttn paged split-KV decode setting (pages of 16 tokens,
 # Hq=32, Hkv=8, D=128).
@@ -151,6 +193,10 @@ CONFIGS = {
             dtype=F16, causal=True, left=512, right=0, seed=104),
     5: dict(name="paged_splitkv_decode", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
             page_size=16, len_lo=1024, len_hi=32768, seed=105),
+    # packed variable-length causal prefill (mlx-mfa "Variable-length" feature): a
+    # serving-style mix of prompt lengths, GQA heads of the long-context workload
+    6: dict(name="packed_varlen_causal_prefill", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
+            causal=True, left=-1, right=-1, len_lo=256, len_hi=4096, seed=106),
 }
 
 
@@ -162,6 +208,9 @@ def config(i: int) -> dict:
 
 def config_inputs(i: int):
     c = config(i)
+    if i == 6:
+        return varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
+                             len_lo=c["len_lo"], len_hi=c["len_hi"])
     if i == 5:
         return paged_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"],
                             len_lo=c["len_lo"], len_hi=c["len_hi"],

@@ -13,6 +13,9 @@ tile by tile:
   is the materialised form of the forward pass (mlx-bun ``flash-attention.ts``:
   the ``manualSdpa`` reference and the forward shader's online softmax, which
   reaches the same result up to rounding).
+* ``attention_varlen``: the same for sequences of different lengths packed along the
+  token axis and delimited by ``cu_seqlens`` (mlx-mfa "Variable-length" feature),
+  each sequence on its own with bottom-right alignment.
 * ``decode_paged``: single-query attention over a paged KV cache, gathered through
   the block table with its own loop (MXFlashAttn paged Split-KV decode; mlx-mfa
   "Paged KV" feature).
@@ -26,8 +29,8 @@ Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed
 forms, invariants, a pure-Python scalar implementation (``oracle.scalar``) and
 PyTorch's float64 CPU attention routine.  No function here is "parity unpinned".
 """
-from .reference import (attention, attention_probs, decode_paged, gather_paged,
-                        lse_merge, visible, visited_tiles, widen, window_bounds)
+from .reference import (attention, attention_probs, attention_varlen, decode_paged,
+                        gather_paged, lse_merge, visible, visited_tiles, widen, window_bounds)
 
-__all__ = ["attention", "attention_probs", "decode_paged", "gather_paged", "lse_merge",
-           "visible", "visited_tiles", "widen", "window_bounds"]
+__all__ = ["attention", "attention_probs", "attention_varlen", "decode_paged", "gather_paged",
+           "lse_merge", "visible", "visited_tiles", "widen", "window_bounds"]

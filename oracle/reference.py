@@ -130,6 +130,71 @@ def attention(q, k, v, scale: float, causal: bool = False, left: int = -1,
     return O, L
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
+                     causal: bool = False, left: int = -1, right: int = -1, rows=None):
+    """Packed variable-length attention, float64 (mlx-mfa "Variable-length" feature:
+    sequences packed back to back and delimited by ``cu_seqlens``).
+
+    q ``[total_q, Hq, D]``, k/v ``[total_k, Hkv, D]``; sequence ``b`` owns query tokens
+    ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1`` and keys ``cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1``.  Each sequence is attended on its own, exactly as ``attention``
+    would on ``[1, H, L, D]`` slices, so the causal / window alignment is bottom-right per
+    sequence: ``off_b = Lk_b - Lq_b``.  (The mlx-mfa 2.5.2 page reports a correction of the
+    varlen causal output for ``N_q < N_k`` without naming the convention; bottom-right is
+    the reading under which a block of new queries after ``Lk_b - Lq_b`` cached keys sees
+    them all, as chunked prefill needs.)  A sequence with queries but no keys gives
+    ``O = 0`` and ``LSE = -inf`` on its rows.
+
+    Returns O ``[total_q, Hq, D]`` and LSE ``[Hq, total_q]``; query tokens outside every
+    sequence keep ``O = 0``, ``LSE = -inf``.  ``rows`` optionally restricts the work to a
+    list of ``(token, head)`` pairs and then returns ``(O [n, D], LSE [n])``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    if any(b < a for a, b in zip(cq[:-1], cq[1:])) or any(b < a for a, b in zip(ck[:-1], ck[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if cq[0] < 0 or ck[0] < 0 or cq[-1] > q.shape[0] or ck[-1] > k.shape[0]:
+        raise ValueError("cu_seqlens out of range")
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+
+    def seq_views(b):
+        qs = q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]    # [1, Hq, Lq, D]
+        ks = k[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]    # [1, Hkv, Lk, D]
+        vs = v[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+        return qs, ks, vs
+
+    if rows is not None:
+        rows = list(rows)
+        O = np.zeros((len(rows), D))
+        L = np.full(len(rows), -np.inf)
+        for n, (t, h) in enumerate(rows):
+            b = next((s for s in range(len(cq) - 1) if cq[s] <= t < cq[s + 1]), None)
+            if b is None or ck[b + 1] == ck[b]:
+                continue
+            qs, ks, vs = seq_views(b)
+            o, lse = attention(qs, ks, vs, scale, causal, left, right, rows=[(0, h, t - cq[b])])
+            O[n], L[n] = o[0], lse[0]
+        return O, L
+    O = np.zeros((total_q, Hq, D))
+    L = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cq) - 1):
+        if cq[b + 1] == cq[b] or ck[b + 1] == ck[b]:
+            continue
+        qs, ks, vs = seq_views(b)
+        o, lse = attention(qs, ks, vs, scale, causal, left, right)
+        O[cq[b]:cq[b + 1]] = o[0].transpose(1, 0, 2)
+        L[:, cq[b]:cq[b + 1]] = lse[0]
+    return O, L
+
+
 def attention_probs(q, k, scale: float, causal=False, left=-1, right=-1):
     """The probability matrix P ``[B, Hq, Nq, Nk]`` (small sizes only)."""
     q = np.asarray(q, dtype=np.float64)

@@ -54,3 +54,25 @@ def test_config5_shape():
     c = A.config(5)
     assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (16, 32, 8, 128, 16)
     assert abs(c["scale"] - 128 ** -0.5) < 1e-15
+
+
+def test_varlen_layout():
+    a = A.varlen_inputs(4, 2, 8, "bf16", 11, B=5, len_lo=1, len_hi=40, pad_q=3, pad_k=2)
+    b = A.varlen_inputs(4, 2, 8, "bf16", 11, B=5, len_lo=1, len_hi=40, pad_q=3, pad_k=2)
+    np.testing.assert_array_equal(a.q, b.q)
+    assert a.cu_seqlens_q.dtype == np.int32 and a.cu_seqlens_q[0] == 0
+    assert np.all(np.diff(a.cu_seqlens_q) >= 1) and np.array_equal(a.cu_seqlens_q, a.cu_seqlens_k)
+    tq = int(a.cu_seqlens_q[-1])
+    assert a.q.shape == (tq + 3, 4, 8) and a.k.shape == (tq + 2, 2, 8)
+    assert np.all(a.q[tq:] == A.NAN_BITS["bf16"]) and np.all(a.v[tq:] == A.NAN_BITS["bf16"])
+    assert not np.any(a.q[:tq] == A.NAN_BITS["bf16"])
+    c = A.varlen_inputs(2, 1, 8, "f16", 12, seqlens_q=[3, 0, 5], seqlens_k=[7, 2, 5])
+    assert c.cu_seqlens_q.tolist() == [0, 3, 3, 8] and c.cu_seqlens_k.tolist() == [0, 7, 9, 14]
+
+
+def test_config6_shape():
+    c = A.config(6)
+    assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["causal"]) == (16, 32, 8, 128, True)
+    x = A.config_inputs(6)
+    L = np.diff(x.cu_seqlens_q)
+    assert L.min() >= 256 and L.max() <= 4096 and x.q.shape[1:] == (32, 128)

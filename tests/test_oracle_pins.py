@@ -256,11 +256,119 @@ def pin_config4_pairs():
     assert int(n.sum()) == 4_071_168
 
 
+def _sdpa_with_lse(torch, q, k, v, scale, mask):
+    """torch's float64 attention plus a torch logsumexp of the masked scores.
+
+    q ``[Lq, Hq, D]``, k/v ``[Lk, Hkv, D]`` numpy; mask ``[Lq, Lk]`` bool tensor (True =
+    visible).  Grouped heads go through SDPA's own ``enable_gqa`` head mapping.
+    """
+    F = torch.nn.functional
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                       enable_gqa=True)
+    kk = tk.repeat_interleave(q.shape[1] // k.shape[1], dim=1)
+    sc = (tq @ kk.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(sc.masked_fill(~mask, float("-inf")), dim=-1)
+    return o[0].permute(1, 0, 2).numpy(), lse[0].numpy()
+
+
+def pin_varlen_block_diagonal():
+    # equal query / key lengths: packed attention is one attention over the concatenated
+    # tokens with a block-diagonal mask (lower-triangular blocks when causal), built by
+    # torch.block_diag / torch.tril and evaluated by torch's float64 SDPA
+    torch = pytest.importorskip("torch")
+    lens = [5, 1, 12, 7]
+    T = sum(lens)
+    q, k, v = _rand((T, 4, 8), 50), _rand((T, 2, 8), 51), _rand((T, 2, 8), 52)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu, cu, 0.4, causal)
+        blocks = [torch.ones(n, n, dtype=torch.bool) for n in lens]
+        if causal:
+            blocks = [torch.tril(b) for b in blocks]
+        Or, Lr = _sdpa_with_lse(torch, q, k, v, 0.4, torch.block_diag(*blocks))
+        np.testing.assert_allclose(O, Or, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(L, Lr, atol=1e-12, rtol=0)
+
+
+def pin_varlen_lower_right():
+    # chunked-prefill packing (Lq_b <= Lk_b): each sequence equals torch's float64 SDPA
+    # under its bottom-right causal bias (torch.nn.attention.bias.causal_lower_right)
+    torch = pytest.importorskip("torch")
+    from torch.nn.attention.bias import causal_lower_right
+    lq, lk = [3, 1, 9, 4], [10, 6, 9, 30]
+    q = _rand((sum(lq), 4, 8), 53)
+    k, v = _rand((sum(lk), 1, 8), 54), _rand((sum(lk), 1, 8), 55)
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, 0.3, causal=True)
+    for b in range(4):
+        mask = causal_lower_right(lq[b], lk[b])._materialize()
+        Or, Lr = _sdpa_with_lse(torch, q[cq[b]:cq[b + 1]], k[ck[b]:ck[b + 1]], v[ck[b]:ck[b + 1]],
+                                0.3, mask)
+        np.testing.assert_allclose(O[cq[b]:cq[b + 1]], Or, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(L[:, cq[b]:cq[b + 1]], Lr, atol=1e-12, rtol=0)
+
+
+def pin_varlen_window_scalar():
+    # sliding windows with Lq_b != Lk_b agree, sequence by sequence, with the independent
+    # pure-Python implementation (which takes off = Nk - Nq itself)
+    lq, lk = [4, 6, 2], [7, 6, 9]
+    q = _rand((sum(lq), 2, 3), 56)
+    k, v = _rand((sum(lk), 2, 3), 57), _rand((sum(lk), 2, 3), 58)
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    for causal, left, right in ((False, 2, 1), (True, 3, -1), (False, -1, 0), (True, 0, 0)):
+        O, L = oracle.attention_varlen(q, k, v, cq, ck, 0.9, causal, left, right)
+        for b in range(3):
+            qs = q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None].tolist()
+            ks = k[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None].tolist()
+            vs = v[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None].tolist()
+            Os, Ls = attention_scalar(qs, ks, vs, 0.9, causal, left, right)
+            np.testing.assert_allclose(O[cq[b]:cq[b + 1]], np.array(Os[0]).transpose(1, 0, 2),
+                                       atol=1e-13, rtol=0)
+            np.testing.assert_allclose(L[:, cq[b]:cq[b + 1]], np.array(Ls[0]), atol=1e-13, rtol=0)
+
+
+def pin_varlen_empty_and_isolated():
+    # a sequence with no queries, one with queries but no keys (O = 0, LSE = -inf) and
+    # padding tokens after the last sequence; rows of one sequence do not depend on the
+    # tokens of any other
+    lq, lk = [3, 0, 4, 2], [5, 2, 0, 6]
+    q = _rand((sum(lq) + 2, 2, 4), 59)
+    k, v = _rand((sum(lk) + 3, 1, 4), 60), _rand((sum(lk) + 3, 1, 4), 61)
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, 0.5, causal=True)
+    assert np.all(O[3:7] == 0.0) and np.all(np.isneginf(L[:, 3:7]))     # no keys
+    assert np.all(O[9:] == 0.0) and np.all(np.isneginf(L[:, 9:]))       # padding
+    assert np.all(np.isfinite(L[:, :3])) and np.all(np.isfinite(L[:, 7:9]))
+    # sequence 3 (Lq 2, Lk 6): the last query sees all 6 keys, the first 5 of them
+    np.testing.assert_allclose(O[8, 0], _ORIG_ATT(q[8:9].transpose(1, 0, 2)[None], k[7:13, :, :].transpose(1, 0, 2)[None],
+                                                  v[7:13].transpose(1, 0, 2)[None], 0.5)[0][0, 0, 0], atol=1e-13)
+    k2, v2, q2 = k.copy(), v.copy(), q.copy()
+    k2[:5] += 1.0
+    v2[:5] *= -3.0
+    q2[:3] += 2.0
+    O2, L2 = oracle.attention_varlen(q2, k2, v2, cq, ck, 0.5, causal=True)
+    np.testing.assert_array_equal(O2[3:], O[3:])
+    np.testing.assert_array_equal(L2[:, 3:], L[:, 3:])
+    # the row-sampling form returns the same rows (up to the BLAS summation order)
+    rows = [(0, 1), (2, 0), (4, 1), (8, 0), (9, 1)]
+    Or, Lr = oracle.attention_varlen(q, k, v, cq, ck, 0.5, causal=True, rows=rows)
+    for n, (t, h) in enumerate(rows):
+        np.testing.assert_allclose(Or[n], O[t, h], atol=1e-14, rtol=0)
+        assert Lr[n] == L[h, t] or abs(Lr[n] - L[h, t]) <= 1e-14
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
-        pin_config4_pairs]
+        pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
+        pin_varlen_window_scalar, pin_varlen_empty_and_isolated]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -339,6 +447,30 @@ def _gqa_mod_attention(q, k, v, scale, causal=False, left=-1, right=-1, rows=Non
 
 _ORIG_ATT = OA.attention
 
+def _mut_varlen_no_isolation(q, k, v, cu_q, cu_k, scale, causal=False, left=-1, right=-1,
+                             rows=None):
+    # plausible mistake: every sequence attends to the keys of the whole pack
+    tk = np.asarray(k).shape[0]
+    cq = np.asarray(cu_q)
+    return _ORIG_VARLEN(q, k, v, cq, np.concatenate([[0], np.full(len(cq) - 1, tk)]), scale,
+                        causal, left, right, rows)
+
+
+def _mut_varlen_top_left(q, k, v, cu_q, cu_k, scale, causal=False, left=-1, right=-1, rows=None):
+    # plausible mistake: top-left causal alignment inside each sequence (key j visible to
+    # query i iff j <= i), i.e. only the first Lq_b keys of a longer sequence ever count
+    cq, ck = np.asarray(cu_q), np.asarray(cu_k)
+    lq = cq[1:] - cq[:-1]
+    lk = ck[1:] - ck[:-1]
+    keep = np.minimum(lk, lq) if causal else lk
+    idx = np.concatenate([np.arange(ck[b], ck[b] + keep[b]) for b in range(len(lq))]).astype(int)
+    ck2 = np.concatenate([[0], np.cumsum(keep)])
+    return _ORIG_VARLEN(q, np.asarray(k)[idx], np.asarray(v)[idx], cq, ck2, scale, causal, left,
+                        right, rows)
+
+
+_ORIG_VARLEN = OA.attention_varlen
+
 MUTATIONS = {
     "exclusive_window": ("visible", _mut_exclusive_window),
     "top_left_causal": ("visible", _mut_top_left_causal),
@@ -348,6 +480,8 @@ MUTATIONS = {
     "wrong_sign": ("_rows_attention", _mut_rows_sign),
     "unweighted_merge": ("lse_merge", _mut_merge_unweighted),
     "gqa_modulo": ("attention", _gqa_mod_attention),
+    "varlen_no_isolation": ("attention_varlen", _mut_varlen_no_isolation),
+    "varlen_top_left": ("attention_varlen", _mut_varlen_top_left),
 }
 
 
