@@ -5,9 +5,10 @@ One *step* is one ``mfa_fwd`` call over the dense causal prefill workload
 before timing).  ``value`` is its throughput in TFLOP/s, counting 4*D FLOP per
 *visible* (query, key) pair.  In the same run the other workloads are timed the same
 way and reported under ``workloads``: the GQA long-context prefill (bf16, N=16384),
-the sliding-window prefill (window (512, 0)), and the paged split-KV decode (HBM
+the sliding-window prefill (window (512, 0)), the paged split-KV decode (HBM
 GB/s over the algorithmic bytes: every cached K/V byte once, plus q, out, LSE, the
-block-table entries used and seq_lens).
+block-table entries used and seq_lens), and the packed variable-length causal prefill
+(``mfa_fwd_varlen``, 16 sequences of 256..4096 tokens, TFLOP/s over visible pairs).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
 workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
@@ -15,7 +16,7 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -148,6 +149,48 @@ def bench_prefill(i, step, steps):
     }
 
 
+def setup_varlen():
+    """Device inputs and one step (one mfa_fwd_varlen call) of the packed workload."""
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(6)
+    x = A.config_inputs(6)
+    q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
+    cq = torch.from_numpy(x.cu_seqlens_q).to("cuda")
+    ck = torch.from_numpy(x.cu_seqlens_k).to("cuda")
+    lq, lk = np.diff(x.cu_seqlens_q), np.diff(x.cu_seqlens_k)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+
+    def step():
+        ea.mfa_fwd_varlen(q, k, v, cq, ck, int(lq.max()), int(lk.max()), scale=c["scale"],
+                          causal=c["causal"], win_left=c["left"], win_right=c["right"], out=out,
+                          lse=lse)
+
+    step.lens = (lq, lk)
+    return step
+
+
+def bench_varlen(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(6)
+    ms, wall = time_calls(step, steps)
+    info = ea.mfa_last_dispatch()
+    lq, lk = step.lens
+    pairs = sum(visible_pairs(int(a), int(b), c["causal"], c["left"], c["right"]) for a, b in zip(lq, lk))
+    flop = 4.0 * c["D"] * pairs * c["Hq"]
+    tf = flop / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {c['dtype']} "
+                    f"causal={int(c['causal'])} lengths in [{c['len_lo']},{c['len_hi']}] "
+                    f"(total {int(lq.sum())} tokens)",
+        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config6", "fwd")},
+        "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
+    }
+
+
 def decode_bytes(p, Hkv, D, Hq):
     L = p.seq_lens.astype(np.int64)
     kv = int(L.sum()) * Hkv * D * 2 * 2
@@ -233,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5")
+    ap.add_argument("--workloads", default="2,3,4,5,6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -252,7 +295,8 @@ def main():
     wl = [int(s) for s in args.workloads.split(",") if s]
     if 2 not in wl:
         wl = [2] + wl
-    steps = {i: (setup_decode() if i == 5 else setup_prefill(i)) for i in wl}
+    setup = {5: setup_decode, 6: setup_varlen}
+    steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
     for i in wl:
@@ -261,7 +305,12 @@ def main():
     torch.cuda.synchronize()
     res = {}
     for i in wl:
-        res[i] = bench_decode(steps[i], args.steps) if i == 5 else bench_prefill(i, steps[i], args.steps)
+        if i == 5:
+            res[i] = bench_decode(steps[i], args.steps)
+        elif i == 6:
+            res[i] = bench_varlen(steps[i], args.steps)
+        else:
+            res[i] = bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)
 
     head = res[2]

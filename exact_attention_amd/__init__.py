@@ -57,6 +57,10 @@ _SIGS = {
     "mfa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_fwd_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                              _VP, _VP]),
+    "mfa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                            _I, _I, _I, _I, _VP]),
+    "mfa_fwd_varlen_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
+                                    _I, _F, _I, _I, _I, _I, _VP, _VP]),
     "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "mfa_decode_num_splits": (_I, [_I, _I, _I]),
     "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -211,6 +215,57 @@ def mfa_fwd_tilelog(q, k, v, tile_log, **kw):
     return mfa_fwd(q, k, v, tile_log=tile_log, **kw)
 
 
+def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   scale: float | None = None, causal: bool = False, win_left: int = -1,
+                   win_right: int = -1, out=None, lse=None, return_lse: bool = True,
+                   tile_log=None):
+    """Packed variable-length forward on torch tensors.
+
+    q [total_q, Hq, D], k/v [total_k, Hkv, D] (fp16 or bf16, token-major); cu_seqlens_q /
+    cu_seqlens_k int32 [B + 1] device tensors; max_seqlen_q / max_seqlen_k host ints
+    bounding every sequence's lengths.  Returns ``(out, lse)`` with lse [Hq, total_q].
+    ``scale`` defaults to 1/sqrt(D) here.  ``tile_log`` selects ``mfa_fwd_varlen_tilelog``.
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [total_q, Hq, D] and k, v [total_k, Hkv, D]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D:
+        raise ValueError("head dimension mismatch")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.numel() - 1
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)):
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must match q")
+    args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else None,
+            _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"),
+            B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, float(scale),
+            int(bool(causal)), int(win_left), int(win_right), dt, _stream(q)]
+    if tile_log is None:
+        _check(lib().mfa_fwd_varlen(*args), "mfa_fwd_varlen")
+    else:
+        if tile_log.dtype != torch.int32:
+            raise TypeError("tile_log must be int32")
+        _check(lib().mfa_fwd_varlen_tilelog(*args, _dev(tile_log, "tile_log")),
+               "mfa_fwd_varlen_tilelog")
+    return out, lse
+
+
 def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
                      num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
                      workspace=None):
@@ -257,5 +312,6 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
 
 
 __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
+           "mfa_fwd_varlen",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
            "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version"]

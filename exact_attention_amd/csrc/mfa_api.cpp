@@ -79,7 +79,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* out, float* ls
                        win_right, dtype);
     if (st) return st;
     MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, Nq, Nk, D, scale,
-                    causal, win_left, win_right, dtype};
+                    causal, win_left, win_right, dtype, nullptr, nullptr, 0, 0};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 1;
@@ -89,6 +89,54 @@ int fwd_common(const void* q, const void* k, const void* v, void* out, float* ls
     mfa_plan plan;
     plan_fill(Nq, Nk, D, causal, win_left, win_right, &plan, nullptr);
     info.planned = plan.visited * (long long)B * Hq;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
+int check_varlen(const void* q, const void* k, const void* v, void* out, const float* lse,
+                 const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv, int total_q,
+                 int total_k, int max_q, int max_k, int D, float scale, int causal, int win_left,
+                 int win_right, int dtype) {
+    if (!q || !k || !v || !out || !cu_q || !cu_k) return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1)
+        return MFA_ERR_SHAPE;
+    if (causal != 0 && causal != 1) return MFA_ERR_ARG;
+    if (Hq % Hkv != 0) return MFA_ERR_GQA;
+    if (win_left < -1 || win_right < -1) return MFA_ERR_WINDOW;
+    if (!isfinite(scale)) return MFA_ERR_SCALE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        ((uintptr_t)cu_q & 3u) || ((uintptr_t)cu_k & 3u) || (lse && ((uintptr_t)lse & 3u)))
+        return MFA_ERR_ALIGN;
+    const int64_t nqt = ((int64_t)max_q + mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (nqt * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
+    if ((double)total_q * Hq * D > 4e18 || (double)total_k * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
+    // one sequence's rows (plus a tile's worth past its end) are addressed with 32-bit
+    // byte offsets
+    if (((int64_t)max_q + mfa_fwd_bm()) * Hq * D * 2 > 0x7fffffffLL ||
+        ((int64_t)max_k + 64) * Hkv * D * 2 > 0x7fffffffLL)
+        return MFA_ERR_OVERFLOW;
+    return MFA_OK;
+}
+
+int varlen_common(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv, int total_q,
+                  int total_k, int max_q, int max_k, int D, float scale, int causal,
+                  int win_left, int win_right, int dtype, void* stream, int32_t* tile_log) {
+    int st = check_varlen(q, k, v, out, lse, cu_q, cu_k, B, Hq, Hkv, total_q, total_k, max_q,
+                          max_k, D, scale, causal, win_left, win_right, dtype);
+    if (st) return st;
+    MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, max_q, max_k, D, scale,
+                    causal, win_left, win_right, dtype, cu_q, cu_k, total_q, total_k};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = 3;
+    info.n_launches = 1;
+    info.planned = -1;   // the sequence lengths are on the device
+    st = mfa_fwd_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
     g_last = info;
     g_have_last = true;
     return MFA_OK;
@@ -148,6 +196,28 @@ int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, floa
     if ((uintptr_t)tile_log & 3u) return MFA_ERR_ALIGN;
     return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
                       win_right, dtype, stream, tile_log);
+}
+
+int mfa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
+                   int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                   float scale, int causal, int win_left, int win_right, int dtype,
+                   void* stream) {
+    return varlen_common(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                         total_k, max_seqlen_q, max_seqlen_k, D, scale, causal, win_left,
+                         win_right, dtype, stream, nullptr);
+}
+
+int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                           int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                           int max_seqlen_k, int D, float scale, int causal, int win_left,
+                           int win_right, int dtype, void* stream, int32_t* tile_log) {
+    if (!tile_log) return MFA_ERR_NULL;
+    if ((uintptr_t)tile_log & 3u) return MFA_ERR_ALIGN;
+    return varlen_common(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                         total_k, max_seqlen_q, max_seqlen_k, D, scale, causal, win_left,
+                         win_right, dtype, stream, tile_log);
 }
 
 int mfa_decode_num_splits(int page_size, int max_pages_per_seq, int num_splits) {

@@ -72,12 +72,17 @@ struct FwdArgs {
     uint16_t* o;
     float* lse;
     int32_t* tile_log;
-    int B, Hq, Hkv, Nq, Nk, g;
+    int B, Hq, Hkv, Nq, Nk, g;   // packed sequences: Nq, Nk = max_seqlen_q, max_seqlen_k
     int n_q_tiles;
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
     float scale_log2_abs;  // |scale| * log2(e)
-    MfaMask mask;
+    MfaMask mask;    // dense layout only (packed sequences build theirs per sequence)
+    // packed sequences ([total, H, D] token-major, delimited by cu_seqlens)
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int total_q, total_k;
+    int causal, left, right;
 };
 
 template <int N>
@@ -132,7 +137,24 @@ __device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p)
     return mfa_lds_read_tr16(p);
 }
 
-template <int D, int DT, int GROUPS, bool TILELOG, bool NEG>
+// Sequence s of a pack: tokens [cu[s], cu[s+1]) clamped into [0, total] and to at most
+// max_len of them, so that every access stays inside the packed tensors whatever the
+// offsets hold.  Uniform over the workgroup (scalar loads of a uniform index).
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int total, int max_len,
+                                           int* start, int* len) {
+    int s0 = __builtin_amdgcn_readfirstlane(cu[s]);
+    int s1 = __builtin_amdgcn_readfirstlane(cu[s + 1]);
+    s0 = s0 < 0 ? 0 : (s0 > total ? total : s0);
+    s1 = s1 < s0 ? s0 : (s1 > total ? total : s1);
+    *start = s0;
+    *len = (s1 - s0) > max_len ? max_len : (s1 - s0);
+}
+
+// VAR: packed variable-length sequences.  Q, O are [total_q, Hq, D] and K, V
+// [total_k, Hkv, D] (rows of one head are Hq * D / Hkv * D elements apart), sequence b
+// spans cu_q[b] .. cu_q[b+1] - 1 and cu_k[b] .. cu_k[b+1] - 1, and its mask is aligned
+// bottom-right on its own lengths.  LSE is [Hq, total_q].
+template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, bool VAR>
 __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     using T = Tile<D>;
     constexpr int BN = kBN;
@@ -173,28 +195,52 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int kvh = h / a.g;
     const int q0 = qt * kBM;
 
+    // this (batch, head)'s sequence: lengths, first tokens and mask
+    int Nq = a.Nq, Nk = a.Nk;
+    int qs = 0, ks = 0;
+    MfaMask mask = a.mask;
+    if constexpr (VAR) {
+        seq_bounds(a.cu_q, b, a.total_q, a.Nq, &qs, &Nq);
+        seq_bounds(a.cu_k, b, a.total_k, a.Nk, &ks, &Nk);
+        mask = mfa_make_mask(Nq, Nk, a.causal, a.left, a.right);
+        if (q0 >= Nq) {   // past the end of this sequence's queries (uniform)
+            if (TILELOG && tid == 0) {
+                int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
+                t[0] = -1;
+                t[1] = 0;
+                t[2] = 0;
+                t[3] = -1;
+            }
+            return;
+        }
+    }
+    // row strides (elements) and the first element of this head's rows
+    const int SQ = VAR ? a.Hq * D : D;
+    const int SK = VAR ? a.Hkv * D : D;
+
     // with two wave groups the visited key tiles [t_lo, t_hi) are split between them:
     // group 0 takes the first ceil(n/2), group 1 the rest
     int t_lo, t_hi;
-    mfa_tile_range(a.mask, a.Nq, kBM, BN, qt, &t_lo, &t_hi);
+    mfa_tile_range(mask, Nq, kBM, BN, qt, &t_lo, &t_hi);
     const int n_all = t_hi - t_lo;
     const int n0 = GROUPS == 1 ? n_all : (n_all + 1) >> 1;
     const int kt_lo = grp == 0 ? t_lo : t_lo + n0;
     const int n = grp == 0 ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
 
-    const size_t head_q = (size_t)(b * a.Hq + h) * (size_t)a.Nq;
-    const size_t head_kv = (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk;
-    const uint16_t* kg = a.k + head_kv * D;
-    const uint16_t* vg = a.v + head_kv * D;
+    const size_t q_base = VAR ? ((size_t)qs * a.Hq + h) * D : (size_t)(b * a.Hq + h) * (size_t)a.Nq * D;
+    const size_t kv_base = VAR ? ((size_t)ks * a.Hkv + kvh) * D : (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk * D;
+    const uint16_t* kg = a.k + kv_base;
+    const uint16_t* vg = a.v + kv_base;
 
     const int qrow = q0 + wave * 32 + l32;
-    const bool qvalid = qrow < a.Nq;
+    const bool qvalid = qrow < Nq;
 
     // ---- Q^T operand in registers (rows past Nq read as zero) --------------------
     mfa_u32x4 qreg[NKB];
     {
-        const auto rq = mfa_rsrc(a.q + head_q * D, (uint32_t)a.Nq * D * 2);
-        const uint32_t off = ((uint32_t)qrow * D + g32 * 8) * 2;
+        // the range ends with the last row's D elements, so rows >= Nq fall outside it
+        const auto rq = mfa_rsrc(a.q + q_base, (uint32_t)((Nq - 1) * SQ + D) * 2);
+        const uint32_t off = ((uint32_t)qrow * SQ + g32 * 8) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) qreg[kb] = mfa_load16(rq, off + kb * 32);
         // complete here, so that no wait for them is left to the key loop (vmcnt is one
@@ -203,9 +249,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
 
     // per-row visible key bounds (inclusive), clamped into int range
-    const int64_t rlo64 = mfa_row_lo(a.mask, qrow);
-    const int64_t rhi64 = mfa_row_hi(a.mask, qrow);
-    const int row_lo = rlo64 > a.Nk ? a.Nk : (int)rlo64;
+    const int64_t rlo64 = mfa_row_lo(mask, qrow);
+    const int64_t rhi64 = mfa_row_hi(mask, qrow);
+    const int row_lo = rlo64 > Nk ? Nk : (int)rlo64;
     const int row_hi = rhi64 < -1 ? -1 : (int)rhi64;
 
     mfa_f32x16 oacc[NDB];
@@ -225,23 +271,28 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     uint32_t kld_off, vld_off;
     {
         const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
-        kld_off = (uint32_t)(row * D + T::k_phys(row, phys) * 8) * 2;
-        vld_off = (uint32_t)(row * D + T::v_phys(row, phys) * 8) * 2;
+        kld_off = (uint32_t)(row * SK + T::k_phys(row, phys) * 8) * 2;
+        vld_off = (uint32_t)(row * SK + T::v_phys(row, phys) * 8) * 2;
     }
     // One buffer range per tile: rows from k0 on (an empty range when the tile is not
     // needed, which makes the copies zero-filling no-ops into a free buffer); copy i of a
-    // thread is at a fixed offset from the tile start.
+    // thread is at a fixed offset from the tile start, kept in a vector register of its
+    // own (the range check applies to it).  Packed rows are SK apart, so there the range
+    // ends with the last row's D elements.
     auto tile_rsrc = [&](const uint16_t* src, int kt, bool need) {
         const int k0 = need ? kt * BN : 0;
-        return mfa_rsrc(src + (size_t)k0 * D, need ? (uint32_t)max(a.Nk - k0, 0) * D * 2 : 0u);
+        const int rows = need ? max(Nk - k0, 0) : 0;
+        const int bytes = VAR ? (rows > 0 ? ((rows - 1) * SK + D) * 2 : 0) : rows * D * 2;
+        return mfa_rsrc(src + (size_t)k0 * SK, (uint32_t)bytes);
     };
+    const uint32_t copy_step = (uint32_t)(4 * RPB * SK * 2);
     auto copy_k = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
         constexpr int buf = decltype(buf_c)::value;
-        mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * (4 * RPB * D * 2));
+        mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * copy_step);
     };
     auto copy_v = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
         constexpr int buf = decltype(buf_c)::value;
-        mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * (4 * RPB * D * 2));
+        mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * copy_step);
     };
     auto issue_k = [&](int kt, auto buf_c) {
         const auto r = tile_rsrc(kg, kt, true);
@@ -332,7 +383,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         const auto rk = tile_rsrc(kg, kt + 2, j + 2 < n);
         const auto rv = tile_rsrc(vg, kt + 1, j + 1 < n);
 
-        if (!mfa_tile_full(a.mask, kBM, BN, qt, kt)) {
+        if (!mfa_tile_full(mask, kBM, BN, qt, kt)) {
             const int k0 = kt * BN;
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb)
@@ -484,7 +535,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const float l_tot = l_run + mfa_swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qvalid) {
-        uint16_t* op = a.o + (head_q + (size_t)qrow) * D + 4 * g32;
+        uint16_t* op = a.o + q_base + (size_t)qrow * SQ + 4 * g32;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -495,8 +546,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
                 *(mfa_u32x2*)(op + db * 32 + 8 * j) = w2;
             }
         }
-        if (a.lse != nullptr && g32 == 0)
-            a.lse[head_q + qrow] = l_tot > 0.f ? (m_run + mfa_log2(l_tot)) * MFA_LN2 : -MFA_INF;
+        if (a.lse != nullptr && g32 == 0) {
+            const size_t li = VAR ? (size_t)h * a.total_q + qs + qrow : (size_t)(b * a.Hq + h) * a.Nq + qrow;
+            a.lse[li] = l_tot > 0.f ? (m_run + mfa_log2(l_tot)) * MFA_LN2 : -MFA_INF;
+        }
     }
     if (TILELOG && tid == 0) {
         int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
@@ -507,29 +560,29 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
 }
 
-template <int D, int DT, int G, bool TL>
+template <int D, int DT, int G, bool TL, bool VAR>
 void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
     const dim3 block(G * kGroupThreads);
     if (neg)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true, VAR>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false, VAR>), grid, block, 0, stream, a);
 }
 
-template <int D, int DT>
+template <int D, int DT, bool VAR>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
     const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
     if (groups == 2) {
-        if (tilelog) launch_sign<D, DT, 2, true>(a, grid, stream, neg);
-        else launch_sign<D, DT, 2, false>(a, grid, stream, neg);
+        if (tilelog) launch_sign<D, DT, 2, true, VAR>(a, grid, stream, neg);
+        else launch_sign<D, DT, 2, false, VAR>(a, grid, stream, neg);
     } else {
-        if (tilelog) launch_sign<D, DT, 1, true>(a, grid, stream, neg);
-        else launch_sign<D, DT, 1, false>(a, grid, stream, neg);
+        if (tilelog) launch_sign<D, DT, 1, true, VAR>(a, grid, stream, neg);
+        else launch_sign<D, DT, 1, false, VAR>(a, grid, stream, neg);
     }
-    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups, tilelog ? ",tilelog" : "",
-             neg ? ",neg" : "");
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups, VAR ? ",varlen" : "",
+             tilelog ? ",tilelog" : "", neg ? ",neg" : "");
     info->BM = kBM;
     info->BN = kBN;
     info->waves = groups * kGroupThreads / 64;
@@ -549,9 +602,8 @@ int mfa_fwd_bn(int) { return kBN; }
 // tiles.  A small grid (at most two workgroups per CU: every workgroup resident at
 // once, so the longest query tile bounds the run) instead gets one 8-wave workgroup
 // per CU whose two groups split the key range of the query tile.
-int mfa_fwd_groups(int B, int Hq, int Nq, int num_cus) {
-    const long long wgs = (long long)((Nq + kBM - 1) / kBM) * B * Hq;
-    return wgs <= 2LL * num_cus ? 2 : 1;
+int mfa_fwd_groups(long long q_tiles, int Hq, int num_cus) {
+    return q_tiles * Hq <= 2LL * num_cus ? 2 : 1;
 }
 int mfa_fwd_bm() { return kBM; }
 
@@ -572,6 +624,14 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.n_q_tiles = (pr.Nq + kBM - 1) / kBM;
     a.HB = pr.B * pr.Hq;
     a.xcd_group = ((pr.B * pr.Hkv) % 8 == 0) ? 1 : 0;
+    a.cu_q = pr.cu_seqlens_q;
+    a.cu_k = pr.cu_seqlens_k;
+    a.total_q = pr.total_q;
+    a.total_k = pr.total_k;
+    a.causal = pr.causal;
+    a.left = pr.left;
+    a.right = pr.right;
+    const bool var = pr.cu_seqlens_q != nullptr;
     // |scale| * log2(e), kept >= 1e-30 so that a masked (-inf) score times it stays
     // -inf; for scale = 0 the visible scores then all scale to ~0, i.e. the same
     // uniform weights up to fp32 rounding
@@ -579,10 +639,21 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.mask = mfa_make_mask(pr.Nq, pr.Nk, pr.causal, pr.left, pr.right);
     const bool tl = pr.tile_log != nullptr;
     const bool neg = pr.scale < 0.f;
-    const int groups = mfa_fwd_groups(pr.B, pr.Hq, pr.Nq, mfa_num_cus());
+    // query tiles that hold rows: every tile of the grid for dense inputs; for packed
+    // sequences at most total_q / BM + B of the grid's B * ceil(max_seqlen_q / BM)
+    long long q_tiles = (long long)a.n_q_tiles * pr.B;
+    if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
+    const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
+    if (var) {
+        if (pr.D == 128)
+            return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, true>(a, stream, groups, tl, neg, info)
+                                       : launch<128, MFA_DT_BF16, true>(a, stream, groups, tl, neg, info);
+        return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, true>(a, stream, groups, tl, neg, info)
+                                   : launch<64, MFA_DT_BF16, true>(a, stream, groups, tl, neg, info);
+    }
     if (pr.D == 128)
-        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, groups, tl, neg, info)
-                                   : launch<128, MFA_DT_BF16>(a, stream, groups, tl, neg, info);
-    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, groups, tl, neg, info)
-                               : launch<64, MFA_DT_BF16>(a, stream, groups, tl, neg, info);
+        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, false>(a, stream, groups, tl, neg, info)
+                                   : launch<128, MFA_DT_BF16, false>(a, stream, groups, tl, neg, info);
+    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, false>(a, stream, groups, tl, neg, info)
+                               : launch<64, MFA_DT_BF16, false>(a, stream, groups, tl, neg, info);
 }

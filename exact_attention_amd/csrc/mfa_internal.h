@@ -17,6 +17,11 @@ struct MfaFwdProblem {
     float scale;
     int causal, left, right;
     int dtype;
+    // packed variable-length sequences (NULL for the dense [B, H, N, D] layout): Nq, Nk
+    // then hold max_seqlen_q, max_seqlen_k
+    const int32_t* cu_seqlens_q;
+    const int32_t* cu_seqlens_k;
+    int total_q, total_k;
 };
 
 struct MfaDecodeProblem {
@@ -41,7 +46,7 @@ int mfa_num_cus();
 
 int mfa_fwd_bm();
 int mfa_fwd_bn(int D);
-int mfa_fwd_groups(int B, int Hq, int Nq, int num_cus);
+int mfa_fwd_groups(long long q_tiles, int Hq, int num_cus);
 int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
 
 int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits);

@@ -1,8 +1,8 @@
 /*
  * mfa.h — C ABI of the MI355X (gfx950) fused exact-attention library, libmfa.so.
  *
- * Two operations, both exact attention O = softmax(scale * Q K^T + mask) V with an
- * fp32 online softmax that never materialises the score matrix:
+ * Exact attention O = softmax(scale * Q K^T + mask) V with an fp32 online softmax that
+ * never materialises the score matrix:
  *
  *   mfa_fwd           tiled forward (prefill) with causal / sliding-window key-tile
  *                     skipping and grouped-query head mapping; writes O and the row
@@ -11,6 +11,9 @@
  *                     max m and sum l in fp32, O = o / l, LSE = m + log l) and the
  *                     mlx-mfa 2.5.2 page's feature list ("Causal tile-skip",
  *                     "Sliding window", "Native GQA").
+ *   mfa_fwd_varlen    the same forward over packed sequences of different lengths
+ *                     delimited by cu_seqlens (mlx-mfa "Variable-length"), each
+ *                     sequence masked on its own lengths.
  *   mfa_decode_paged  single-query decode over a paged KV cache, split across
  *                     workgroups along the keys, with partial (O, LSE) pairs merged in
  *                     a second pass.  Defined by the mlx-mfa 2.5.2 page ("Flash Decode
@@ -115,6 +118,44 @@ int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, floa
                     int causal, int win_left, int win_right, int dtype, void* stream,
                     int32_t* tile_log);
 
+/* Forward pass over packed variable-length sequences (mlx-mfa 2.5.2 feature list:
+ * "Variable-length", packed sequences delimited by cu_seqlens; the page's note that
+ * the causal varlen output for N_q < N_k was corrected).  Each sequence is attended on
+ * its own, with the visibility rule above applied to its own lengths: for sequence b,
+ * Nq = Lq_b, Nk = Lk_b and off = Lk_b - Lq_b (bottom-right), so a chunk of Lq_b new
+ * queries after Lk_b - Lq_b earlier keys (chunked prefill) sees all of them.
+ *   q    [total_q, Hq,  D]  dtype   token-major: sequence b owns tokens
+ *                                   cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   k, v [total_k, Hkv, D]  dtype   sequence b owns cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1
+ *   out  [total_q, Hq,  D]  dtype   rows of tokens outside every sequence are not written
+ *   lse  [Hq, total_q]      float32 or NULL (natural log, as for mfa_fwd)
+ *   cu_seqlens_q, cu_seqlens_k: int32 [B + 1] device memory, read by the kernel
+ *   max_seqlen_q, max_seqlen_k: host upper bounds of Lq_b and Lk_b (they size the grid)
+ * Device-side contract (the offsets stay on the device and are not checked on the
+ * host): both arrays are non-decreasing, start at >= 0 and end at <= total_q / total_k,
+ * and Lq_b <= max_seqlen_q, Lk_b <= max_seqlen_k.  Out of contract the kernel stays in
+ * bounds (offsets are clamped into the tensors and lengths to the maxima) but the result
+ * is unspecified.  Lq_b = 0 writes nothing; Lq_b > 0 with Lk_b = 0 gives O = 0 and
+ * LSE = -inf on those rows.  mfa_last_dispatch reports planned = -1 (lengths unknown
+ * on the host).
+ * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE, _GQA, _WINDOW, _SCALE, _ALIGN, _ARG,
+ * _OVERFLOW, _HIP. */
+int mfa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   int B, int Hq, int Hkv, int total_q, int total_k,
+                   int max_seqlen_q, int max_seqlen_k, int D, float scale,
+                   int causal, int win_left, int win_right, int dtype, void* stream);
+
+/* mfa_fwd_varlen plus the per-tile visit record of mfa_fwd_tilelog, indexed by
+ * (b, h, query tile t) with n_q_tiles = ceil(max_seqlen_q / BM); tiles past a
+ * sequence's end record (-1, 0, 0, -1). */
+int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int B, int Hq, int Hkv, int total_q, int total_k,
+                           int max_seqlen_q, int max_seqlen_k, int D, float scale,
+                           int causal, int win_left, int win_right, int dtype, void* stream,
+                           int32_t* tile_log);
+
 /* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).
  * Returns 0 if the arguments are invalid. */
 size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
@@ -157,13 +198,14 @@ int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
  * record: backend, operation, selection and split fields). */
 typedef struct {
     char kernel[96];      /* kernel name of the main launch */
-    int op;               /* 1 = forward, 2 = paged decode */
+    int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward */
     int BM, BN, waves;    /* forward tile configuration */
     int grid[3];          /* main launch grid */
     int block;            /* threads per workgroup */
     int num_splits;       /* decode: key splits (grid.x of the split kernel) */
     int chunk_tokens;     /* decode: logical tokens per split */
-    long long planned;    /* forward: key tiles visited over all (b, h); decode: 0 */
+    long long planned;    /* forward: key tiles visited over all (b, h); varlen: -1;
+                             decode: 0 */
     int n_launches;       /* kernels enqueued by the call */
 } mfa_dispatch_info;
 

@@ -127,6 +127,30 @@ def test_fwd_validation(kw, code):
     assert fwd(**kw) == code
 
 
+def fwd_varlen(**kw):
+    a = dict(q=A1, k=A2, v=A3, out=A4, lse=A5, cq=0x60000, ck=0x70000, B=3, Hq=4, Hkv=2, tq=300,
+             tk=400, mq=200, mk=250, D=64, scale=0.1, causal=1, left=-1, right=-1, dtype=1,
+             stream=None)
+    a.update(kw)
+    return ea.lib().mfa_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cq"], a["ck"],
+                                   a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                   a["D"], a["scale"], a["causal"], a["left"], a["right"],
+                                   a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(cq=None), -1), (dict(ck=None), -1), (dict(out=None), -1),
+    (dict(dtype=2), -5), (dict(D=32), -4), (dict(B=0), -2), (dict(tq=0), -2), (dict(tk=0), -2),
+    (dict(mq=0), -2), (dict(mk=0), -2), (dict(Hq=6, Hkv=4), -3), (dict(left=-3), -6),
+    (dict(scale=float("nan")), -7), (dict(q=A1 + 2), -12), (dict(cq=0x60002), -12),
+    (dict(lse=A5 + 1), -12), (dict(causal=-1), -13),
+    (dict(mq=1 << 24, Hq=64, Hkv=64), -10), (dict(mk=1 << 24, Hkv=4), -10),
+    (dict(B=1 << 20, Hq=64, Hkv=64, mq=1 << 20), -10),
+])
+def test_fwd_varlen_validation(kw, code):
+    assert fwd_varlen(**kw) == code
+
+
 def dec(**kw):
     a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, out=0x60000, lse=0x70000, B=2, Hq=8, Hkv=2, D=128,
              page_size=16, num_pages=10, max_pages=4, scale=0.1, num_splits=0, ws=0x80000,
