@@ -114,26 +114,87 @@ def paged_inputs(B: int, Hq: int, Hkv: int, D: int, dtype: str, seed: int, *,
     k_tok = _normal_bits(rng, (total, Hkv, D), dtype)
     v_tok = _normal_bits(rng, (total, Hkv, D), dtype)
 
+    block_table, k_pages, v_pages = _scatter_pages(k_tok, v_tok, seq_lens, perm, num_pages,
+                                                   page_size, max_pages_per_seq, dtype)
+    return PagedInputs(q, k_pages, v_pages, block_table, seq_lens.astype(np.int32),
+                       page_size, dtype, used)
+
+
+def _scatter_pages(k_tok, v_tok, seq_lens, perm, num_pages, page_size, max_pages_per_seq, dtype):
+    """Deal the permuted pages to the sequences in order and copy each sequence's tokens
+    (consecutive in ``k_tok`` / ``v_tok``) into them; everything else holds NaN."""
+    B = len(seq_lens)
+    Hkv, D = k_tok.shape[1:]
     block_table = np.full((B, max_pages_per_seq), -1, dtype=np.int32)
     k_pages = np.full((num_pages, page_size, Hkv, D), NAN_BITS[dtype], dtype=np.uint16)
     v_pages = np.full((num_pages, page_size, Hkv, D), NAN_BITS[dtype], dtype=np.uint16)
     cursor = 0
     tok0 = 0
     for b in range(B):
-        n = pages_per_seq[b]
+        L = int(seq_lens[b])
+        n = int(math.ceil(L / page_size))
         pages = perm[cursor:cursor + n]
         cursor += n
         block_table[b, :n] = pages
-        L = int(seq_lens[b])
-        # scatter the sequence's tokens page by page
         for j in range(n):
             t0 = j * page_size
             t1 = min(L, t0 + page_size)
             k_pages[pages[j], : t1 - t0] = k_tok[tok0 + t0: tok0 + t1]
             v_pages[pages[j], : t1 - t0] = v_tok[tok0 + t0: tok0 + t1]
         tok0 += L
-    return PagedInputs(q, k_pages, v_pages, block_table, seq_lens.astype(np.int32),
-                       page_size, dtype, used)
+    return block_table, k_pages, v_pages
+
+
+@dataclass
+class PagedVarlenInputs:
+    q: np.ndarray             # uint16 bits [total_q, Hq, D]
+    k_pages: np.ndarray       # uint16 bits [num_pages, page_size, Hkv, D]
+    v_pages: np.ndarray
+    block_table: np.ndarray   # int32 [B, max_pages_per_seq], -1 where unused
+    seq_lens_k: np.ndarray    # int32 [B]: cached tokens, the new ones included
+    cu_seqlens_q: np.ndarray  # int32 [B + 1]
+    page_size: int
+    dtype: str
+
+
+def paged_varlen_inputs(Hq: int, Hkv: int, D: int, dtype: str, seed: int, *,
+                        B: int | None = None, new_lo: int | None = None, new_hi: int | None = None,
+                        ctx_lo: int | None = None, ctx_hi: int | None = None, seqlens_q=None,
+                        ctx_lens=None, page_size: int = 16, max_pages_per_seq: int | None = None,
+                        extra_pages: int = 0) -> PagedVarlenInputs:
+    """Chunked prefill over a paged KV cache: each sequence has ``ctx_b`` earlier tokens
+    cached and ``Lq_b`` new ones whose K/V are already appended, so ``Lk_b = ctx_b + Lq_b``
+    and the queries are the last ``Lq_b`` positions (bottom-right alignment).
+
+    Draw order: new-token counts (uniform in ``[new_lo, new_hi]`` unless ``seqlens_q``
+    is given), context lengths (uniform in ``[ctx_lo, ctx_hi]`` unless ``ctx_lens``),
+    the page permutation, Q ``[total_q, Hq, D]``, then the K tokens and the V tokens of
+    every sequence in order.  Pages are dealt and filled as in ``paged_inputs``.
+    """
+    rng = np.random.default_rng(seed)
+    if seqlens_q is None:
+        seqlens_q = rng.integers(new_lo, new_hi, endpoint=True, size=B)
+    seqlens_q = np.asarray(seqlens_q, dtype=np.int64)
+    B = len(seqlens_q)
+    if ctx_lens is None:
+        ctx_lens = rng.integers(ctx_lo, ctx_hi, endpoint=True, size=B)
+    lk = np.asarray(ctx_lens, dtype=np.int64) + seqlens_q
+    pages_per_seq = [int(math.ceil(int(L) / page_size)) for L in lk]
+    used = int(sum(pages_per_seq))
+    num_pages = max(1, used + int(extra_pages))
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, max(pages_per_seq))
+    if max(pages_per_seq) > max_pages_per_seq:
+        raise ValueError("max_pages_per_seq too small for the drawn lengths")
+    perm = rng.permutation(num_pages).astype(np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int32)
+    q = _normal_bits(rng, (int(cu_q[-1]), Hq, D), dtype)
+    total_k = int(lk.sum())
+    k_tok = _normal_bits(rng, (total_k, Hkv, D), dtype)
+    v_tok = _normal_bits(rng, (total_k, Hkv, D), dtype)
+    bt, kp, vp = _scatter_pages(k_tok, v_tok, lk, perm, num_pages, page_size, max_pages_per_seq,
+                                dtype)
+    return PagedVarlenInputs(q, kp, vp, bt, lk.astype(np.int32), cu_q, page_size, dtype)
 
 
 @dataclass
@@ -197,6 +258,11 @@ CONFIGS = {
     # serving-style mix of prompt lengths, GQA heads of the long-context workload
     6: dict(name="packed_varlen_causal_prefill", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
             causal=True, left=-1, right=-1, len_lo=256, len_hi=4096, seed=106),
+    # chunked prefill over the paged cache (mlx-mfa "Paged + packed varlen queries"):
+    # new chunks of 512..2048 tokens after 1024..16384 cached ones, pages of 16
+    7: dict(name="paged_chunked_prefill", B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True,
+            left=-1, right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
+            ctx_hi=16384, seed=107),
 }
 
 
@@ -208,6 +274,10 @@ def config(i: int) -> dict:
 
 def config_inputs(i: int):
     c = config(i)
+    if i == 7:
+        return paged_varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
+                                   new_lo=c["new_lo"], new_hi=c["new_hi"], ctx_lo=c["ctx_lo"],
+                                   ctx_hi=c["ctx_hi"], page_size=c["page_size"])
     if i == 6:
         return varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
                              len_lo=c["len_lo"], len_hi=c["len_hi"])

@@ -16,6 +16,8 @@ tile by tile:
 * ``attention_varlen``: the same for sequences of different lengths packed along the
   token axis and delimited by ``cu_seqlens`` (mlx-mfa "Variable-length" feature),
   each sequence on its own with bottom-right alignment.
+* ``attention_varlen_paged``: packed queries whose keys come from a paged KV cache
+  (chunked prefill; mlx-mfa "Paged + packed varlen queries").
 * ``decode_paged``: single-query attention over a paged KV cache, gathered through
   the block table with its own loop (MXFlashAttn paged Split-KV decode; mlx-mfa
   "Paged KV" feature).
@@ -29,8 +31,10 @@ Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed
 forms, invariants, a pure-Python scalar implementation (``oracle.scalar``) and
 PyTorch's float64 CPU attention routine.  No function here is "parity unpinned".
 """
-from .reference import (attention, attention_probs, attention_varlen, decode_paged,
-                        gather_paged, lse_merge, visible, visited_tiles, widen, window_bounds)
+from .reference import (attention, attention_probs, attention_varlen, attention_varlen_paged,
+                        decode_paged, gather_paged, lse_merge, visible, visited_tiles, widen,
+                        window_bounds)
 
-__all__ = ["attention", "attention_probs", "attention_varlen", "decode_paged", "gather_paged",
-           "lse_merge", "visible", "visited_tiles", "widen", "window_bounds"]
+__all__ = ["attention", "attention_probs", "attention_varlen", "attention_varlen_paged",
+           "decode_paged", "gather_paged", "lse_merge", "visible", "visited_tiles", "widen",
+           "window_bounds"]

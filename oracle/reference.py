@@ -195,6 +195,32 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
     return O, L
 
 
+def attention_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
+                           scale: float, page_size: int, causal: bool = False, left: int = -1,
+                           right: int = -1, rows=None):
+    """Packed queries over a paged KV cache, float64 (mlx-mfa "Paged + packed varlen
+    queries"; MXFlashAttn paged-cache addressing).
+
+    q ``[total_q, Hq, D]`` with sequence ``b`` owning query tokens ``cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1``; its ``Lk_b = seq_lens_k[b]`` keys are gathered from the
+    ``[P, page_size, Hkv, D]`` pools through ``block_table`` (``gather_paged``).  The result
+    is ``attention_varlen`` over the gathered keys: each sequence on its own, bottom-right
+    aligned.  Returns O ``[total_q, Hq, D]`` and LSE ``[Hq, total_q]`` (or the sampled rows).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hkv, D = k_pages.shape[2], k_pages.shape[3]
+    B = len(seq_lens_k)
+    ks, vs = [], []
+    for b in range(B):
+        n = int(seq_lens_k[b])
+        ks.append(gather_paged(k_pages, block_table, b, n, page_size))
+        vs.append(gather_paged(v_pages, block_table, b, n, page_size))
+    k = np.concatenate(ks) if ks else np.zeros((0, Hkv, D))
+    v = np.concatenate(vs) if vs else np.zeros((0, Hkv, D))
+    cu_k = np.concatenate([[0], np.cumsum([int(x) for x in seq_lens_k])])
+    return attention_varlen(q, k, v, cu_seqlens_q, cu_k, scale, causal, left, right, rows)
+
+
 def attention_probs(q, k, scale: float, causal=False, left=-1, right=-1):
     """The probability matrix P ``[B, Hq, Nq, Nk]`` (small sizes only)."""
     q = np.asarray(q, dtype=np.float64)

@@ -76,3 +76,15 @@ def test_config6_shape():
     x = A.config_inputs(6)
     L = np.diff(x.cu_seqlens_q)
     assert L.min() >= 256 and L.max() <= 4096 and x.q.shape[1:] == (32, 128)
+
+
+def test_paged_varlen_layout():
+    p = A.paged_varlen_inputs(4, 2, 8, "f16", 13, seqlens_q=[3, 20, 1], ctx_lens=[0, 17, 40],
+                              extra_pages=2)
+    assert p.seq_lens_k.tolist() == [3, 37, 41] and p.cu_seqlens_q.tolist() == [0, 3, 23, 24]
+    assert p.q.shape == (24, 4, 8) and p.k_pages.shape == (1 + 3 + 3 + 2, 16, 2, 8)
+    assert p.block_table.shape == (3, 3) and p.block_table[0, 1] == -1
+    used = np.concatenate([p.block_table[b, : -(-int(L) // 16)] for b, L in enumerate(p.seq_lens_k)])
+    assert len(set(used.tolist())) == len(used) == 7
+    c = A.config(7)
+    assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (8, 32, 8, 128, 16)

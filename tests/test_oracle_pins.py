@@ -363,12 +363,59 @@ def pin_varlen_empty_and_isolated():
         assert Lr[n] == L[h, t] or abs(Lr[n] - L[h, t]) <= 1e-14
 
 
+def _paged_varlen_tokens(seed, Hq, Hkv, D, lq, ctx, extra_pages):
+    """The contiguous Q, K, V tokens of a paged_varlen_inputs draw, redrawn in its order."""
+    lq, ctx = np.asarray(lq), np.asarray(ctx)
+    lk = lq + ctx
+    rng = np.random.default_rng(seed)
+    rng.permutation(int(sum(-(-int(L) // 16) for L in lk)) + extra_pages)
+    q = oracle.widen(A._normal_bits(rng, (int(lq.sum()), Hq, D), "bf16"), "bf16")
+    k = oracle.widen(A._normal_bits(rng, (int(lk.sum()), Hkv, D), "bf16"), "bf16")
+    v = oracle.widen(A._normal_bits(rng, (int(lk.sum()), Hkv, D), "bf16"), "bf16")
+    return q, k, v, lk
+
+
+def pin_varlen_paged():
+    # chunked prefill over pages: each sequence equals torch's float64 SDPA under its
+    # bottom-right causal bias on the contiguous tokens (all ctx + new keys); a one-token
+    # chunk equals paged decode; moving the pages in the pool changes nothing
+    torch = pytest.importorskip("torch")
+    from torch.nn.attention.bias import causal_lower_right
+    lq, ctx = [5, 1, 17, 3], [40, 9, 0, 64]
+    p = A.paged_varlen_inputs(4, 2, 8, "bf16", 70, seqlens_q=lq, ctx_lens=ctx, extra_pages=2)
+    kp, vp, q = (oracle.widen(x, "bf16") for x in (p.k_pages, p.v_pages, p.q))
+    O, L = oracle.attention_varlen_paged(q, kp, vp, p.block_table, p.seq_lens_k, p.cu_seqlens_q,
+                                         0.35, 16, causal=True)
+    qt, kt, vt, lk = _paged_varlen_tokens(70, 4, 2, 8, lq, ctx, 2)
+    np.testing.assert_array_equal(qt, q)
+    cq = p.cu_seqlens_q
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    for b in range(4):
+        mask = causal_lower_right(lq[b], int(lk[b]))._materialize()
+        Or, Lr = _sdpa_with_lse(torch, q[cq[b]:cq[b + 1]], kt[ck[b]:ck[b + 1]], vt[ck[b]:ck[b + 1]],
+                                0.35, mask)
+        np.testing.assert_allclose(O[cq[b]:cq[b + 1]], Or, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(L[:, cq[b]:cq[b + 1]], Lr, atol=1e-12, rtol=0)
+    # sequence 1 has a one-token chunk: it is paged decode of that token
+    Od, Ld = oracle.decode_paged(q[cq[1]:cq[2]], kp, vp, p.block_table[1:2], p.seq_lens_k[1:2],
+                                 0.35, 16)
+    np.testing.assert_allclose(O[cq[1]], Od[0], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(L[:, cq[1]], Ld[0], atol=1e-13, rtol=0)
+    perm = np.random.default_rng(3).permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    bt2 = np.where(p.block_table >= 0, inv[np.maximum(p.block_table, 0)], -1)
+    O3, L3 = oracle.attention_varlen_paged(q, kp[perm], vp[perm], bt2, p.seq_lens_k, cq, 0.35, 16,
+                                           causal=True)
+    np.testing.assert_array_equal(O3, O)
+    np.testing.assert_array_equal(L3, L)
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
         pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
-        pin_varlen_window_scalar, pin_varlen_empty_and_isolated]
+        pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -471,6 +518,18 @@ def _mut_varlen_top_left(q, k, v, cu_q, cu_k, scale, causal=False, left=-1, righ
 
 _ORIG_VARLEN = OA.attention_varlen
 
+
+def _mut_varlen_paged_context_only(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
+                                  scale, page_size, causal=False, left=-1, right=-1, rows=None):
+    # plausible mistake: the new tokens' own keys are left out (Lk = context length only)
+    lq = np.diff(np.asarray(cu_seqlens_q))
+    ctx = np.maximum(np.asarray(seq_lens_k) - lq, 0)
+    return _ORIG_VARLEN_PAGED(q, k_pages, v_pages, block_table, ctx, cu_seqlens_q, scale,
+                              page_size, causal, left, right, rows)
+
+
+_ORIG_VARLEN_PAGED = OA.attention_varlen_paged
+
 MUTATIONS = {
     "exclusive_window": ("visible", _mut_exclusive_window),
     "top_left_causal": ("visible", _mut_top_left_causal),
@@ -482,6 +541,7 @@ MUTATIONS = {
     "gqa_modulo": ("attention", _gqa_mod_attention),
     "varlen_no_isolation": ("attention_varlen", _mut_varlen_no_isolation),
     "varlen_top_left": ("attention_varlen", _mut_varlen_top_left),
+    "varlen_paged_context_only": ("attention_varlen_paged", _mut_varlen_paged_context_only),
 }
 
 
