@@ -8,7 +8,9 @@ way and reported under ``workloads``: the GQA long-context prefill (bf16, N=1638
 the sliding-window prefill (window (512, 0)), the paged split-KV decode (HBM
 GB/s over the algorithmic bytes: every cached K/V byte once, plus q, out, LSE, the
 block-table entries used and seq_lens), and the packed variable-length causal prefill
-(``mfa_fwd_varlen``, 16 sequences of 256..4096 tokens, TFLOP/s over visible pairs).
+(``mfa_fwd_varlen``, 16 sequences of 256..4096 tokens, TFLOP/s over visible pairs), and
+chunked prefill over the paged cache (``mfa_fwd_varlen_paged``, 8 sequences, new chunks
+of 512..2048 tokens after 1024..16384 cached ones).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
 workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
@@ -16,7 +18,7 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -191,6 +193,51 @@ def bench_varlen(step, steps):
     }
 
 
+def setup_chunked():
+    """Device inputs and one step (one mfa_fwd_varlen_paged call) of the chunked prefill."""
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(7)
+    p = A.config_inputs(7)
+    q = to_dev(p.q, c["dtype"])
+    kp = to_dev(p.k_pages, c["dtype"])
+    vp = to_dev(p.v_pages, c["dtype"])
+    bt = torch.from_numpy(p.block_table).to("cuda")
+    sl = torch.from_numpy(p.seq_lens_k).to("cuda")
+    cq = torch.from_numpy(p.cu_seqlens_q).to("cuda")
+    lq = np.diff(p.cu_seqlens_q)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+
+    def step():
+        ea.mfa_fwd_varlen_paged(q, kp, vp, bt, sl, cq, int(lq.max()), scale=c["scale"],
+                                causal=c["causal"], win_left=c["left"], win_right=c["right"],
+                                out=out, lse=lse)
+
+    step.lens = (lq, p.seq_lens_k.astype(np.int64))
+    return step
+
+
+def bench_chunked(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(7)
+    ms, wall = time_calls(step, steps)
+    info = ea.mfa_last_dispatch()
+    lq, lk = step.lens
+    pairs = sum(visible_pairs(int(a), int(b), c["causal"], c["left"], c["right"]) for a, b in zip(lq, lk))
+    flop = 4.0 * c["D"] * pairs * c["Hq"]
+    tf = flop / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {c['dtype']} "
+                    f"page=16 new tokens {int(lq.sum())} in chunks of [{c['new_lo']},{c['new_hi']}], "
+                    f"cached keys {int(lk.sum())}",
+        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config7", "fwd")},
+        "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
+    }
+
+
 def decode_bytes(p, Hkv, D, Hq):
     L = p.seq_lens.astype(np.int64)
     kv = int(L.sum()) * Hkv * D * 2 * 2
@@ -276,7 +323,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5,6")
+    ap.add_argument("--workloads", default="2,3,4,5,6,7")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -295,7 +342,7 @@ def main():
     wl = [int(s) for s in args.workloads.split(",") if s]
     if 2 not in wl:
         wl = [2] + wl
-    setup = {5: setup_decode, 6: setup_varlen}
+    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked}
     steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
@@ -309,6 +356,8 @@ def main():
             res[i] = bench_decode(steps[i], args.steps)
         elif i == 6:
             res[i] = bench_varlen(steps[i], args.steps)
+        elif i == 7:
+            res[i] = bench_chunked(steps[i], args.steps)
         else:
             res[i] = bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)

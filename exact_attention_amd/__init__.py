@@ -61,6 +61,8 @@ _SIGS = {
                             _I, _I, _I, _I, _VP]),
     "mfa_fwd_varlen_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
                                     _I, _F, _I, _I, _I, _I, _VP, _VP]),
+    "mfa_fwd_varlen_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
+                                  _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "mfa_decode_num_splits": (_I, [_I, _I, _I]),
     "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -266,6 +268,53 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     return out, lse
 
 
+def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
+                         max_seqlen_q: int, scale: float | None = None, causal: bool = False,
+                         win_left: int = -1, win_right: int = -1, out=None, lse=None,
+                         return_lse: bool = True):
+    """Packed queries over a paged KV cache (chunked prefill) on torch tensors.
+
+    q [total_q, Hq, D]; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
+    [B, max_pages_per_seq]; seq_lens_k int32 [B] (cached keys, the new tokens' included);
+    cu_seqlens_q int32 [B + 1]; all on the device.  Returns ``(out, lse)``, lse
+    [Hq, total_q].
+    """
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [total_q, Hq, D] and the page pools [P, page, Hkv, D]")
+    total_q, Hq, D = q.shape
+    P, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError("head dimension mismatch")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share one dtype")
+    for t, n in ((block_table, "block_table"), (seq_lens_k, "seq_lens_k"), (cu_seqlens_q, "cu_seqlens_q")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    B = block_table.shape[0]
+    if block_table.dim() != 2 or tuple(seq_lens_k.shape) != (B,) or tuple(cu_seqlens_q.shape) != (B + 1,):
+        raise ValueError("block_table must be [B, max_pages], seq_lens_k [B], cu_seqlens_q [B + 1]")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)):
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must match q")
+    _check(lib().mfa_fwd_varlen_paged(
+        _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(block_table, "block_table"), _dev(seq_lens_k, "seq_lens_k"),
+        _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, total_q, int(max_seqlen_q), D,
+        page_size, P, block_table.shape[1], float(scale), int(bool(causal)), int(win_left),
+        int(win_right), dt, _stream(q)), "mfa_fwd_varlen_paged")
+    return out, lse
+
+
 def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
                      num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
                      workspace=None):
@@ -312,6 +361,6 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
 
 
 __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
-           "mfa_fwd_varlen",
+           "mfa_fwd_varlen", "mfa_fwd_varlen_paged",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
            "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version"]

@@ -79,7 +79,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* out, float* ls
                        win_right, dtype);
     if (st) return st;
     MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, Nq, Nk, D, scale,
-                    causal, win_left, win_right, dtype, nullptr, nullptr, 0, 0};
+                    causal, win_left, win_right, dtype, nullptr, nullptr, 0, 0,
+                    nullptr, nullptr, 0, 0};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 1;
@@ -129,12 +130,54 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
                           max_k, D, scale, causal, win_left, win_right, dtype);
     if (st) return st;
     MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, max_q, max_k, D, scale,
-                    causal, win_left, win_right, dtype, cu_q, cu_k, total_q, total_k};
+                    causal, win_left, win_right, dtype, cu_q, cu_k, total_q, total_k,
+                    nullptr, nullptr, 0, 0};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 3;
     info.n_launches = 1;
     info.planned = -1;   // the sequence lengths are on the device
+    st = mfa_fwd_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
+int varlen_paged_common(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens_k,
+                        const int32_t* cu_q, void* out, float* lse, int B, int Hq, int Hkv,
+                        int total_q, int max_q, int D, int page_size, int num_pages,
+                        int max_pages, float scale, int causal, int win_left, int win_right,
+                        int dtype, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens_k || !cu_q || !out)
+        return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || max_q < 1) return MFA_ERR_SHAPE;
+    if (causal != 0 && causal != 1) return MFA_ERR_ARG;
+    if (Hq % Hkv != 0) return MFA_ERR_GQA;
+    if (win_left < -1 || win_right < -1) return MFA_ERR_WINDOW;
+    if (!isfinite(scale)) return MFA_ERR_SCALE;
+    if (page_size != 16 || num_pages < 1 || max_pages < 1) return MFA_ERR_PAGED;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out) ||
+        ((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens_k & 3u) || ((uintptr_t)cu_q & 3u) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MFA_ERR_ALIGN;
+    const int64_t nqt = ((int64_t)max_q + mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (nqt * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
+    if ((double)total_q * Hq * D > 4e18 || (double)num_pages * page_size * Hkv * D > 4e18)
+        return MFA_ERR_OVERFLOW;
+    if (((int64_t)max_q + mfa_fwd_bm()) * Hq * D * 2 > 0x7fffffffLL) return MFA_ERR_OVERFLOW;
+    if ((int64_t)max_pages * page_size > 0x3fffffffLL) return MFA_ERR_OVERFLOW;
+    MfaFwdProblem p{q, k_pages, v_pages, out, lse, nullptr, B, Hq, Hkv, max_q,
+                    max_pages * page_size, D, scale, causal, win_left, win_right, dtype,
+                    cu_q, nullptr, total_q, 0, block_table, seq_lens_k, num_pages, max_pages};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = 4;
+    info.n_launches = 1;
+    info.planned = -1;
     st = mfa_fwd_launch(p, (hipStream_t)stream, &info);
     if (st) return st;
     g_last = info;
@@ -218,6 +261,18 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
     return varlen_common(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
                          total_k, max_seqlen_q, max_seqlen_k, D, scale, causal, win_left,
                          win_right, dtype, stream, tile_log);
+}
+
+int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens_k,
+                         const int32_t* cu_seqlens_q, void* out, float* lse, int B, int Hq,
+                         int Hkv, int total_q, int max_seqlen_q, int D, int page_size,
+                         int num_pages, int max_pages_per_seq, float scale, int causal,
+                         int win_left, int win_right, int dtype, void* stream) {
+    return varlen_paged_common(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q, out,
+                               lse, B, Hq, Hkv, total_q, max_seqlen_q, D, page_size, num_pages,
+                               max_pages_per_seq, scale, causal, win_left, win_right, dtype,
+                               stream);
 }
 
 int mfa_decode_num_splits(int page_size, int max_pages_per_seq, int num_splits) {

@@ -116,6 +116,12 @@ __device__ __forceinline__ mfa_u32x2 mfa_load8(__amdgpu_buffer_rsrc_t r, uint32_
 }
 __device__ __forceinline__ float mfa_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Wave-uniform read of an int32 the kernel never writes, through the scalar data cache
+// (a scalar load, counted by lgkmcnt rather than vmcnt).  p must be uniform.
+__device__ __forceinline__ int32_t mfa_uniform_load(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Value of x held by lane (lane ^ 32).
 __device__ __forceinline__ float mfa_swap_halves(float x) {
     return __shfl_xor(x, 32, 64);

@@ -83,6 +83,11 @@ struct FwdArgs {
     const int32_t* cu_k;
     int total_q, total_k;
     int causal, left, right;
+    // keys in a paged cache ([num_pages, 16, Hkv, D] pools, block_table [B, max_pages],
+    // seq_lens_k [B]) for packed queries
+    const int32_t* block_table;
+    const int32_t* seq_lens_k;
+    int max_pages, num_pages;
 };
 
 template <int N>
@@ -142,20 +147,25 @@ __device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p)
 // offsets hold.  Uniform over the workgroup (scalar loads of a uniform index).
 __device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int total, int max_len,
                                            int* start, int* len) {
-    int s0 = __builtin_amdgcn_readfirstlane(cu[s]);
-    int s1 = __builtin_amdgcn_readfirstlane(cu[s + 1]);
+    int s0 = mfa_uniform_load(cu + s);
+    int s1 = mfa_uniform_load(cu + s + 1);
     s0 = s0 < 0 ? 0 : (s0 > total ? total : s0);
     s1 = s1 < s0 ? s0 : (s1 > total ? total : s1);
     *start = s0;
     *len = (s1 - s0) > max_len ? max_len : (s1 - s0);
 }
 
-// VAR: packed variable-length sequences.  Q, O are [total_q, Hq, D] and K, V
-// [total_k, Hkv, D] (rows of one head are Hq * D / Hkv * D elements apart), sequence b
-// spans cu_q[b] .. cu_q[b+1] - 1 and cu_k[b] .. cu_k[b+1] - 1, and its mask is aligned
-// bottom-right on its own lengths.  LSE is [Hq, total_q].
-template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, bool VAR>
+// MODE 0: dense [B, H, N, D] tensors.
+// MODE 1: packed variable-length sequences.  Q, O are [total_q, Hq, D] and K, V
+//   [total_k, Hkv, D] (rows of one head are Hq * D / Hkv * D elements apart), sequence b
+//   spans cu_q[b] .. cu_q[b+1] - 1 and cu_k[b] .. cu_k[b+1] - 1, and its mask is aligned
+//   bottom-right on its own lengths.  LSE is [Hq, total_q].
+// MODE 2: packed queries as in MODE 1; sequence b's seq_lens_k[b] keys sit in a paged
+//   cache, token t in page block_table[b, t / 16], slot t % 16.
+template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, int MODE>
 __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
+    constexpr bool VAR = MODE != 0;
+    constexpr bool PAGED = MODE == 2;
     using T = Tile<D>;
     constexpr int BN = kBN;
     constexpr int NKB = D / 16;   // k-steps of S^T = K Q^T
@@ -201,7 +211,13 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     MfaMask mask = a.mask;
     if constexpr (VAR) {
         seq_bounds(a.cu_q, b, a.total_q, a.Nq, &qs, &Nq);
-        seq_bounds(a.cu_k, b, a.total_k, a.Nk, &ks, &Nk);
+        if constexpr (PAGED) {
+            // cached tokens, clamped to the block table's capacity
+            const int L = mfa_uniform_load(a.seq_lens_k + b);
+            Nk = L < 0 ? 0 : (L > a.Nk ? a.Nk : L);
+        } else {
+            seq_bounds(a.cu_k, b, a.total_k, a.Nk, &ks, &Nk);
+        }
         mask = mfa_make_mask(Nq, Nk, a.causal, a.left, a.right);
         if (q0 >= Nq) {   // past the end of this sequence's queries (uniform)
             if (TILELOG && tid == 0) {
@@ -228,7 +244,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int n = grp == 0 ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
 
     const size_t q_base = VAR ? ((size_t)qs * a.Hq + h) * D : (size_t)(b * a.Hq + h) * (size_t)a.Nq * D;
-    const size_t kv_base = VAR ? ((size_t)ks * a.Hkv + kvh) * D : (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk * D;
+    // (paged: the head's slice of the pool's page 0; pages are 16 * SK elements apart)
+    const size_t kv_base = PAGED ? (size_t)kvh * D
+                           : VAR ? ((size_t)ks * a.Hkv + kvh) * D
+                                 : (size_t)(b * a.Hkv + kvh) * (size_t)a.Nk * D;
     const uint16_t* kg = a.k + kv_base;
     const uint16_t* vg = a.v + kv_base;
 
@@ -279,30 +298,93 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // thread is at a fixed offset from the tile start, kept in a vector register of its
     // own (the range check applies to it).  Packed rows are SK apart, so there the range
     // ends with the last row's D elements.
+    //
+    // Paged keys: a key tile is BN / 16 pages, and the rows of copy i of this wave all lie in
+    // page ((4 * i + wave) * RPB) / 16 of the tile, at row (row & 15) of that page; the copy
+    // gets a range over the page's valid rows of this head (empty for an unused or invalid
+    // page).  The page ids of the tiles a stage copies are read one stage ahead.
+    constexpr int PAGE = 16;
+    struct PagedTile {
+        int kt;
+        bool need;
+    };
     auto tile_rsrc = [&](const uint16_t* src, int kt, bool need) {
-        const int k0 = need ? kt * BN : 0;
-        const int rows = need ? max(Nk - k0, 0) : 0;
-        const int bytes = VAR ? (rows > 0 ? ((rows - 1) * SK + D) * 2 : 0) : rows * D * 2;
-        return mfa_rsrc(src + (size_t)k0 * SK, (uint32_t)bytes);
+        if constexpr (PAGED) {
+            return PagedTile{kt, need};
+        } else {
+            const int k0 = need ? kt * BN : 0;
+            const int rows = need ? max(Nk - k0, 0) : 0;
+            const int bytes = VAR ? (rows > 0 ? ((rows - 1) * SK + D) * 2 : 0) : rows * D * 2;
+            return mfa_rsrc(src + (size_t)k0 * SK, (uint32_t)bytes);
+        }
     };
     const uint32_t copy_step = (uint32_t)(4 * RPB * SK * 2);
-    auto copy_k = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
-        constexpr int buf = decltype(buf_c)::value;
-        mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * copy_step);
+    uint32_t kpg_off = 0, vpg_off = 0;
+    if constexpr (PAGED) {
+        const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
+        kpg_off = (uint32_t)((row & (PAGE - 1)) * SK + T::k_phys(row, phys) * 8) * 2;
+        vpg_off = (uint32_t)((row & (PAGE - 1)) * SK + T::v_phys(row, phys) * 8) * 2;
+    }
+    const int32_t* bt_row = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+    auto page_slot = [&](int kt, int i) { return kt * (BN / PAGE) + ((4 * i + wave) * RPB) / PAGE; };
+    auto load_ids = [&](int kt, bool need, int(&ids)[T::LOADS]) {
+#pragma unroll
+        for (int i = 0; i < T::LOADS; ++i) {
+            const int slot = page_slot(kt, i);
+            ids[i] = (need && slot * PAGE < Nk) ? mfa_uniform_load(bt_row + slot) : -1;
+        }
     };
-    auto copy_v = [&](__amdgpu_buffer_rsrc_t r, auto buf_c, int i) {
+    auto page_rsrc = [&](const uint16_t* pool, int kt, int i, int pid) {
+        const int slot = page_slot(kt, i);
+        const int rows = min(Nk - slot * PAGE, PAGE);
+        const bool ok = pid >= 0 && pid < a.num_pages && rows > 0;
+        return mfa_rsrc(pool + (ok ? (size_t)pid * (PAGE * SK) : 0),
+                        ok ? (uint32_t)(((rows - 1) * SK + D) * 2) : 0u);
+    };
+    int kpid[T::LOADS], vpid[T::LOADS];   // ids of the tiles the current stage copies
+    auto copy_k = [&](const auto& r, auto buf_c, int i) {
         constexpr int buf = decltype(buf_c)::value;
-        mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * copy_step);
+        if constexpr (PAGED)
+            mfa_load16_lds(page_rsrc(kg, r.kt, i, r.need ? kpid[i] : -1),
+                           smem + buf * T::ELEMS + (4 * i + wave) * 512, kpg_off);
+        else
+            mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * copy_step);
+    };
+    auto copy_v = [&](const auto& r, auto buf_c, int i) {
+        constexpr int buf = decltype(buf_c)::value;
+        if constexpr (PAGED)
+            mfa_load16_lds(page_rsrc(vg, r.kt, i, r.need ? vpid[i] : -1),
+                           smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vpg_off);
+        else
+            mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * copy_step);
     };
     auto issue_k = [&](int kt, auto buf_c) {
-        const auto r = tile_rsrc(kg, kt, true);
+        if constexpr (PAGED) {
+            int ids[T::LOADS];
+            load_ids(kt, true, ids);
 #pragma unroll
-        for (int i = 0; i < T::LOADS; ++i) copy_k(r, buf_c, i);
+            for (int i = 0; i < T::LOADS; ++i)
+                mfa_load16_lds(page_rsrc(kg, kt, i, ids[i]), smem + decltype(buf_c)::value * T::ELEMS + (4 * i + wave) * 512,
+                               kpg_off);
+        } else {
+            const auto r = tile_rsrc(kg, kt, true);
+#pragma unroll
+            for (int i = 0; i < T::LOADS; ++i) copy_k(r, buf_c, i);
+        }
     };
     auto issue_v = [&](int kt, auto buf_c) {
-        const auto r = tile_rsrc(vg, kt, true);
+        if constexpr (PAGED) {
+            int ids[T::LOADS];
+            load_ids(kt, true, ids);
 #pragma unroll
-        for (int i = 0; i < T::LOADS; ++i) copy_v(r, buf_c, i);
+            for (int i = 0; i < T::LOADS; ++i)
+                mfa_load16_lds(page_rsrc(vg, kt, i, ids[i]),
+                               smem + (2 + decltype(buf_c)::value) * T::ELEMS + (4 * i + wave) * 512, vpg_off);
+        } else {
+            const auto r = tile_rsrc(vg, kt, true);
+#pragma unroll
+            for (int i = 0; i < T::LOADS; ++i) copy_v(r, buf_c, i);
+        }
     };
 
     // ---- per-lane LDS operand addresses (elements; buffer and block offsets are
@@ -382,6 +464,11 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         // start would queue every wave behind the CU's address path)
         const auto rk = tile_rsrc(kg, kt + 2, j + 2 < n);
         const auto rv = tile_rsrc(vg, kt + 1, j + 1 < n);
+        int kpid_n[T::LOADS], vpid_n[T::LOADS];   // (paged) ids for the next stage's copies
+        if constexpr (PAGED) {
+            load_ids(kt + 3, j + 3 < n, kpid_n);
+            load_ids(kt + 2, j + 2 < n, vpid_n);
+        }
 
         if (!mfa_tile_full(mask, kBM, BN, qt, kt)) {
             const int k0 = kt * BN;
@@ -468,6 +555,13 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
 
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's direct loads landed
         block_barrier();
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int i = 0; i < T::LOADS; ++i) {
+                kpid[i] = kpid_n[i];
+                vpid[i] = vpid_n[i];
+            }
+        }
     };
 
     // Barriers are workgroup-wide, so both groups run n0 stages; a group with fewer
@@ -478,6 +572,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             issue_k(kt_lo, MfaInt<0>{});
             issue_v(kt_lo, MfaInt<0>{});
             if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
+            if constexpr (PAGED) {
+                load_ids(kt_lo + 2, 2 < n, kpid);
+                load_ids(kt_lo + 1, 1 < n, vpid);
+            }
             __builtin_amdgcn_s_waitcnt(0x0f70);
         }
         block_barrier();
@@ -560,28 +658,29 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
 }
 
-template <int D, int DT, int G, bool TL, bool VAR>
+template <int D, int DT, int G, bool TL, int MODE>
 void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
     const dim3 block(G * kGroupThreads);
     if (neg)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true, VAR>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true, MODE>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false, VAR>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false, MODE>), grid, block, 0, stream, a);
 }
 
-template <int D, int DT, bool VAR>
+template <int D, int DT, int MODE>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
     const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
     if (groups == 2) {
-        if (tilelog) launch_sign<D, DT, 2, true, VAR>(a, grid, stream, neg);
-        else launch_sign<D, DT, 2, false, VAR>(a, grid, stream, neg);
+        if (tilelog) launch_sign<D, DT, 2, true, MODE>(a, grid, stream, neg);
+        else launch_sign<D, DT, 2, false, MODE>(a, grid, stream, neg);
     } else {
-        if (tilelog) launch_sign<D, DT, 1, true, VAR>(a, grid, stream, neg);
-        else launch_sign<D, DT, 1, false, VAR>(a, grid, stream, neg);
+        if (tilelog) launch_sign<D, DT, 1, true, MODE>(a, grid, stream, neg);
+        else launch_sign<D, DT, 1, false, MODE>(a, grid, stream, neg);
     }
     snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups, VAR ? ",varlen" : "",
+             DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
+             MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
              tilelog ? ",tilelog" : "", neg ? ",neg" : "");
     info->BM = kBM;
     info->BN = kBN;
@@ -591,6 +690,18 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
     info->grid[2] = 1;
     info->block = groups * kGroupThreads;
     return hipGetLastError() == hipSuccess ? MFA_OK : MFA_ERR_HIP;
+}
+
+
+
+template <int MODE>
+int launch_dt(const MfaFwdProblem& pr, const FwdArgs& a, hipStream_t stream, int groups, bool tl,
+              bool neg, mfa_dispatch_info* info) {
+    if (pr.D == 128)
+        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, MODE>(a, stream, groups, tl, neg, info)
+                                   : launch<128, MFA_DT_BF16, MODE>(a, stream, groups, tl, neg, info);
+    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, MODE>(a, stream, groups, tl, neg, info)
+                               : launch<64, MFA_DT_BF16, MODE>(a, stream, groups, tl, neg, info);
 }
 
 }  // namespace
@@ -631,7 +742,12 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.causal = pr.causal;
     a.left = pr.left;
     a.right = pr.right;
+    a.block_table = pr.block_table;
+    a.seq_lens_k = pr.seq_lens_k;
+    a.max_pages = pr.max_pages;
+    a.num_pages = pr.num_pages;
     const bool var = pr.cu_seqlens_q != nullptr;
+    const int mode = pr.block_table != nullptr ? 2 : var ? 1 : 0;
     // |scale| * log2(e), kept >= 1e-30 so that a masked (-inf) score times it stays
     // -inf; for scale = 0 the visible scores then all scale to ~0, i.e. the same
     // uniform weights up to fp32 rounding
@@ -644,16 +760,7 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     long long q_tiles = (long long)a.n_q_tiles * pr.B;
     if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
     const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
-    if (var) {
-        if (pr.D == 128)
-            return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, true>(a, stream, groups, tl, neg, info)
-                                       : launch<128, MFA_DT_BF16, true>(a, stream, groups, tl, neg, info);
-        return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, true>(a, stream, groups, tl, neg, info)
-                                   : launch<64, MFA_DT_BF16, true>(a, stream, groups, tl, neg, info);
-    }
-    if (pr.D == 128)
-        return pr.dtype == MFA_F16 ? launch<128, MFA_DT_F16, false>(a, stream, groups, tl, neg, info)
-                                   : launch<128, MFA_DT_BF16, false>(a, stream, groups, tl, neg, info);
-    return pr.dtype == MFA_F16 ? launch<64, MFA_DT_F16, false>(a, stream, groups, tl, neg, info)
-                               : launch<64, MFA_DT_BF16, false>(a, stream, groups, tl, neg, info);
+    if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
+    if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);
+    return launch_dt<0>(pr, a, stream, groups, tl, neg, info);
 }

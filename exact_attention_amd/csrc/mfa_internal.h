@@ -22,6 +22,11 @@ struct MfaFwdProblem {
     const int32_t* cu_seqlens_q;
     const int32_t* cu_seqlens_k;
     int total_q, total_k;
+    // keys in a paged cache (with packed queries; NULL otherwise): Nk then holds the
+    // block table's capacity max_pages * 16
+    const int32_t* block_table;
+    const int32_t* seq_lens_k;
+    int num_pages, max_pages;
 };
 
 struct MfaDecodeProblem {

@@ -14,6 +14,8 @@
  *   mfa_fwd_varlen    the same forward over packed sequences of different lengths
  *                     delimited by cu_seqlens (mlx-mfa "Variable-length"), each
  *                     sequence masked on its own lengths.
+ *   mfa_fwd_varlen_paged  packed queries whose keys sit in a paged KV cache (chunked
+ *                     prefill; mlx-mfa "Paged + packed varlen queries").
  *   mfa_decode_paged  single-query decode over a paged KV cache, split across
  *                     workgroups along the keys, with partial (O, LSE) pairs merged in
  *                     a second pass.  Defined by the mlx-mfa 2.5.2 page ("Flash Decode
@@ -156,6 +158,37 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
                            int causal, int win_left, int win_right, int dtype, void* stream,
                            int32_t* tile_log);
 
+/* Packed queries over a paged KV cache: chunked prefill and speculative or
+ * multi-token verification (mlx-mfa 2.5.2 capability table, "Paged + packed varlen
+ * queries"; the paged-cache addressing of mfa_decode_paged).  Sequence b has
+ * Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] new query tokens and Lk_b = seq_lens_k[b]
+ * cached keys, which include the new tokens' own keys (appended before the call); the
+ * visibility rule applies with Nq = Lq_b, Nk = Lk_b, off = Lk_b - Lq_b, so the queries
+ * are the last Lq_b positions of the sequence.
+ *   q            [total_q, Hq, D]                    dtype (token-major, as mfa_fwd_varlen)
+ *   k_pages      [num_pages, page_size, Hkv, D]      dtype
+ *   v_pages      [num_pages, page_size, Hkv, D]      dtype
+ *   block_table  [B, max_pages_per_seq] int32 (device): token t of sequence b lives in
+ *                page block_table[b, t / page_size], slot t % page_size
+ *   seq_lens_k   [B] int32 (device)
+ *   cu_seqlens_q [B + 1] int32 (device)
+ *   out          [total_q, Hq, D] dtype;  lse [Hq, total_q] float32 or NULL
+ *   page_size must be 16.
+ * Device-side contract: cu_seqlens_q as for mfa_fwd_varlen (Lq_b <= max_seqlen_q);
+ * 0 <= seq_lens_k[b] <= max_pages_per_seq * page_size; the first
+ * ceil(seq_lens_k[b] / page_size) entries of row b of block_table are valid page
+ * indices.  Out of contract the kernel stays in bounds (offsets and lengths are clamped,
+ * pages outside [0, num_pages) read as zeros) but the result is unspecified.  Slots
+ * past seq_lens_k[b] are never used, whatever they hold.
+ * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE, _GQA, _WINDOW, _SCALE, _PAGED, _ALIGN,
+ * _ARG, _OVERFLOW, _HIP. */
+int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens_k,
+                         const int32_t* cu_seqlens_q, void* out, float* lse,
+                         int B, int Hq, int Hkv, int total_q, int max_seqlen_q, int D,
+                         int page_size, int num_pages, int max_pages_per_seq, float scale,
+                         int causal, int win_left, int win_right, int dtype, void* stream);
+
 /* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).
  * Returns 0 if the arguments are invalid. */
 size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
@@ -198,13 +231,14 @@ int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
  * record: backend, operation, selection and split fields). */
 typedef struct {
     char kernel[96];      /* kernel name of the main launch */
-    int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward */
+    int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward,
+                             4 = packed queries over a paged cache */
     int BM, BN, waves;    /* forward tile configuration */
     int grid[3];          /* main launch grid */
     int block;            /* threads per workgroup */
     int num_splits;       /* decode: key splits (grid.x of the split kernel) */
     int chunk_tokens;     /* decode: logical tokens per split */
-    long long planned;    /* forward: key tiles visited over all (b, h); varlen: -1;
+    long long planned;    /* forward: key tiles visited over all (b, h); varlen, paged: -1;
                              decode: 0 */
     int n_launches;       /* kernels enqueued by the call */
 } mfa_dispatch_info;
