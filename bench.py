@@ -210,7 +210,8 @@ def setup_chunked():
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
 
     def step():
-        ea.mfa_fwd_varlen_paged(q, kp, vp, bt, sl, cq, int(lq.max()), scale=c["scale"],
+        ea.mfa_fwd_varlen_paged(q, kp, vp, bt, sl, cq, int(lq.max()), int(p.seq_lens_k.max()),
+                                scale=c["scale"],
                                 causal=c["causal"], win_left=c["left"], win_right=c["right"],
                                 out=out, lse=lse)
 

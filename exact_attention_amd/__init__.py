@@ -62,7 +62,7 @@ _SIGS = {
     "mfa_fwd_varlen_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
                                     _I, _F, _I, _I, _I, _I, _VP, _VP]),
     "mfa_fwd_varlen_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
-                                  _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
+                                  _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "mfa_decode_num_splits": (_I, [_I, _I, _I]),
     "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -269,15 +269,16 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
 
 
 def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
-                         max_seqlen_q: int, scale: float | None = None, causal: bool = False,
+                         max_seqlen_q: int, max_seqlen_k: int, scale: float | None = None,
+                         causal: bool = False,
                          win_left: int = -1, win_right: int = -1, out=None, lse=None,
                          return_lse: bool = True):
     """Packed queries over a paged KV cache (chunked prefill) on torch tensors.
 
     q [total_q, Hq, D]; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
     [B, max_pages_per_seq]; seq_lens_k int32 [B] (cached keys, the new tokens' included);
-    cu_seqlens_q int32 [B + 1]; all on the device.  Returns ``(out, lse)``, lse
-    [Hq, total_q].
+    cu_seqlens_q int32 [B + 1]; all on the device; max_seqlen_q / max_seqlen_k host bounds
+    of every sequence's query and key counts.  Returns ``(out, lse)``, lse [Hq, total_q].
     """
     torch = _torch()
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
@@ -309,7 +310,8 @@ def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlen
         _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
         _dev(block_table, "block_table"), _dev(seq_lens_k, "seq_lens_k"),
         _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(out, "out"),
-        _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, total_q, int(max_seqlen_q), D,
+        _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, total_q, int(max_seqlen_q),
+        int(max_seqlen_k), D,
         page_size, P, block_table.shape[1], float(scale), int(bool(causal)), int(win_left),
         int(win_right), dt, _stream(q)), "mfa_fwd_varlen_paged")
     return out, lse

@@ -3,6 +3,8 @@
 // returns a negative status and touches no memory (the "reject malformed input, never
 // fall back silently" contract of the MXFlashAttn 1.5.0 and mlx-mfa pages).
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "mfa_geometry.h"
@@ -111,8 +113,8 @@ int check_varlen(const void* q, const void* k, const void* v, void* out, const f
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         ((uintptr_t)cu_q & 3u) || ((uintptr_t)cu_k & 3u) || (lse && ((uintptr_t)lse & 3u)))
         return MFA_ERR_ALIGN;
-    const int64_t nqt = ((int64_t)max_q + mfa_fwd_bm() - 1) / mfa_fwd_bm();
-    if (nqt * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
+    const int64_t rounds = (std::max(max_q, max_k) + (int64_t)mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (rounds * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
     if ((double)total_q * Hq * D > 4e18 || (double)total_k * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
     // one sequence's rows (plus a tile's worth past its end) are addressed with 32-bit
     // byte offsets
@@ -147,14 +149,14 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
 int varlen_paged_common(const void* q, const void* k_pages, const void* v_pages,
                         const int32_t* block_table, const int32_t* seq_lens_k,
                         const int32_t* cu_q, void* out, float* lse, int B, int Hq, int Hkv,
-                        int total_q, int max_q, int D, int page_size, int num_pages,
+                        int total_q, int max_q, int max_k, int D, int page_size, int num_pages,
                         int max_pages, float scale, int causal, int win_left, int win_right,
                         int dtype, void* stream) {
     if (!q || !k_pages || !v_pages || !block_table || !seq_lens_k || !cu_q || !out)
         return MFA_ERR_NULL;
     int st = check_common(dtype, D);
     if (st) return st;
-    if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || max_q < 1) return MFA_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || max_q < 1 || max_k < 1) return MFA_ERR_SHAPE;
     if (causal != 0 && causal != 1) return MFA_ERR_ARG;
     if (Hq % Hkv != 0) return MFA_ERR_GQA;
     if (win_left < -1 || win_right < -1) return MFA_ERR_WINDOW;
@@ -164,14 +166,16 @@ int varlen_paged_common(const void* q, const void* k_pages, const void* v_pages,
         ((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens_k & 3u) || ((uintptr_t)cu_q & 3u) ||
         (lse && ((uintptr_t)lse & 3u)))
         return MFA_ERR_ALIGN;
-    const int64_t nqt = ((int64_t)max_q + mfa_fwd_bm() - 1) / mfa_fwd_bm();
-    if (nqt * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
+    const int64_t rounds = (std::max(max_q, max_k) + (int64_t)mfa_fwd_bm() - 1) / mfa_fwd_bm();
+    if (rounds * (int64_t)B * (int64_t)Hq > kMaxGrid) return MFA_ERR_OVERFLOW;
     if ((double)total_q * Hq * D > 4e18 || (double)num_pages * page_size * Hkv * D > 4e18)
         return MFA_ERR_OVERFLOW;
     if (((int64_t)max_q + mfa_fwd_bm()) * Hq * D * 2 > 0x7fffffffLL) return MFA_ERR_OVERFLOW;
     if ((int64_t)max_pages * page_size > 0x3fffffffLL) return MFA_ERR_OVERFLOW;
+    // keys per sequence: at most max_seqlen_k and the block table's capacity
+    const int key_cap = std::min(max_k, max_pages * page_size);
     MfaFwdProblem p{q, k_pages, v_pages, out, lse, nullptr, B, Hq, Hkv, max_q,
-                    max_pages * page_size, D, scale, causal, win_left, win_right, dtype,
+                    key_cap, D, scale, causal, win_left, win_right, dtype,
                     cu_q, nullptr, total_q, 0, block_table, seq_lens_k, num_pages, max_pages};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
@@ -266,11 +270,12 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
 int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages,
                          const int32_t* block_table, const int32_t* seq_lens_k,
                          const int32_t* cu_seqlens_q, void* out, float* lse, int B, int Hq,
-                         int Hkv, int total_q, int max_seqlen_q, int D, int page_size,
-                         int num_pages, int max_pages_per_seq, float scale, int causal,
-                         int win_left, int win_right, int dtype, void* stream) {
+                         int Hkv, int total_q, int max_seqlen_q, int max_seqlen_k, int D,
+                         int page_size, int num_pages, int max_pages_per_seq, float scale,
+                         int causal, int win_left, int win_right, int dtype, void* stream) {
     return varlen_paged_common(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q, out,
-                               lse, B, Hq, Hkv, total_q, max_seqlen_q, D, page_size, num_pages,
+                               lse, B, Hq, Hkv, total_q, max_seqlen_q, max_seqlen_k, D,
+                               page_size, num_pages,
                                max_pages_per_seq, scale, causal, win_left, win_right, dtype,
                                stream);
 }

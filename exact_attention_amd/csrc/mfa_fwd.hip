@@ -54,6 +54,8 @@
 // mfa_tile_full rejects (the invisible scores become -inf, so exp2 gives P = 0); a
 // row whose offset is still -inf uses 0 in its place so exp never sees
 // (-inf) - (-inf).
+#include <algorithm>
+
 #include "mfa_device.h"
 #include "mfa_geometry.h"
 #include "mfa_internal.h"
@@ -73,7 +75,8 @@ struct FwdArgs {
     float* lse;
     int32_t* tile_log;
     int B, Hq, Hkv, Nq, Nk, g;   // packed sequences: Nq, Nk = max_seqlen_q, max_seqlen_k
-    int n_q_tiles;
+    int n_q_tiles;   // query tiles per (batch, head) (of max_seqlen_q for packed sequences)
+    int n_rounds;    // grid = n_rounds * HB
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
     float scale_log2_abs;  // |scale| * log2(e)
@@ -188,8 +191,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int round = id / a.HB;
     const int w = id - round * a.HB;
     // longest query tiles first: with one workgroup per CU, dynamic dispatch then
-    // hands the short tiles to the CUs that finish early
-    const int qt = a.n_q_tiles - 1 - round;
+    // hands the short tiles to the CUs that finish early.  For packed sequences the
+    // rounds count down the end of the tile's key range in BM-key units (below), which
+    // orders the tiles of all sequences by causal work, whatever their lengths.
+    int qt = a.n_q_tiles - 1 - round;
     int b, h;
     if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
@@ -203,7 +208,6 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         h = w - b * a.Hq;
     }
     const int kvh = h / a.g;
-    const int q0 = qt * kBM;
 
     // this (batch, head)'s sequence: lengths, first tokens and mask
     int Nq = a.Nq, Nk = a.Nk;
@@ -219,17 +223,26 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             seq_bounds(a.cu_k, b, a.total_k, a.Nk, &ks, &Nk);
         }
         mask = mfa_make_mask(Nq, Nk, a.causal, a.left, a.right);
-        if (q0 >= Nq) {   // past the end of this sequence's queries (uniform)
-            if (TILELOG && tid == 0) {
-                int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
-                t[0] = -1;
-                t[1] = 0;
-                t[2] = 0;
-                t[3] = -1;
+        // tile qt of this sequence ends its causal key range near off + (qt + 1) * BM, so
+        // it runs in round n_rounds - 1 - qt - c with c = floor(off / BM) (0 if off < 0);
+        // n_rounds >= ceil(Nq / BM) + c for every sequence, so each tile has one round
+        const int n_tiles = (Nq + kBM - 1) / kBM;
+        const int c = Nk > Nq ? (Nk - Nq) / kBM : 0;
+        qt = a.n_rounds - 1 - round - c;
+        // the records of tiles past this sequence's last one are written by the workgroup
+        // of its last tile (by round 0's if it has none)
+        if (TILELOG && tid == 0 && (n_tiles > 0 ? qt == n_tiles - 1 : round == 0)) {
+            for (int t = n_tiles; t < a.n_q_tiles; ++t) {
+                int32_t* r = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + t) * 4;
+                r[0] = -1;
+                r[1] = 0;
+                r[2] = 0;
+                r[3] = -1;
             }
-            return;
         }
+        if (qt < 0 || qt >= n_tiles) return;   // no tile of this sequence here (uniform)
     }
+    const int q0 = qt * kBM;
     // row strides (elements) and the first element of this head's rows
     const int SQ = VAR ? a.Hq * D : D;
     const int SK = VAR ? a.Hkv * D : D;
@@ -670,7 +683,7 @@ void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
 template <int D, int DT, int MODE>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
-    const dim3 grid((unsigned)a.n_q_tiles * (unsigned)a.HB);
+    const dim3 grid((unsigned)a.n_rounds * (unsigned)a.HB);
     if (groups == 2) {
         if (tilelog) launch_sign<D, DT, 2, true, MODE>(a, grid, stream, neg);
         else launch_sign<D, DT, 2, false, MODE>(a, grid, stream, neg);
@@ -733,6 +746,7 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.Nk = pr.Nk;
     a.g = pr.Hq / pr.Hkv;
     a.n_q_tiles = (pr.Nq + kBM - 1) / kBM;
+    a.n_rounds = pr.cu_seqlens_q != nullptr ? std::max(a.n_q_tiles, (pr.Nk + kBM - 1) / kBM) : a.n_q_tiles;
     a.HB = pr.B * pr.Hq;
     a.xcd_group = ((pr.B * pr.Hkv) % 8 == 0) ? 1 : 0;
     a.cu_q = pr.cu_seqlens_q;

@@ -173,9 +173,10 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
  *   seq_lens_k   [B] int32 (device)
  *   cu_seqlens_q [B + 1] int32 (device)
  *   out          [total_q, Hq, D] dtype;  lse [Hq, total_q] float32 or NULL
+ *   max_seqlen_q, max_seqlen_k: host upper bounds of Lq_b and Lk_b (they size the grid)
  *   page_size must be 16.
  * Device-side contract: cu_seqlens_q as for mfa_fwd_varlen (Lq_b <= max_seqlen_q);
- * 0 <= seq_lens_k[b] <= max_pages_per_seq * page_size; the first
+ * 0 <= seq_lens_k[b] <= min(max_seqlen_k, max_pages_per_seq * page_size); the first
  * ceil(seq_lens_k[b] / page_size) entries of row b of block_table are valid page
  * indices.  Out of contract the kernel stays in bounds (offsets and lengths are clamped,
  * pages outside [0, num_pages) read as zeros) but the result is unspecified.  Slots
@@ -185,8 +186,9 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
 int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages,
                          const int32_t* block_table, const int32_t* seq_lens_k,
                          const int32_t* cu_seqlens_q, void* out, float* lse,
-                         int B, int Hq, int Hkv, int total_q, int max_seqlen_q, int D,
-                         int page_size, int num_pages, int max_pages_per_seq, float scale,
+                         int B, int Hq, int Hkv, int total_q, int max_seqlen_q,
+                         int max_seqlen_k, int D, int page_size, int num_pages,
+                         int max_pages_per_seq, float scale,
                          int causal, int win_left, int win_right, int dtype, void* stream);
 
 /* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).

@@ -153,12 +153,12 @@ def test_fwd_varlen_validation(kw, code):
 
 def fwd_paged(**kw):
     a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, cq=0x60000, out=0x70000, lse=0x80000, B=3, Hq=4,
-             Hkv=2, tq=300, mq=200, D=128, page=16, num_pages=50, max_pages=20, scale=0.1,
+             Hkv=2, tq=300, mq=200, mk=320, D=128, page=16, num_pages=50, max_pages=20, scale=0.1,
              causal=1, left=-1, right=-1, dtype=0, stream=None)
     a.update(kw)
     return ea.lib().mfa_fwd_varlen_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["cq"],
                                          a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["tq"],
-                                         a["mq"], a["D"], a["page"], a["num_pages"],
+                                         a["mq"], a["mk"], a["D"], a["page"], a["num_pages"],
                                          a["max_pages"], a["scale"], a["causal"], a["left"],
                                          a["right"], a["dtype"], a["stream"])
 
@@ -166,7 +166,7 @@ def fwd_paged(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(kp=None), -1), (dict(bt=None), -1), (dict(sl=None), -1),
     (dict(cq=None), -1), (dict(out=None), -1), (dict(dtype=7), -5), (dict(D=96), -4),
-    (dict(B=0), -2), (dict(tq=0), -2), (dict(mq=0), -2), (dict(Hq=5, Hkv=2), -3),
+    (dict(B=0), -2), (dict(tq=0), -2), (dict(mq=0), -2), (dict(mk=0), -2), (dict(Hq=5, Hkv=2), -3),
     (dict(right=-2), -6), (dict(scale=float("inf")), -7), (dict(page=32), -9),
     (dict(num_pages=0), -9), (dict(max_pages=0), -9), (dict(kp=A2 + 8), -12),
     (dict(sl=A5 + 2), -12), (dict(cq=0x60001), -12), (dict(causal=3), -13),

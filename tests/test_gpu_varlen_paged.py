@@ -30,7 +30,8 @@ def run(p, scale, causal=True, left=-1, right=-1, block_table=None, k_pages=None
           f"lq={lq.tolist()[:8]} lk={p.seq_lens_k.tolist()[:8]} causal={causal} "
           f"win=({left},{right})", flush=True)
     O, L = ea.mfa_fwd_varlen_paged(q, kp, vp, bt, dev_i32(p.seq_lens_k), dev_i32(p.cu_seqlens_q),
-                                   int(max(1, lq.max())), scale=scale, causal=causal,
+                                   int(max(1, lq.max())), int(max(1, p.seq_lens_k.max())),
+                                   scale=scale, causal=causal,
                                    win_left=left, win_right=right)
     torch.cuda.synchronize()
     return O, L
