@@ -145,6 +145,34 @@ def _scatter_pages(k_tok, v_tok, seq_lens, perm, num_pages, page_size, max_pages
     return block_table, k_pages, v_pages
 
 
+def paged_multi_inputs(B: int, Nq: int, Hq: int, Hkv: int, D: int, dtype: str, seed: int, *,
+                       len_lo: int, len_hi: int, page_size: int = 16,
+                       max_pages_per_seq: int | None = None, extra_pages: int = 0,
+                       seq_lens=None) -> PagedInputs:
+    """``paged_inputs`` with ``Nq`` query tokens per sequence: q is ``[B, Nq, Hq, D]``
+    (same draw order; the q draw has the extra token axis)."""
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        seq_lens = rng.integers(len_lo, len_hi, endpoint=True, size=B)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    pages_per_seq = [int(math.ceil(int(L) / page_size)) for L in seq_lens]
+    used = int(sum(pages_per_seq))
+    num_pages = max(1, used + int(extra_pages))
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, int(math.ceil(len_hi / page_size)))
+    if max(pages_per_seq, default=0) > max_pages_per_seq:
+        raise ValueError("max_pages_per_seq too small for the drawn sequence lengths")
+    perm = rng.permutation(num_pages).astype(np.int64)
+    q = _normal_bits(rng, (B, Nq, Hq, D), dtype)
+    total = int(seq_lens.sum())
+    k_tok = _normal_bits(rng, (total, Hkv, D), dtype)
+    v_tok = _normal_bits(rng, (total, Hkv, D), dtype)
+    block_table, k_pages, v_pages = _scatter_pages(k_tok, v_tok, seq_lens, perm, num_pages,
+                                                   page_size, max_pages_per_seq, dtype)
+    return PagedInputs(q, k_pages, v_pages, block_table, seq_lens.astype(np.int32),
+                       page_size, dtype, used)
+
+
 @dataclass
 class PagedVarlenInputs:
     q: np.ndarray             # uint16 bits [total_q, Hq, D]
@@ -260,6 +288,9 @@ CONFIGS = {
             causal=True, left=-1, right=-1, len_lo=256, len_hi=4096, seed=106),
     # chunked prefill over the paged cache (mlx-mfa "Paged + packed varlen queries"):
     # new chunks of 512..2048 tokens after 1024..16384 cached ones, pages of 16
+    # speculative verification: 4 new tokens per sequence over the decode workload's cache
+    8: dict(name="paged_multi_query_decode", B=16, Nq=4, Hq=32, Hkv=8, D=128, dtype=BF16,
+            page_size=16, len_lo=1024, len_hi=32768, seed=108),
     7: dict(name="paged_chunked_prefill", B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True,
             left=-1, right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
             ctx_hi=16384, seed=107),
@@ -274,6 +305,9 @@ def config(i: int) -> dict:
 
 def config_inputs(i: int):
     c = config(i)
+    if i == 8:
+        return paged_multi_inputs(c["B"], c["Nq"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"],
+                                  len_lo=c["len_lo"], len_hi=c["len_hi"], page_size=c["page_size"])
     if i == 7:
         return paged_varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
                                    new_lo=c["new_lo"], new_hi=c["new_hi"], ctx_lo=c["ctx_lo"],

@@ -21,6 +21,8 @@ tile by tile:
 * ``decode_paged``: single-query attention over a paged KV cache, gathered through
   the block table with its own loop (MXFlashAttn paged Split-KV decode; mlx-mfa
   "Paged KV" feature).
+* ``decode_paged_multi``: decode of up to a few new tokens per sequence (speculative
+  verification), causal among the new tokens (mlx-mfa "Flash Decode ... N_q <= 4").
 * ``lse_merge``: the combination of partial (O, LSE) pairs that a split-KV decode's
   second pass performs (mlx-mfa "Flash Decode — two-phase split-KV").
 * ``visited_tiles``: the brute-force set of key tiles holding at least one visible
@@ -32,9 +34,9 @@ forms, invariants, a pure-Python scalar implementation (``oracle.scalar``) and
 PyTorch's float64 CPU attention routine.  No function here is "parity unpinned".
 """
 from .reference import (attention, attention_probs, attention_varlen, attention_varlen_paged,
-                        decode_paged, gather_paged, lse_merge, visible, visited_tiles, widen,
-                        window_bounds)
+                        decode_paged, decode_paged_multi, gather_paged, lse_merge, visible,
+                        visited_tiles, widen, window_bounds)
 
 __all__ = ["attention", "attention_probs", "attention_varlen", "attention_varlen_paged",
-           "decode_paged", "gather_paged", "lse_merge", "visible", "visited_tiles", "widen",
-           "window_bounds"]
+           "decode_paged", "decode_paged_multi", "gather_paged", "lse_merge", "visible",
+           "visited_tiles", "widen", "window_bounds"]

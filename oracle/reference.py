@@ -284,6 +284,32 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float,
     return O, L
 
 
+def decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: float,
+                       page_size: int):
+    """Decode of ``Nq`` new tokens per sequence over a paged KV cache, float64 (mlx-mfa
+    "Flash Decode — two-phase split-KV for N_q <= 4"; MTPLX verify attention).
+
+    q ``[B, Nq, Hq, D]``; the ``seq_lens[b]`` cached tokens include the new ones, which are
+    the last ``Nq`` positions, so new token ``n`` sees the keys at positions
+    ``<= seq_lens[b] - Nq + n`` (bottom-right causal).  Returns O ``[B, Nq, Hq, D]`` and
+    LSE ``[B, Nq, Hq]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Nq, Hq, D = q.shape
+    O = np.zeros((B, Nq, Hq, D))
+    L = np.full((B, Nq, Hq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        kb = gather_paged(k_pages, block_table, b, n, page_size).transpose(1, 0, 2)[None]
+        vb = gather_paged(v_pages, block_table, b, n, page_size).transpose(1, 0, 2)[None]
+        o, lse = attention(q[b].transpose(1, 0, 2)[None], kb, vb, scale, causal=True)
+        O[b] = o[0].transpose(1, 0, 2)
+        L[b] = lse[0].T
+    return O, L
+
+
 def lse_merge(parts):
     """Combine partial results over a partition of the keys.
 

@@ -410,12 +410,34 @@ def pin_varlen_paged():
     np.testing.assert_array_equal(L3, L)
 
 
+def pin_decode_multi():
+    # Nq new tokens over the paged cache: one token equals paged decode; every sequence
+    # equals torch's float64 SDPA with the bottom-right causal bias on its gathered keys
+    torch = pytest.importorskip("torch")
+    from torch.nn.attention.bias import causal_lower_right
+    p = A.paged_multi_inputs(3, 3, 4, 2, 8, "f16", 80, len_lo=3, len_hi=60, extra_pages=2)
+    q, kp, vp = (oracle.widen(x, "f16") for x in (p.q, p.k_pages, p.v_pages))
+    O, L = oracle.decode_paged_multi(q, kp, vp, p.block_table, p.seq_lens, 0.4, 16)
+    for b in range(3):
+        n = int(p.seq_lens[b])
+        kb = oracle.gather_paged(kp, p.block_table, b, n, 16)
+        vb = oracle.gather_paged(vp, p.block_table, b, n, 16)
+        Or, Lr = _sdpa_with_lse(torch, q[b], kb, vb, 0.4, causal_lower_right(3, n)._materialize())
+        np.testing.assert_allclose(O[b], Or, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(L[b], Lr.T, atol=1e-12, rtol=0)
+    O1, L1 = oracle.decode_paged_multi(q[:, 2:], kp, vp, p.block_table, p.seq_lens, 0.4, 16)
+    Od, Ld = oracle.decode_paged(q[:, 2], kp, vp, p.block_table, p.seq_lens, 0.4, 16)
+    np.testing.assert_allclose(O1[:, 0], Od, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(L1[:, 0], Ld, atol=1e-13, rtol=0)
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
         pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
-        pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged]
+        pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged,
+        pin_decode_multi]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -530,6 +552,23 @@ def _mut_varlen_paged_context_only(q, k_pages, v_pages, block_table, seq_lens_k,
 
 _ORIG_VARLEN_PAGED = OA.attention_varlen_paged
 
+
+def _mut_decode_multi_top_left(q, k_pages, v_pages, block_table, seq_lens, scale, page_size):
+    # plausible mistake: new token n sees only the first n + 1 cached keys (top-left)
+    q = np.asarray(q, dtype=np.float64)
+    B, Nq, Hq, D = q.shape
+    O = np.zeros((B, Nq, Hq, D))
+    L = np.full((B, Nq, Hq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        kb = OA.gather_paged(k_pages, block_table, b, n, page_size).transpose(1, 0, 2)[None]
+        vb = OA.gather_paged(v_pages, block_table, b, n, page_size).transpose(1, 0, 2)[None]
+        o, lse = _ORIG_ATT(q[b].transpose(1, 0, 2)[None], kb[:, :, :Nq], vb[:, :, :Nq], scale,
+                           causal=True)
+        O[b] = o[0].transpose(1, 0, 2)
+        L[b] = lse[0].T
+    return O, L
+
 MUTATIONS = {
     "exclusive_window": ("visible", _mut_exclusive_window),
     "top_left_causal": ("visible", _mut_top_left_causal),
@@ -542,6 +581,7 @@ MUTATIONS = {
     "varlen_no_isolation": ("attention_varlen", _mut_varlen_no_isolation),
     "varlen_top_left": ("attention_varlen", _mut_varlen_top_left),
     "varlen_paged_context_only": ("attention_varlen_paged", _mut_varlen_paged_context_only),
+    "decode_multi_top_left": ("decode_paged_multi", _mut_decode_multi_top_left),
 }
 
 
