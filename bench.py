@@ -10,7 +10,8 @@ GB/s over the algorithmic bytes: every cached K/V byte once, plus q, out, LSE, t
 block-table entries used and seq_lens), and the packed variable-length causal prefill
 (``mfa_fwd_varlen``, 16 sequences of 256..4096 tokens, TFLOP/s over visible pairs), and
 chunked prefill over the paged cache (``mfa_fwd_varlen_paged``, 8 sequences, new chunks
-of 512..2048 tokens after 1024..16384 cached ones).
+of 512..2048 tokens after 1024..16384 cached ones), and the 4-token verification decode
+(``mfa_decode_paged_multi`` over the decode workload's cache shape, HBM GB/s).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
 workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
@@ -18,7 +19,7 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -239,12 +240,12 @@ def bench_chunked(step, steps):
     }
 
 
-def decode_bytes(p, Hkv, D, Hq):
+def decode_bytes(p, Hkv, D, Hq, Nq=1):
     L = p.seq_lens.astype(np.int64)
     kv = int(L.sum()) * Hkv * D * 2 * 2
     B = len(L)
-    qo = 2 * B * Hq * D * 2
-    lse = B * Hq * 4
+    qo = 2 * B * Nq * Hq * D * 2
+    lse = B * Nq * Hq * 4
     bt = 4 * int(np.ceil(L / p.page_size).sum())
     return kv + qo + lse + bt + 4 * B
 
@@ -291,6 +292,48 @@ def bench_decode(step, steps):
     }
 
 
+def setup_multi():
+    """Device inputs and one step (one mfa_decode_paged_multi call) of the 4-token decode."""
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(8)
+    p = A.config_inputs(8)
+    q = to_dev(p.q, c["dtype"])
+    kp = to_dev(p.k_pages, c["dtype"])
+    vp = to_dev(p.v_pages, c["dtype"])
+    bt = torch.from_numpy(p.block_table).to("cuda")
+    sl = torch.from_numpy(p.seq_lens).to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    nbytes = ea.mfa_decode_multi_workspace_bytes(c["B"], c["Nq"], c["Hq"], c["D"], 16, bt.shape[1], 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        ea.mfa_decode_paged_multi(q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse, workspace=ws)
+
+    step.seq_lens = p.seq_lens
+    step.page_size = p.page_size
+    return step
+
+
+def bench_multi(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(8)
+    ms, wall = time_calls(step, steps)
+    info = ea.mfa_last_dispatch()
+    nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"], c["Nq"])
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"{c['name']} B={c['B']} Nq={c['Nq']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} bf16 "
+                    f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
+        "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("decode_config8", "decode")},
+        "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
+        "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
+    }
+
+
 def cpu_baseline(budget_s=10.0):
     """The float64 oracle on this host over whole heads of the dense causal prefill."""
     import oracle
@@ -324,7 +367,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5,6,7")
+    ap.add_argument("--workloads", default="2,3,4,5,6,7,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -343,7 +386,7 @@ def main():
     wl = [int(s) for s in args.workloads.split(",") if s]
     if 2 not in wl:
         wl = [2] + wl
-    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked}
+    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi}
     steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
@@ -359,6 +402,8 @@ def main():
             res[i] = bench_varlen(steps[i], args.steps)
         elif i == 7:
             res[i] = bench_chunked(steps[i], args.steps)
+        elif i == 8:
+            res[i] = bench_multi(steps[i], args.steps)
         else:
             res[i] = bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)

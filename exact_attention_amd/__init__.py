@@ -64,6 +64,9 @@ _SIGS = {
     "mfa_fwd_varlen_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
                                   _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "mfa_decode_multi_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
+    "mfa_decode_paged_multi": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
+                                    _I, _F, _I, _VP, ctypes.c_size_t, _I, _VP]),
     "mfa_decode_num_splits": (_I, [_I, _I, _I]),
     "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
                               _I, _VP, ctypes.c_size_t, _I, _VP]),
@@ -362,7 +365,59 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
     return out, lse
 
 
+def mfa_decode_multi_workspace_bytes(B: int, Nq: int, Hq: int, D: int, page_size: int,
+                                     max_pages_per_seq: int, num_splits: int = 0) -> int:
+    return int(lib().mfa_decode_multi_workspace_bytes(B, Nq, Hq, D, page_size, max_pages_per_seq,
+                                                      num_splits))
+
+
+def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
+                           num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
+                           workspace=None):
+    """Paged split-KV decode of Nq <= 4 new tokens per sequence on torch tensors.
+
+    q [B, Nq, Hq, D]; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
+    [B, max_pages_per_seq]; seq_lens int32 [B] (the new tokens included).  Returns
+    ``(out [B, Nq, Hq, D], lse [B, Nq, Hq])``.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B, Nq, Hq, D] and the page pools [P, page, Hkv, D]")
+    B, Nq, Hq, D = q.shape
+    P, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError("head dimension mismatch")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share one dtype")
+    dt = _dtype_code(q)
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    need = mfa_decode_multi_workspace_bytes(B, Nq, Hq, D, page_size, max_pages, num_splits)
+    if need == 0:
+        raise MfaError(-2, "mfa_decode_multi_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mfa_decode_paged_multi(
+        _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None,
+        B, Nq, Hq, Hkv, D, page_size, P, max_pages, float(scale), int(num_splits),
+        _dev(workspace, "workspace"), wbytes, dt, _stream(q)), "mfa_decode_paged_multi")
+    return out, lse
+
+
 __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
-           "mfa_fwd_varlen", "mfa_fwd_varlen_paged",
+           "mfa_fwd_varlen", "mfa_fwd_varlen_paged", "mfa_decode_paged_multi",
+           "mfa_decode_multi_workspace_bytes",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
            "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version"]

@@ -195,6 +195,43 @@ int decode_splits(int max_pages, int num_splits, int* chunk_pages) {
     return (max_pages + c - 1) / c;
 }
 
+int decode_common(const void* q, const void* k_pages, const void* v_pages,
+                  const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                  int B, int Nq, int Hq, int Hkv, int D, int page_size, int num_pages,
+                  int max_pages_per_seq, float scale, int num_splits, void* workspace,
+                  size_t workspace_bytes, int dtype, void* stream, int multi) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MFA_ERR_NULL;
+    int st = check_common(dtype, D);
+    if (st) return st;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nq > 4) return MFA_ERR_SHAPE;
+    if (B > 65535 || Hq > 65535 || (int64_t)B * Nq * Hq > 0x7fffffffLL) return MFA_ERR_OVERFLOW;
+    if (Hq % Hkv != 0) return MFA_ERR_GQA;
+    if (page_size != 16 || num_pages < 1 || max_pages_per_seq < 1) return MFA_ERR_PAGED;
+    if (!isfinite(scale)) return MFA_ERR_SCALE;
+    if (num_splits < 0) return MFA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out) ||
+        ((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MFA_ERR_ALIGN;
+    if ((double)num_pages * page_size * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
+    int chunk_pages = 0;
+    const int S = decode_splits(max_pages_per_seq, num_splits, &chunk_pages);
+    const size_t need = (size_t)B * (size_t)Nq * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return MFA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MFA_ERR_ALIGN;
+    MfaDecodeProblem p{q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, D,
+                       num_pages, max_pages_per_seq, scale, S, chunk_pages, workspace, dtype,
+                       Nq, multi};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = multi ? 5 : 2;
+    st = mfa_decode_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
 }  // namespace
 
 int mfa_num_cus() {
@@ -294,40 +331,31 @@ size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_p
     return (size_t)B * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
 }
 
+size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
+                                        int max_pages_per_seq, int num_splits) {
+    if (Nq < 1 || Nq > 4) return 0;
+    const size_t one = mfa_decode_workspace_bytes(B, Hq, D, page_size, max_pages_per_seq, num_splits);
+    return one * (size_t)Nq;
+}
+
 int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                      const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
                      int B, int Hq, int Hkv, int D, int page_size, int num_pages,
                      int max_pages_per_seq, float scale, int num_splits, void* workspace,
                      size_t workspace_bytes, int dtype, void* stream) {
-    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MFA_ERR_NULL;
-    int st = check_common(dtype, D);
-    if (st) return st;
-    if (B < 1 || Hq < 1 || Hkv < 1) return MFA_ERR_SHAPE;
-    if (B > 65535 || Hq > 65535) return MFA_ERR_OVERFLOW;
-    if (Hq % Hkv != 0) return MFA_ERR_GQA;
-    if (page_size != 16 || num_pages < 1 || max_pages_per_seq < 1) return MFA_ERR_PAGED;
-    if (!isfinite(scale)) return MFA_ERR_SCALE;
-    if (num_splits < 0) return MFA_ERR_ARG;
-    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out) ||
-        ((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u) ||
-        (lse && ((uintptr_t)lse & 3u)))
-        return MFA_ERR_ALIGN;
-    if ((double)num_pages * page_size * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
-    int chunk_pages = 0;
-    const int S = decode_splits(max_pages_per_seq, num_splits, &chunk_pages);
-    const size_t need = (size_t)B * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
-    if (!workspace || workspace_bytes < need) return MFA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MFA_ERR_ALIGN;
-    MfaDecodeProblem p{q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, D,
-                       num_pages, max_pages_per_seq, scale, S, chunk_pages, workspace, dtype};
-    mfa_dispatch_info info;
-    memset(&info, 0, sizeof(info));
-    info.op = 2;
-    st = mfa_decode_launch(p, (hipStream_t)stream, &info);
-    if (st) return st;
-    g_last = info;
-    g_have_last = true;
-    return MFA_OK;
+    return decode_common(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, 1, Hq, Hkv, D,
+                         page_size, num_pages, max_pages_per_seq, scale, num_splits, workspace,
+                         workspace_bytes, dtype, stream, 0);
+}
+
+int mfa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, const int32_t* seq_lens, void* out,
+                           float* lse, int B, int Nq, int Hq, int Hkv, int D, int page_size,
+                           int num_pages, int max_pages_per_seq, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    return decode_common(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Nq, Hq, Hkv, D,
+                         page_size, num_pages, max_pages_per_seq, scale, num_splits, workspace,
+                         workspace_bytes, dtype, stream, 1);
 }
 
 int mfa_last_dispatch(mfa_dispatch_info* out) {

@@ -51,6 +51,7 @@ struct DecArgs {
     uint16_t* out;
     float* lse;
     int B, Hq, Hkv, g;
+    int nq;          // query tokens per sequence (q, out: [B, nq, Hq, D]; LSE [B, nq, Hq])
     int num_pages, max_pages;
     int S, chunk_pages;
     float scale_log2;
@@ -272,6 +273,228 @@ __global__ __launch_bounds__(kThreads, 3) void mfa_decode_split_kernel(DecArgs a
     }
 }
 
+// Multi-token decode (nq <= 4 new tokens per sequence, e.g. speculative verification):
+// the nq tokens are the last nq cached positions, and token n sees the keys at positions
+// <= L - nq + n.  One workgroup per (split, group of HPW query heads, sequence) as in the
+// single-token kernel, but both products run on the matrix cores, with the HPW * nq
+// <= 16 query rows of one KV head packed into the 16 columns of a 16x16x32 MFMA:
+//   S^T = K Q^T: A = 16 token rows of a page read straight from HBM (lane % 16 = token,
+//     lane / 16 = 16-byte chunk of each 64-byte quarter), B = column c = query row
+//     (token c / HPW, head c % HPW).  Lane (G = lane / 16, c) then holds the scores of
+//     tokens 4G .. 4G+3 of the page for row c.
+//   O^T += V^T P^T over the 32 tokens of two pages, with the k index ordered so that
+//     k-group G is {tokens 4G .. 4G+3 of page 0, tokens 4G .. 4G+3 of page 1}: the B
+//     operand P^T is then exactly the lane's own 8 exponentials, and the A operand V^T
+//     (16 columns x those 8 tokens per lane group) comes from two transposing LDS reads
+//     of the wave's own copy of the two pages (direct global -> LDS loads, XOR-swizzled
+//     16-byte chunks; no other wave touches it, so no barrier is needed).
+// A row's max is shared by its four lanes (two exchanges); each lane keeps its own part
+// of the row sum.  The four waves' partial states are merged in LDS at the end.
+template <int D>
+__device__ __forceinline__ int dec_v_phys(int row, int ch) {
+    // the 4 rows a transposing read touches land on distinct 16-byte chunks
+    return (D == 128) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
+}
+
+template <int D, int DT, int HPW>
+__global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArgs a) {
+    constexpr int NKB = D / 32;                  // k-steps of S^T
+    constexpr int NDB = D / 16;                  // 16-column blocks of O^T
+    constexpr int KCH = D / 8;                   // 16-byte chunks per token row
+    constexpr int VLOADS = kPage * KCH / 64;     // direct loads per page (4 or 2)
+    constexpr int TILE = kPG * kPage * D;        // 16-bit elements of a wave's V copy
+    static_assert(kPG == 2, "two pages per step");
+    __shared__ __attribute__((aligned(1024))) uint16_t sv_all[kWaves * TILE];
+    __shared__ float sm_m[kWaves][16];
+    __shared__ float sm_l[kWaves][16];
+
+    const int s = blockIdx.x;
+    const int hg = blockIdx.y;
+    const int b = blockIdx.z;
+    const int h0 = hg * HPW;
+    const int kvh = h0 / a.g;
+    const int nq = a.nq;
+
+    const int L = clamp_len(mfa_uniform_load(a.seq_lens + b), a.max_pages);
+    const int n_pages_b = (L + kPage - 1) / kPage;
+    const int page_begin = s * a.chunk_pages;
+    if (page_begin >= n_pages_b) return;   // empty split: its slots are neither written nor read
+    const int page_end = min(page_begin + a.chunk_pages, n_pages_b);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4;
+    const int c = lane & 15;
+    const int ppw = a.chunk_pages / kWaves;
+    const int w_begin = page_begin + wave * ppw;
+    const int w_end = min(w_begin + ppw, page_end);
+    uint16_t* sv = sv_all + wave * TILE;
+
+    // column c of the score tile: query token n_c, head h0 + c % HPW (c >= HPW * nq: unused)
+    const bool col_ok = c < HPW * nq;
+    const int n_c = c / HPW;
+    const int lim = L - nq + n_c;   // last visible key position of row c
+    mfa_u32x4 qb[NKB];
+    {
+        const uint16_t* qp = a.q + (((size_t)b * nq + (col_ok ? n_c : 0)) * a.Hq + h0 + c % HPW) * D;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            qb[kb] = col_ok ? *(const mfa_u32x4*)(qp + (4 * kb + G) * 8) : mfa_u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const uint32_t tok_bytes = (uint32_t)a.Hkv * D * 2;
+    const uint32_t k_off = (uint32_t)c * tok_bytes;   // A row = token c of the page
+    // direct V load i of page j: LDS slots (j * VLOADS + i) * 64 + lane, i.e. step row
+    // r = slot / KCH (token r - 16 j of page j), physical chunk slot % KCH, which holds
+    // logical chunk dec_v_phys(r, phys); the swizzle depends on r only through bits that
+    // do not change with i or j, so one per-lane offset serves every load
+    uint32_t v_off;
+    {
+        const int r = lane / KCH, phys = lane % KCH;
+        v_off = (uint32_t)r * tok_bytes + (uint32_t)dec_v_phys<D>(r, phys) * 16;
+    }
+    constexpr int TOK_PER_LOAD = 64 / KCH;
+    // transposing reads: lane group G' = G reads rows 4G' + i / 4 of a page, columns
+    // 16 db + 4 (i % 4) .. +3, i = lane % 16
+    int v_rd[NDB];
+    {
+        const int i = lane & 15;
+        const int r = 4 * G + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 16 * db + 4 * (i & 3);
+            v_rd[db] = r * D + dec_v_phys<D>(r, col >> 3) * 8 + (col & 7);
+        }
+    }
+
+    float m_run = -MFA_INF;   // row c's exponent offset (log2 domain), same in its 4 lanes
+    float l_run = 0.f;        // this lane's part of row c's sum
+    mfa_f32x4 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfa_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+    const size_t page_elems = (size_t)kPage * a.Hkv * D;
+    int pid_next[kPG];
+#pragma unroll
+    for (int j = 0; j < kPG; ++j) pid_next[j] = w_begin + j < w_end ? mfa_uniform_load(bt + w_begin + j) : -1;
+
+    for (int pg = w_begin; pg < w_end; pg += kPG) {
+        mfa_u32x4 kr[kPG][NKB];
+        int nv[kPG];
+#pragma unroll
+        for (int j = 0; j < kPG; ++j) {
+            const int pid = pid_next[j];
+            const bool pvalid = pid >= 0 && pid < a.num_pages && pg + j < w_end;
+            nv[j] = pvalid ? min(kPage, L - (pg + j) * kPage) : 0;
+            const size_t pbase = (size_t)(pvalid ? pid : 0) * page_elems + (size_t)kvh * D;
+            const uint32_t bytes = (uint32_t)nv[j] * tok_bytes;
+            const auto rk = mfa_rsrc(a.kp + pbase, bytes);
+            const auto rv = mfa_rsrc(a.vp + pbase, bytes);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kr[j][kb] = mfa_load16(rk, k_off + (4 * kb + G) * 16);
+#pragma unroll
+            for (int i = 0; i < VLOADS; ++i)
+                mfa_load16_lds(rv, sv + (j * VLOADS + i) * 512, v_off + (uint32_t)(i * TOK_PER_LOAD) * tok_bytes);
+        }
+#pragma unroll
+        for (int j = 0; j < kPG; ++j)
+            pid_next[j] = pg + kPG + j < w_end ? mfa_uniform_load(bt + pg + kPG + j) : -1;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // scores (log2 domain), masked: position p visible iff p < L and p <= lim
+        float x[kPG][4];
+#pragma unroll
+        for (int j = 0; j < kPG; ++j) {
+            mfa_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) acc = mfa_mfma16<DT>(kr[j][kb], qb[kb], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * G + i;
+                const bool vis = t < nv[j] && (pg + j) * kPage + t <= lim;
+                x[j][i] = vis ? acc[i] * a.scale_log2 : -MFA_INF;
+            }
+        }
+        float tmax = -MFA_INF;
+#pragma unroll
+        for (int j = 0; j < kPG; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[j][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool raise = tmax > m_run + kLazy;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float m_new = raise ? tmax : m_run;
+            const float alpha = (m_run == -MFA_INF) ? 0.f : mfa_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -MFA_INF) ? 0.f : m_run;
+        mfa_u32x4 pb;
+#pragma unroll
+        for (int j = 0; j < kPG; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float p0 = mfa_exp2(x[j][2 * e] - m_use);
+                const float p1 = mfa_exp2(x[j][2 * e + 1] - m_use);
+                const uint32_t pk = mfa_pack2<DT>(p0, p1);
+                pb[2 * j + e] = pk;
+                if constexpr (DT == MFA_DT_F16)
+                    l_run = mfa_sum2<DT>(pk, l_run);
+                else
+                    l_run += p0 + p1;
+            }
+
+        // O^T += V^T P^T from the wave's LDS copy of the two pages
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the direct loads have landed
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const mfa_u32x2 lo = mfa_lds_read_tr16(sv + v_rd[db]);
+            const mfa_u32x2 hi = mfa_lds_read_tr16(sv + kPage * D + v_rd[db]);
+            oacc[db] = mfa_mfma16<DT>(mfa_u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, oacc[db]);
+        }
+        // the next step's copies overwrite the buffer: its reads must have returned
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    }
+
+    // merge the four waves' partial states of each row in LDS (reusing the V buffers)
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);   // the row's four lanes: c + 16 G
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    __syncthreads();
+    float* sm_o = reinterpret_cast<float*>(sv_all);   // [kWaves][16][D]
+    static_assert(kWaves * 16 * D * 4 <= kWaves * TILE * 2, "merge buffer fits");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        *(mfa_f32x4*)&sm_o[(wave * 16 + c) * D + 16 * db + 4 * G] = oacc[db];
+    if (G == 0) {
+        sm_m[wave][c] = m_run;
+        sm_l[wave][c] = l_tot;
+    }
+    __syncthreads();
+    const int R = HPW * nq;
+    for (int idx = tid; idx < R * D; idx += kThreads) {
+        const int row = idx / D, d = idx - row * D;
+        float M = -MFA_INF;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+        float lt = 0.f, ot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (sm_m[w][row] == -MFA_INF) ? 0.f : mfa_exp2(sm_m[w][row] - M);
+            lt += f * sm_l[w][row];
+            ot += f * sm_o[(w * 16 + row) * D + d];
+        }
+        const int n = row / HPW, hh = row - n * HPW;
+        const size_t slot = (((size_t)b * nq + n) * a.Hq + h0 + hh) * a.S + s;
+        a.ws_o[slot * D + d] = lt > 0.f ? ot / lt : 0.f;
+        if (d == 0) a.ws_lse[slot] = lt > 0.f ? M + mfa_log2(lt) : -MFA_INF;
+    }
+}
+
 // One workgroup of 4 waves per (sequence, head).  Wave w merges the splits
 // s = w, w + 4, ...: lane s % 64 holds a split's LSE, the weights are broadcast with
 // readlane and every lane accumulates D/64 columns; the 4 waves are then merged in LDS.
@@ -279,8 +502,8 @@ template <int D, int DT>
 __global__ __launch_bounds__(256) void mfa_decode_combine_kernel(DecArgs a) {
     constexpr int PER = D / 64;
     constexpr int NW = 4;
-    const int bh = blockIdx.x;
-    const int b = bh / a.Hq;
+    const int bh = blockIdx.x;   // (b * nq + n) * Hq + h
+    const int b = bh / (a.Hq * a.nq);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int L = clamp_len(a.seq_lens[b], a.max_pages);
@@ -376,6 +599,33 @@ int launch_hpw(const DecArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
     return launch<D, DT, 1>(a, stream, info);
 }
 
+template <int D, int DT, int HPW>
+int launch_mq(const DecArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
+    const dim3 grid1((unsigned)a.S, (unsigned)(a.Hq / HPW), (unsigned)a.B);
+    hipLaunchKernelGGL((mfa_decode_mq_split_kernel<D, DT, HPW>), grid1, dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
+    hipLaunchKernelGGL((mfa_decode_combine_kernel<D, DT>), dim3((unsigned)(a.B * a.nq * a.Hq)), dim3(256), 0,
+                       stream, a);
+    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_decode_mq_split_kernel<D=%d,%s,HPW=%d,nq=%d>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16", HPW, a.nq);
+    info->grid[0] = (int)grid1.x;
+    info->grid[1] = (int)grid1.y;
+    info->grid[2] = (int)grid1.z;
+    info->block = kThreads;
+    info->waves = kWaves;
+    info->n_launches = 2;
+    return MFA_OK;
+}
+
+// Query heads per workgroup: the largest of 4, 2, 1 that divides g with HPW * nq <= 16.
+template <int D, int DT>
+int launch_mq_hpw(const DecArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
+    if (a.g % 4 == 0 && 4 * a.nq <= 16) return launch_mq<D, DT, 4>(a, stream, info);
+    if (a.g % 2 == 0 && 2 * a.nq <= 16) return launch_mq<D, DT, 2>(a, stream, info);
+    return launch_mq<D, DT, 1>(a, stream, info);
+}
+
 }  // namespace
 
 int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits) {
@@ -405,15 +655,23 @@ int mfa_decode_launch(const MfaDecodeProblem& pr, hipStream_t stream, mfa_dispat
     a.Hq = pr.Hq;
     a.Hkv = pr.Hkv;
     a.g = pr.Hq / pr.Hkv;
+    a.nq = pr.nq;
     a.num_pages = pr.num_pages;
     a.max_pages = pr.max_pages_per_seq;
     a.chunk_pages = pr.chunk_pages;
     a.S = pr.num_splits;
     a.scale_log2 = pr.scale * 1.4426950408889634f;
     a.ws_o = (float*)pr.workspace;
-    a.ws_lse = a.ws_o + (size_t)pr.B * pr.Hq * pr.num_splits * pr.D;
+    a.ws_lse = a.ws_o + (size_t)pr.B * pr.nq * pr.Hq * pr.num_splits * pr.D;
     info->num_splits = a.S;
     info->chunk_tokens = a.chunk_pages * kPage;
+    if (pr.multi) {
+        if (pr.D == 128)
+            return pr.dtype == MFA_F16 ? launch_mq_hpw<128, MFA_DT_F16>(a, stream, info)
+                                       : launch_mq_hpw<128, MFA_DT_BF16>(a, stream, info);
+        return pr.dtype == MFA_F16 ? launch_mq_hpw<64, MFA_DT_F16>(a, stream, info)
+                                   : launch_mq_hpw<64, MFA_DT_BF16>(a, stream, info);
+    }
     if (pr.D == 128)
         return pr.dtype == MFA_F16 ? launch_hpw<128, MFA_DT_F16>(a, stream, info)
                                    : launch_hpw<128, MFA_DT_BF16>(a, stream, info);

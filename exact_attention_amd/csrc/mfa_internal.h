@@ -44,6 +44,8 @@ struct MfaDecodeProblem {
     int chunk_pages;     // pages per split
     void* workspace;
     int dtype;
+    int nq;              // query tokens per sequence (1 for mfa_decode_paged)
+    int multi;           // 1: the multi-token kernel (mfa_decode_paged_multi)
 };
 
 // Compute units of the current device (cached per device).

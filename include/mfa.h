@@ -16,6 +16,8 @@
  *                     sequence masked on its own lengths.
  *   mfa_fwd_varlen_paged  packed queries whose keys sit in a paged KV cache (chunked
  *                     prefill; mlx-mfa "Paged + packed varlen queries").
+ *   mfa_decode_paged_multi  the same for Nq <= 4 new tokens per sequence (speculative
+ *                     verification), with the query rows of a KV head packed together.
  *   mfa_decode_paged  single-query decode over a paged KV cache, split across
  *                     workgroups along the keys, with partial (O, LSE) pairs merged in
  *                     a second pass.  Defined by the mlx-mfa 2.5.2 page ("Flash Decode
@@ -229,12 +231,36 @@ int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                      int max_pages_per_seq, float scale, int num_splits,
                      void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
-/* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
+/* Bytes of workspace mfa_decode_paged_multi needs (0 if the arguments are invalid). */
+size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
+                                        int max_pages_per_seq, int num_splits);
+
+/* Paged split-KV decode of Nq <= 4 new tokens per sequence, e.g. the verification step of
+ * speculative decoding (mlx-mfa 2.5.2 feature list: "Flash Decode — two-phase split-KV for
+ * N_q <= 4"; the packed-GQA verify kernel of the MTPLX verify-attention page).  The new
+ * tokens' keys are already in the cache: they are its last Nq positions, and new token n
+ * sees the keys at positions <= seq_lens[b] - Nq + n (the visibility rule above with
+ * Nk = seq_lens[b], causal).  The g * Nq query rows of one KV head are computed together.
+ *   q    [B, Nq, Hq, D] dtype        out [B, Nq, Hq, D] dtype    lse [B, Nq, Hq] float32 or NULL
+ *   k_pages, v_pages, block_table, seq_lens, page_size, num_pages, max_pages_per_seq,
+ *   num_splits: as for mfa_decode_paged, with the same device-side contract.
+ *   workspace: at least mfa_decode_multi_workspace_bytes(...) bytes of device memory.
+ * A row with no visible key (seq_lens[b] < Nq - n) gets O = 0 and LSE = -inf.
+ * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE (also Nq outside 1..4), _GQA, _PAGED,
+ * _SCALE, _ALIGN, _WORKSPACE, _ARG, _OVERFLOW, _HIP. */
+int mfa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           void* out, float* lse,
+                           int B, int Nq, int Hq, int Hkv, int D, int page_size, int num_pages,
+                           int max_pages_per_seq, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* What the last successful launch on this host thread ran/* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
  * record: backend, operation, selection and split fields). */
 typedef struct {
     char kernel[96];      /* kernel name of the main launch */
     int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward,
-                             4 = packed queries over a paged cache */
+                             4 = packed queries over a paged cache, 5 = multi-token decode */
     int BM, BN, waves;    /* forward tile configuration */
     int grid[3];          /* main launch grid */
     int block;            /* threads per workgroup */

@@ -198,6 +198,36 @@ def test_decode_validation(kw, code):
     assert dec(**kw) == code
 
 
+def dec_multi(**kw):
+    a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, out=0x60000, lse=0x70000, B=2, Nq=4, Hq=8, Hkv=2,
+             D=128, page_size=16, num_pages=10, max_pages=4, scale=0.1, num_splits=0, ws=0x80000,
+             ws_bytes=1 << 30, dtype=1, stream=None)
+    a.update(kw)
+    return ea.lib().mfa_decode_paged_multi(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["out"],
+                                           a["lse"], a["B"], a["Nq"], a["Hq"], a["Hkv"], a["D"],
+                                           a["page_size"], a["num_pages"], a["max_pages"],
+                                           a["scale"], a["num_splits"], a["ws"], a["ws_bytes"],
+                                           a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(sl=None), -1), (dict(dtype=5), -5), (dict(D=80), -4),
+    (dict(Nq=0), -2), (dict(Nq=5), -2), (dict(B=0), -2), (dict(Hkv=3), -3),
+    (dict(page_size=8), -9), (dict(scale=float("nan")), -7), (dict(num_splits=-2), -13),
+    (dict(ws=None), -8), (dict(ws_bytes=100), -8), (dict(out=0x60004), -12),
+])
+def test_decode_multi_validation(kw, code):
+    assert dec_multi(**kw) == code
+
+
+def test_multi_workspace_bytes():
+    one = ea.mfa_decode_workspace_bytes(16, 32, 128, 16, 2048, 0)
+    for nq in (1, 2, 3, 4):
+        assert ea.mfa_decode_multi_workspace_bytes(16, nq, 32, 128, 16, 2048, 0) == nq * one
+    assert ea.mfa_decode_multi_workspace_bytes(16, 5, 32, 128, 16, 2048, 0) == 0
+    assert ea.mfa_decode_multi_workspace_bytes(16, 0, 32, 128, 16, 2048, 0) == 0
+
+
 def test_workspace_and_splits():
     for max_pages, ns in [(2048, 0), (64, 0), (4, 0), (2048, 1), (2048, 7), (100, 3), (9, 1000)]:
         S = ea.mfa_decode_num_splits(16, max_pages, ns)
