@@ -130,6 +130,77 @@ def attention(q, k, v, scale: float, causal: bool = False, left: int = -1,
     return O, L
 
 
+def attention_ext(q, k, v, scale: float, causal: bool = False, left: int = -1, right: int = -1,
+                  softcap: float = 0.0, alibi_slopes=None, bias=None, block_mask=None,
+                  block_q: int = 0, block_k: int = 0, rows=None):
+    """Attention with score modifiers and a block-sparse mask, float64 (mlx-mfa 2.5.2
+    feature list: "Softcap", "ALiBi", "Block-sparse attention"; mlx-mfa 2.61.0 "Native
+    attn_bias" additive bias).
+
+    q ``[B, Hq, Nq, D]``, k/v ``[B, Hkv, Nk, D]``.  The score of query ``i`` and key ``j``
+    (``off = Nk - Nq``) is built in this order:
+
+    * ``s = scale * q_i . k_j``;
+    * softcap ``c > 0``: ``s = c * tanh(s / c)``;
+    * ALiBi (``alibi_slopes[h]``, one per query head): ``s -= slope_h * |i + off - j|``;
+    * additive bias (``bias`` of shape ``[B, Hq, Nk]``, a per-key bias broadcast over
+      the queries): ``s += bias[b, h, j]``;
+
+    then the causal / window visibility of ``attention`` and the block mask
+    (``block_mask[b, h, i // block_q, j // block_k]`` true = computed) both remove keys,
+    and the softmax runs over the remaining ones.  A row left with no key gives
+    ``O = 0``, ``LSE = -inf``.  Returns ``(O, LSE)`` like ``attention``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    off = Nk - Nq
+    cols = np.arange(Nk)
+
+    def row_block(b, h, ii):
+        kv = h // g
+        s = scale * (q[b, h, ii] @ k[b, kv].T)
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        if alibi_slopes is not None:
+            s = s - float(alibi_slopes[h]) * np.abs(ii[:, None] + off - cols[None, :])
+        if bias is not None:
+            s = s + np.asarray(bias, dtype=np.float64)[b, h][None, :]
+        vis = visible(ii[:, None], cols[None, :], Nq, Nk, causal, left, right)
+        if block_mask is not None:
+            bm = np.asarray(block_mask).astype(bool)[b, h]
+            vis = vis & bm[ii[:, None] // block_q, cols[None, :] // block_k]
+        s = np.where(vis, s, -np.inf)
+        any_vis = vis.any(axis=1)
+        m = np.where(any_vis, s.max(axis=1, initial=-np.inf), 0.0)
+        e = np.exp(s - m[:, None])
+        z = e.sum(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            p = np.where(any_vis[:, None], e / np.where(any_vis, z, 1.0)[:, None], 0.0)
+            lse = np.where(any_vis, m + np.log(np.where(any_vis, z, 1.0)), -np.inf)
+        return p @ v[b, kv], lse
+
+    if rows is not None:
+        rows = list(rows)
+        O = np.zeros((len(rows), D))
+        L = np.zeros(len(rows))
+        for n, (b, h, i) in enumerate(rows):
+            o, lse = row_block(b, h, np.array([i]))
+            O[n], L[n] = o[0], lse[0]
+        return O, L
+    O = np.zeros((B, Hq, Nq, D))
+    L = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            for r0 in range(0, Nq, 512):
+                ii = np.arange(r0, min(Nq, r0 + 512))
+                O[b, h, ii], L[b, h, ii] = row_block(b, h, ii)
+    return O, L
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
                      causal: bool = False, left: int = -1, right: int = -1, rows=None):
     """Packed variable-length attention, float64 (mlx-mfa "Variable-length" feature:

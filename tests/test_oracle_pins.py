@@ -15,7 +15,7 @@ import pytest
 import attn_inputs as A
 import oracle
 import oracle.reference as OA
-from oracle.scalar import attention_scalar, logsumexp_scalar
+from oracle.scalar import attention_scalar, attention_scalar_ext, logsumexp_scalar
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -431,13 +431,81 @@ def pin_decode_multi():
     np.testing.assert_allclose(L1[:, 0], Ld, atol=1e-13, rtol=0)
 
 
+def pin_ext_scalar():
+    # softcap, ALiBi, key bias and a block mask together, against the independent scalar
+    # implementation on tiny inputs (Nq != Nk, GQA)
+    q, k, v = _rand((1, 4, 5, 3), 90, 2.0), _rand((1, 2, 7, 3), 91, 2.0), _rand((1, 2, 7, 3), 92)
+    slopes = [0.5, 0.25, 0.125, 0.0625]
+    bias = _rand((1, 4, 7), 93)
+    bm = (np.random.default_rng(94).random((1, 4, 3, 4)) > 0.3)
+    for causal, left, right, sc in ((True, -1, -1, 3.0), (False, 2, 1, 0.0), (False, -1, -1, 1.5)):
+        O, L = oracle.attention_ext(q, k, v, 0.7, causal, left, right, softcap=sc,
+                                    alibi_slopes=slopes, bias=bias, block_mask=bm, block_q=2,
+                                    block_k=2)
+        Os, Ls = attention_scalar_ext(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, left, right,
+                                      sc, slopes, bias.tolist(), bm.tolist(), 2, 2)
+        np.testing.assert_allclose(O, np.array(Os), atol=1e-13, rtol=0)
+        np.testing.assert_allclose(L, np.array(Ls), atol=1e-13, rtol=0)
+
+
+def pin_ext_bias_torch():
+    # the per-key bias is torch's float attn_mask broadcast over the query rows (float64
+    # SDPA); with ALiBi under the causal mask, -slope * (i + off - j) differs from the key
+    # bias slope * j only by a per-row constant, which the softmax removes and the LSE keeps
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v = _rand((2, 3, 9, 8), 95), _rand((2, 3, 12, 8), 96), _rand((2, 3, 12, 8), 97)
+    bias = _rand((2, 3, 12), 98)
+    O, L = oracle.attention_ext(q, k, v, 0.3, bias=bias)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=torch.from_numpy(bias)[:, :, None, :], scale=0.3)
+    np.testing.assert_allclose(O, ref.numpy(), atol=1e-12, rtol=0)
+    slopes = np.array([0.3, 0.1, 0.02])
+    Oa, La = oracle.attention_ext(q, k, v, 0.3, causal=True, alibi_slopes=slopes)
+    kb = np.broadcast_to(slopes[None, :, None] * np.arange(12)[None, None, :], (2, 3, 12))
+    Ob, Lb = oracle.attention_ext(q, k, v, 0.3, causal=True, bias=kb)
+    np.testing.assert_allclose(Oa, Ob, atol=1e-12, rtol=0)
+    i = np.arange(9)
+    np.testing.assert_allclose(La, Lb - slopes[None, :, None] * (i + 3)[None, None, :], atol=1e-12,
+                               rtol=0)
+
+
+def pin_ext_limits_and_blocks():
+    # softcap -> infinity and zero slopes give plain attention; an all-true block mask
+    # changes nothing; a block mask equals torch's float64 SDPA with the block mask
+    # expanded element-wise (np.kron) as a boolean attn_mask
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v = _rand((1, 2, 10, 4), 99), _rand((1, 2, 10, 4), 100), _rand((1, 2, 10, 4), 101)
+    O0, L0 = oracle.attention(q, k, v, 0.5, True)
+    O1, L1 = oracle.attention_ext(q, k, v, 0.5, True, softcap=1e9, alibi_slopes=[0.0, 0.0],
+                                  block_mask=np.ones((1, 2, 5, 4), bool), block_q=2, block_k=3)
+    np.testing.assert_allclose(O1, O0, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(L1, L0, atol=1e-12, rtol=0)
+    for shape, bq, bk in (((1, 2, 5, 4), 2, 3), ((1, 2, 5, 5), 2, 2)):
+        bm = np.random.default_rng(102).random(shape) > 0.4
+        bm[..., 0] = True   # every row keeps a key block
+        Ob, _ = oracle.attention_ext(q, k, v, 0.5, block_mask=bm, block_q=bq, block_k=bk)
+        for h in range(2):
+            full = np.kron(bm[0, h], np.ones((bq, bk), bool))[:10, :10]
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q[:, h:h + 1]),
+                                                 torch.from_numpy(k[:, h:h + 1]),
+                                                 torch.from_numpy(v[:, h:h + 1]),
+                                                 attn_mask=torch.from_numpy(full), scale=0.5)
+            np.testing.assert_allclose(Ob[:, h:h + 1], ref.numpy(), atol=1e-12, rtol=0)
+    # a tiny softcap squeezes every score into (-c, c): the weights approach uniform
+    Oc, Lc = oracle.attention_ext(q, k, v, 0.5, softcap=1e-9)
+    np.testing.assert_allclose(Oc[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (10, 4)), atol=1e-8)
+    np.testing.assert_allclose(Lc, np.log(10.0), atol=1e-8)
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
         pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
         pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged,
-        pin_decode_multi]
+        pin_decode_multi, pin_ext_scalar, pin_ext_bias_torch, pin_ext_limits_and_blocks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -551,6 +619,41 @@ def _mut_varlen_paged_context_only(q, k_pages, v_pages, block_table, seq_lens_k,
 
 
 _ORIG_VARLEN_PAGED = OA.attention_varlen_paged
+_ORIG_EXT = OA.attention_ext
+
+
+def _mut_ext_softcap_unscaled(q, k, v, scale, causal=False, left=-1, right=-1, softcap=0.0,
+                              alibi_slopes=None, bias=None, block_mask=None, block_q=0, block_k=0,
+                              rows=None):
+    # plausible mistake: softcap applied before the scale (tanh of the raw dot product)
+    if softcap > 0:
+        softcap = softcap * scale
+    return _ORIG_EXT(q, k, v, scale, causal, left, right, softcap, alibi_slopes, bias, block_mask,
+                     block_q, block_k, rows)
+
+
+def _mut_ext_alibi_sign(q, k, v, scale, causal=False, left=-1, right=-1, softcap=0.0,
+                        alibi_slopes=None, bias=None, block_mask=None, block_q=0, block_k=0,
+                        rows=None):
+    # plausible mistake: the ALiBi penalty added instead of subtracted
+    if alibi_slopes is not None:
+        alibi_slopes = [-x for x in alibi_slopes]
+    return _ORIG_EXT(q, k, v, scale, causal, left, right, softcap, alibi_slopes, bias, block_mask,
+                     block_q, block_k, rows)
+
+
+def _mut_ext_block_transposed(q, k, v, scale, causal=False, left=-1, right=-1, softcap=0.0,
+                              alibi_slopes=None, bias=None, block_mask=None, block_q=0, block_k=0,
+                              rows=None):
+    # plausible mistake: block mask indexed (key block, query block) -- for a square mask
+    # the transpose, otherwise the two block sizes swapped
+    if block_mask is not None:
+        if block_mask.shape[-1] == block_mask.shape[-2]:
+            block_mask = np.swapaxes(block_mask, -1, -2)
+        else:
+            block_q, block_k = block_k, block_q
+    return _ORIG_EXT(q, k, v, scale, causal, left, right, softcap, alibi_slopes, bias, block_mask,
+                     block_q, block_k, rows)
 
 
 def _mut_decode_multi_top_left(q, k_pages, v_pages, block_table, seq_lens, scale, page_size):
@@ -582,6 +685,9 @@ MUTATIONS = {
     "varlen_top_left": ("attention_varlen", _mut_varlen_top_left),
     "varlen_paged_context_only": ("attention_varlen_paged", _mut_varlen_paged_context_only),
     "decode_multi_top_left": ("decode_paged_multi", _mut_decode_multi_top_left),
+    "ext_softcap_unscaled": ("attention_ext", _mut_ext_softcap_unscaled),
+    "ext_alibi_sign": ("attention_ext", _mut_ext_alibi_sign),
+    "ext_block_transposed": ("attention_ext", _mut_ext_block_transposed),
 }
 
 
