@@ -47,6 +47,16 @@ class mfa_dispatch_info(ctypes.Structure):
                 ("n_launches", ctypes.c_int)]
 
 
+class mfa_fwd_ext_args(ctypes.Structure):
+    _fields_ = [("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("bias_stride_b", ctypes.c_longlong),
+                ("bias_stride_h", ctypes.c_longlong), ("block_mask", ctypes.c_void_p),
+                ("mask_stride_b", ctypes.c_longlong), ("mask_stride_h", ctypes.c_longlong),
+                ("mask_q_blocks", ctypes.c_int), ("mask_k_blocks", ctypes.c_int),
+                ("block_q", ctypes.c_int), ("block_k", ctypes.c_int),
+                ("tile_log", ctypes.c_void_p)]
+
+
 _LIB = None
 
 _VP = ctypes.c_void_p
@@ -57,6 +67,8 @@ _SIGS = {
     "mfa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_fwd_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                              _VP, _VP]),
+    "mfa_fwd_ext": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                         ctypes.POINTER(mfa_fwd_ext_args), _I, _VP]),
     "mfa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                             _I, _I, _I, _I, _VP]),
     "mfa_fwd_varlen_tilelog": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
@@ -218,6 +230,71 @@ def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left:
 
 def mfa_fwd_tilelog(q, k, v, tile_log, **kw):
     return mfa_fwd(q, k, v, tile_log=tile_log, **kw)
+
+
+def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_left: int = -1,
+                win_right: int = -1, softcap: float = 0.0, alibi_slopes=None, bias=None,
+                block_mask=None, block_q: int = 0, block_k: int = 0, out=None, lse=None,
+                return_lse: bool = True, tile_log=None):
+    """Dense forward with score modifiers and a block-sparse mask on torch tensors.
+
+    q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D].  ``alibi_slopes``: float32 [Hq].  ``bias``: float32
+    with the keys as its last, contiguous dimension, broadcastable to [B, Hq, Nk] through
+    its strides (e.g. [Nk], [Hq, Nk] or [B, Hq, Nk] views).  ``block_mask``: uint8/bool
+    [B?, H?, nqb, nkb] (leading dims broadcast through strides) with blocks of
+    ``block_q`` x ``block_k`` (multiples of 32).  Returns ``(out, lse)``.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ext = mfa_fwd_ext_args()
+    ext.softcap = float(softcap)
+    keep = []
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,):
+            raise ValueError("alibi_slopes must be float32 [Hq]")
+        ext.alibi_slopes = _dev(alibi_slopes, "alibi_slopes")
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.shape[-1] != Nk or bias.stride(-1) != 1:
+            raise ValueError("bias must be float32 with a contiguous last dimension of Nk")
+        b3 = bias.expand(B, Hq, Nk) if bias.dim() <= 3 else None
+        if b3 is None:
+            raise ValueError("bias must broadcast to [B, Hq, Nk]")
+        if not bias.is_cuda:
+            raise ValueError("bias must be a device tensor")
+        ext.bias = bias.data_ptr()
+        ext.bias_stride_b, ext.bias_stride_h = b3.stride(0), b3.stride(1)
+        keep.append(bias)
+    if block_mask is not None:
+        bm = block_mask if block_mask.dtype == torch.uint8 else block_mask.to(torch.uint8)
+        if bm.dim() != 4 or bm.stride(-1) != 1 or not bm.is_cuda:
+            raise ValueError("block_mask must be a 4-D device tensor [B?, H?, nqb, nkb]")
+        b4 = bm.expand(B, Hq, bm.shape[2], bm.shape[3])
+        if b4.stride(2) != bm.shape[3]:
+            raise ValueError("block_mask rows must be contiguous")
+        ext.block_mask = bm.data_ptr()
+        ext.mask_stride_b, ext.mask_stride_h = b4.stride(0), b4.stride(1)
+        ext.mask_q_blocks, ext.mask_k_blocks = bm.shape[2], bm.shape[3]
+        ext.block_q, ext.block_k = int(block_q), int(block_k)
+        keep.append(bm)
+    if tile_log is not None:
+        if tile_log.dtype != torch.int32:
+            raise TypeError("tile_log must be int32")
+        ext.tile_log = _dev(tile_log, "tile_log")
+    _check(lib().mfa_fwd_ext(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                             _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, Nq, Nk, D,
+                             float(scale), int(bool(causal)), int(win_left), int(win_right),
+                             ctypes.byref(ext), dt, _stream(q)), "mfa_fwd_ext")
+    return out, lse
 
 
 def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
@@ -417,7 +494,8 @@ def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: fl
 
 
 __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
-           "mfa_fwd_varlen", "mfa_fwd_varlen_paged", "mfa_decode_paged_multi",
+           "mfa_fwd_ext", "mfa_fwd_ext_args", "mfa_fwd_varlen", "mfa_fwd_varlen_paged",
+           "mfa_decode_paged_multi",
            "mfa_decode_multi_workspace_bytes",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
            "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version"]

@@ -76,13 +76,14 @@ void plan_fill(int Nq, int Nk, int D, int causal, int left, int right, mfa_plan*
 
 int fwd_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                int Hq, int Hkv, int Nq, int Nk, int D, float scale, int causal, int win_left,
-               int win_right, int dtype, void* stream, int32_t* tile_log) {
+               int win_right, int dtype, void* stream, int32_t* tile_log,
+               const mfa_fwd_ext_args* ext = nullptr) {
     int st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
                        win_right, dtype);
     if (st) return st;
     MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, Nq, Nk, D, scale,
                     causal, win_left, win_right, dtype, nullptr, nullptr, 0, 0,
-                    nullptr, nullptr, 0, 0};
+                    nullptr, nullptr, 0, 0, ext};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 1;
@@ -92,6 +93,10 @@ int fwd_common(const void* q, const void* k, const void* v, void* out, float* ls
     mfa_plan plan;
     plan_fill(Nq, Nk, D, causal, win_left, win_right, &plan, nullptr);
     info.planned = plan.visited * (long long)B * Hq;
+    if (ext) {
+        info.op = 6;
+        if (ext->block_mask) info.planned = -1;
+    }
     g_last = info;
     g_have_last = true;
     return MFA_OK;
@@ -133,7 +138,7 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
     if (st) return st;
     MfaFwdProblem p{q, k, v, out, lse, tile_log, B, Hq, Hkv, max_q, max_k, D, scale,
                     causal, win_left, win_right, dtype, cu_q, cu_k, total_q, total_k,
-                    nullptr, nullptr, 0, 0};
+                    nullptr, nullptr, 0, 0, nullptr};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 3;
@@ -176,7 +181,8 @@ int varlen_paged_common(const void* q, const void* k_pages, const void* v_pages,
     const int key_cap = std::min(max_k, max_pages * page_size);
     MfaFwdProblem p{q, k_pages, v_pages, out, lse, nullptr, B, Hq, Hkv, max_q,
                     key_cap, D, scale, causal, win_left, win_right, dtype,
-                    cu_q, nullptr, total_q, 0, block_table, seq_lens_k, num_pages, max_pages};
+                    cu_q, nullptr, total_q, 0, block_table, seq_lens_k, num_pages, max_pages,
+                    nullptr};
     mfa_dispatch_info info;
     memset(&info, 0, sizeof(info));
     info.op = 4;
@@ -271,6 +277,29 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
             int win_right, int dtype, void* stream) {
     return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
                       win_right, dtype, stream, nullptr);
+}
+
+int mfa_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                int Hkv, int Nq, int Nk, int D, float scale, int causal, int win_left,
+                int win_right, const mfa_fwd_ext_args* ext, int dtype, void* stream) {
+    if (!ext) return MFA_ERR_NULL;
+    if (!(ext->softcap >= 0.f) || !isfinite(ext->softcap)) return MFA_ERR_ARG;
+    if (ext->bias && (ext->bias_stride_b < 0 || ext->bias_stride_h < 0)) return MFA_ERR_ARG;
+    if (ext->bias && (((uintptr_t)ext->bias & 3u) != 0)) return MFA_ERR_ALIGN;
+    if (ext->alibi_slopes && (((uintptr_t)ext->alibi_slopes & 3u) != 0)) return MFA_ERR_ALIGN;
+    if (ext->tile_log && (((uintptr_t)ext->tile_log & 3u) != 0)) return MFA_ERR_ALIGN;
+    if (ext->block_mask) {
+        if (ext->block_q < 32 || ext->block_k < 32 || ext->block_q % 32 || ext->block_k % 32)
+            return MFA_ERR_ARG;
+        if (ext->mask_stride_b < 0 || ext->mask_stride_h < 0) return MFA_ERR_ARG;
+        if (Nq >= 1 && Nk >= 1 &&
+            ((int64_t)ext->mask_q_blocks * ext->block_q < Nq ||
+             (int64_t)ext->mask_k_blocks * ext->block_k < Nk))
+            return MFA_ERR_ARG;
+        if (Nk > 131072) return MFA_ERR_OVERFLOW;
+    }
+    return fwd_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
+                      win_right, dtype, stream, ext->tile_log, ext);
 }
 
 int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, float* lse, int B,

@@ -91,7 +91,18 @@ struct FwdArgs {
     const int32_t* block_table;
     const int32_t* seq_lens_k;
     int max_pages, num_pages;
+    // score modifiers and block-sparse mask (MODE 3)
+    float scale;            // signed; applied before the modifiers
+    float softcap;          // > 0: s -> softcap * tanh(s / softcap)
+    const float* alibi;     // [Hq] or NULL: s -= slope_h * |i + off - j|
+    const float* bias;      // or NULL: s += bias[b * bias_sb + h * bias_sh + j]
+    long long bias_sb, bias_sh;
+    const uint8_t* bmask;   // or NULL: block (i / block_q, j / block_k) of (b, h) computed iff != 0
+    long long bm_sb, bm_sh;
+    int bm_nkb, block_q, block_k;
 };
+
+constexpr int kMaxList = 2048;   // visited key tiles a block-sparse query tile may list
 
 template <int N>
 struct MfaInt {
@@ -144,6 +155,14 @@ __device__ __forceinline__ mfa_u32x4 lds_read16(const uint16_t* __restrict__ p) 
 __device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
     return mfa_lds_read_tr16(p);
 }
+__device__ __forceinline__ int lds_read_i32(const int* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const int lds_i32;
+    return *(lds_i32*)p;
+}
+__device__ __forceinline__ mfa_f32x4 lds_read_f4(const float* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const mfa_f32x4 lds_f32x4;
+    return *(lds_f32x4*)p;
+}
 
 // Sequence s of a pack: tokens [cu[s], cu[s+1]) clamped into [0, total] and to at most
 // max_len of them, so that every access stays inside the packed tensors whatever the
@@ -165,9 +184,13 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int total, 
 //   bottom-right on its own lengths.  LSE is [Hq, total_q].
 // MODE 2: packed queries as in MODE 1; sequence b's seq_lens_k[b] keys sit in a paged
 //   cache, token t in page block_table[b, t / 16], slot t % 16.
+// MODE 3: dense tensors with score modifiers (softcap, ALiBi, an additive per-key bias)
+//   and an optional block-sparse mask: the workgroup first lists the key tiles of its
+//   causal / window range that hold a computed block (a compacted list in LDS, with
+//   per-(wave, 32-key block) visibility bits and a no-mask flag), then walks the list.
 template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, int MODE>
 __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
-    constexpr bool VAR = MODE != 0;
+    constexpr bool VAR = MODE == 1 || MODE == 2;   // packed sequences
     constexpr bool PAGED = MODE == 2;
     using T = Tile<D>;
     constexpr int BN = kBN;
@@ -251,10 +274,74 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // group 0 takes the first ceil(n/2), group 1 the rest
     int t_lo, t_hi;
     mfa_tile_range(mask, Nq, kBM, BN, qt, &t_lo, &t_hi);
-    const int n_all = t_hi - t_lo;
+    int n_all = t_hi - t_lo;
+
+    // block-sparse: list the tiles of [t_lo, t_hi) holding a computed block (one wave
+    // scans 64 tiles per ballot); entry = tile | visibility bits (2 * wave + key block)
+    // << 20 | no-mask flag << 28
+    __shared__ int tlist[MODE == 3 ? kMaxList : 1];
+    __shared__ int tcount;
+    const bool use_list = MODE == 3 && a.bmask != nullptr;
+    if constexpr (MODE == 3) {
+        if (use_list) {
+            if (tid < 64) {
+                const uint8_t* bm = a.bmask + (size_t)b * a.bm_sb + (size_t)h * a.bm_sh;
+                int cnt = 0;
+                for (int base = t_lo; base < t_hi; base += 64) {
+                    const int kt = base + lane;
+                    bool any = false, all = true;
+                    int bits = 0;
+                    if (kt < t_hi) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int r0 = q0 + 32 * w;
+                            if (r0 >= Nq) {      // rows past the end: no constraint
+                                bits |= 3 << (2 * w);
+                                continue;
+                            }
+                            const int qb = r0 / a.block_q;
+                            const int r1 = min(r0 + 31, Nq - 1);
+                            const int64_t lo0 = mfa_row_lo(mask, r0), hi1 = mfa_row_hi(mask, r1);
+#pragma unroll
+                            for (int nb = 0; nb < 2; ++nb) {
+                                // the 32 x 32 sub-block lies in one mask block; it is computed
+                                // iff that block is on and some pair in it is causal / window
+                                // visible (row bounds grow by one per row, so checking the
+                                // first row's low end and the last row's high end suffices)
+                                const int k0 = kt * BN + 32 * nb;
+                                const int k1 = min(k0 + 31, Nk - 1);
+                                const bool on = k0 < Nk && hi1 >= k0 && lo0 <= k1 &&
+                                                bm[(size_t)qb * a.bm_nkb + k0 / a.block_k] != 0;
+                                bits |= (on ? 1 : 0) << (2 * w + nb);
+                                any |= on;
+                                all &= on;
+                            }
+                        }
+                    }
+                    const uint64_t mk = __builtin_amdgcn_ballot_w64(any);
+                    const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+                    if (any && pos < kMaxList)
+                        tlist[pos] = kt | (bits << 20) | ((all && mfa_tile_full(mask, kBM, BN, qt, kt)) ? 1 << 28 : 0);
+                    cnt += __builtin_popcountll(mk);
+                }
+                if (lane == 0) tcount = cnt < kMaxList ? cnt : kMaxList;
+            }
+            __syncthreads();
+            n_all = tcount;
+        }
+    }
     const int n0 = GROUPS == 1 ? n_all : (n_all + 1) >> 1;
     const int kt_lo = grp == 0 ? t_lo : t_lo + n0;
     const int n = grp == 0 ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
+    const int lbase = grp == 0 ? 0 : n0;        // this group's first list entry
+    // key tile of this group's idx-th visited tile
+    auto tile_at = [&](int idx) {
+        if constexpr (MODE == 3) {
+            if (use_list) return __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + lbase + idx) & 0xfffff);
+        }
+        return kt_lo + idx;
+    };
 
     const size_t q_base = VAR ? ((size_t)qs * a.Hq + h) * D : (size_t)(b * a.Hq + h) * (size_t)a.Nq * D;
     // (paged: the head's slice of the pool's page 0; pages are 16 * SK elements apart)
@@ -285,6 +372,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int64_t rhi64 = mfa_row_hi(mask, qrow);
     const int row_lo = rlo64 > Nk ? Nk : (int)rlo64;
     const int row_hi = rhi64 < -1 ? -1 : (int)rhi64;
+    const float alibi_slope = (MODE == 3 && a.alibi != nullptr)
+                                  ? __builtin_bit_cast(float, mfa_uniform_load((const int32_t*)a.alibi + h))
+                                  : 0.f;
 
     mfa_f32x16 oacc[NDB];
 #pragma unroll
@@ -426,6 +516,59 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const float sl2 = a.scale_log2_abs;
     int n_edge = 0;
 
+    // ---- score modifiers (MODE 3): the scores become scale * q.k, softcapped, minus the
+    // ALiBi distance penalty, plus the key bias (copied to LDS one stage ahead) ----------
+    __shared__ __attribute__((aligned(16))) float sbias[MODE == 3 ? GROUPS * 2 * kBN : 4];
+    auto copy_bias = [&](int kt, int buf) {
+        const int k0 = kt * BN;
+        const float* row = a.bias + (size_t)b * a.bias_sb + (size_t)h * a.bias_sh;
+        const auto r = mfa_rsrc(row + k0, (uint32_t)max(Nk - k0, 0) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(sbias + (grp * 2 + buf) * kBN), 4,
+            (uint32_t)lane * 4, 0, 0, 0);
+    };
+    auto apply_modifiers = [&](mfa_f32x16(&sc)[NNB], int kt, int buf) {
+        const int k0 = kt * BN;
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) sc[nb] *= a.scale;
+        if (a.softcap > 0.f) {   // c * tanh(x / c) = c - 2c / (exp(2x / c) + 1)
+            const float c = a.softcap, k2 = 2.f * 1.4426950408889634f / c;
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float t = mfa_exp2(sc[nb][r] * k2);
+                    sc[nb][r] = c - 2.f * c * __builtin_amdgcn_rcpf(t + 1.f);
+                }
+        }
+        if (a.alibi != nullptr) {
+            const float slope = alibi_slope;
+            const int qpos = qrow + (Nk - Nq);
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + nb * 32 + 16 * (r >> 3) + 8 * g32 + (r & 7);
+                    sc[nb][r] -= slope * fabsf((float)(qpos - key));
+                }
+        }
+        if (a.bias != nullptr) {
+            const float* bl = sbias + (grp * 2 + buf) * kBN;
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kk = nb * 32 + 16 * hh + 8 * g32;
+                    const mfa_f32x4 b0 = lds_read_f4(bl + kk), b1 = lds_read_f4(bl + kk + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sc[nb][8 * hh + e] += b0[e];
+                        sc[nb][8 * hh + 4 + e] += b1[e];
+                    }
+                }
+        }
+    };
+
     // S^T = K Q^T for the key tile in K buffer KBUF into s
     auto qk_mfma = [&](auto kb_c, mfa_f32x16(&s)[NNB]) {
         constexpr int kbuf = decltype(kb_c)::value;
@@ -472,25 +615,41 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // -inf (after the sign of scale), so the rest of the stage is the same code.
     auto stage = [&](const int j, auto p_c, mfa_f32x16(&s_cur)[NNB], mfa_f32x16(&s_next)[NNB]) {
         constexpr int P = decltype(p_c)::value;
-        const int kt = kt_lo + j;
+        int kt = kt_lo + j;
+        int ent = 0;   // block-sparse list entry of tile j
+        int kt_k = kt + 2, kt_v = kt + 1;
+        if constexpr (MODE == 3) {
+            if (use_list) {
+                ent = __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + lbase + j));
+                kt = ent & 0xfffff;
+                kt_k = j + 2 < n ? tile_at(j + 2) : 0;
+                kt_v = j + 1 < n ? tile_at(j + 1) : 0;
+            }
+        }
         // copies of K(j+2) and V(j+1), spread over the stage (a burst of copies at the
         // start would queue every wave behind the CU's address path)
-        const auto rk = tile_rsrc(kg, kt + 2, j + 2 < n);
-        const auto rv = tile_rsrc(vg, kt + 1, j + 1 < n);
+        const auto rk = tile_rsrc(kg, kt_k, j + 2 < n);
+        const auto rv = tile_rsrc(vg, kt_v, j + 1 < n);
+        if constexpr (MODE == 3) {
+            if (a.bias != nullptr && wave == 0 && j + 1 < n) copy_bias(kt_v, P ^ 1);
+            apply_modifiers(s_cur, kt, P);
+        }
         int kpid_n[T::LOADS], vpid_n[T::LOADS];   // (paged) ids for the next stage's copies
         if constexpr (PAGED) {
             load_ids(kt + 3, j + 3 < n, kpid_n);
             load_ids(kt + 2, j + 2 < n, vpid_n);
         }
 
-        if (!mfa_tile_full(mask, kBM, BN, qt, kt)) {
+        const bool full = use_list ? ((ent >> 28) & 1) != 0 : mfa_tile_full(mask, kBM, BN, qt, kt);
+        if (!full) {
             const int k0 = kt * BN;
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + nb * 32 + 16 * (r >> 3) + 8 * g32 + (r & 7);
-                    const bool vis = key >= row_lo && key <= row_hi;
+                    const bool vis = key >= row_lo && key <= row_hi &&
+                                     (!use_list || ((ent >> (20 + 2 * wave + nb)) & 1) != 0);
                     s_cur[nb][r] = vis ? s_cur[nb][r] : (NEG ? MFA_INF : -MFA_INF);
                 }
             if (TILELOG) ++n_edge;
@@ -582,9 +741,12 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     mfa_f32x16 sA[NNB], sB[NNB];
     if (n0 > 0) {
         if (n > 0) {
-            issue_k(kt_lo, MfaInt<0>{});
-            issue_v(kt_lo, MfaInt<0>{});
-            if (n > 1) issue_k(kt_lo + 1, MfaInt<1>{});
+            issue_k(tile_at(0), MfaInt<0>{});
+            issue_v(tile_at(0), MfaInt<0>{});
+            if constexpr (MODE == 3) {
+                if (a.bias != nullptr && wave == 0) copy_bias(tile_at(0), 0);
+            }
+            if (n > 1) issue_k(tile_at(1), MfaInt<1>{});
             if constexpr (PAGED) {
                 load_ids(kt_lo + 2, 2 < n, kpid);
                 load_ids(kt_lo + 1, 1 < n, vpid);
@@ -664,10 +826,15 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
     if (TILELOG && tid == 0) {
         int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
-        t[0] = n_all ? t_lo : -1;
+        int first = t_lo, last = t_hi;
+        if (use_list && n_all > 0) {
+            first = tlist[0] & 0xfffff;
+            last = (tlist[n_all - 1] & 0xfffff) + 1;
+        }
+        t[0] = n_all ? first : -1;
         t[1] = n_all;
         t[2] = n_edge;
-        t[3] = n_all ? t_hi : -1;
+        t[3] = n_all ? last : -1;
     }
 }
 
@@ -693,7 +860,7 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
     }
     snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
-             MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
+             MODE == 3 ? ",ext" : MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
              tilelog ? ",tilelog" : "", neg ? ",neg" : "");
     info->BM = kBM;
     info->BN = kBN;
@@ -760,20 +927,35 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.seq_lens_k = pr.seq_lens_k;
     a.max_pages = pr.max_pages;
     a.num_pages = pr.num_pages;
+    a.scale = pr.scale;
+    a.softcap = pr.ext ? pr.ext->softcap : 0.f;
+    a.alibi = pr.ext ? pr.ext->alibi_slopes : nullptr;
+    a.bias = pr.ext ? pr.ext->bias : nullptr;
+    a.bias_sb = pr.ext ? pr.ext->bias_stride_b : 0;
+    a.bias_sh = pr.ext ? pr.ext->bias_stride_h : 0;
+    a.bmask = pr.ext ? pr.ext->block_mask : nullptr;
+    a.bm_sb = pr.ext ? pr.ext->mask_stride_b : 0;
+    a.bm_sh = pr.ext ? pr.ext->mask_stride_h : 0;
+    a.bm_nkb = pr.ext ? pr.ext->mask_k_blocks : 0;
+    a.block_q = pr.ext ? pr.ext->block_q : 0;
+    a.block_k = pr.ext ? pr.ext->block_k : 0;
     const bool var = pr.cu_seqlens_q != nullptr;
-    const int mode = pr.block_table != nullptr ? 2 : var ? 1 : 0;
+    const int mode = pr.ext != nullptr ? 3 : pr.block_table != nullptr ? 2 : var ? 1 : 0;
     // |scale| * log2(e), kept >= 1e-30 so that a masked (-inf) score times it stays
     // -inf; for scale = 0 the visible scores then all scale to ~0, i.e. the same
     // uniform weights up to fp32 rounding
     a.scale_log2_abs = fmaxf(fabsf(pr.scale) * 1.4426950408889634f, 1e-30f);
+    // (MODE 3 applies the signed scale itself, before the modifiers)
+    if (mode == 3) a.scale_log2_abs = 1.4426950408889634f;
     a.mask = mfa_make_mask(pr.Nq, pr.Nk, pr.causal, pr.left, pr.right);
     const bool tl = pr.tile_log != nullptr;
-    const bool neg = pr.scale < 0.f;
+    const bool neg = mode != 3 && pr.scale < 0.f;
     // query tiles that hold rows: every tile of the grid for dense inputs; for packed
     // sequences at most total_q / BM + B of the grid's B * ceil(max_seqlen_q / BM)
     long long q_tiles = (long long)a.n_q_tiles * pr.B;
     if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
     const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
+    if (mode == 3) return launch_dt<3>(pr, a, stream, groups, tl, neg, info);
     if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
     if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);
     return launch_dt<0>(pr, a, stream, groups, tl, neg, info);

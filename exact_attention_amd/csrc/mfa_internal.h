@@ -27,6 +27,8 @@ struct MfaFwdProblem {
     const int32_t* block_table;
     const int32_t* seq_lens_k;
     int num_pages, max_pages;
+    // dense forward with modifiers / block mask (NULL otherwise)
+    const mfa_fwd_ext_args* ext;
 };
 
 struct MfaDecodeProblem {

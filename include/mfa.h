@@ -11,6 +11,8 @@
  *                     max m and sum l in fp32, O = o / l, LSE = m + log l) and the
  *                     mlx-mfa 2.5.2 page's feature list ("Causal tile-skip",
  *                     "Sliding window", "Native GQA").
+ *   mfa_fwd_ext       the same with softcap, ALiBi, an additive key bias and a
+ *                     block-sparse mask (mlx-mfa "Softcap", "ALiBi", "Block-sparse").
  *   mfa_fwd_varlen    the same forward over packed sequences of different lengths
  *                     delimited by cu_seqlens (mlx-mfa "Variable-length"), each
  *                     sequence masked on its own lengths.
@@ -121,6 +123,47 @@ int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, floa
                     int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
                     int causal, int win_left, int win_right, int dtype, void* stream,
                     int32_t* tile_log);
+
+/* Score modifiers and block-sparse mask for mfa_fwd_ext (mlx-mfa 2.5.2 feature list:
+ * "Softcap — tanh softcapping fused in-kernel", "ALiBi — per-head linear position bias",
+ * "Block-sparse attention — block_mask tensor skips entire tiles"; mlx-mfa 2.61.0
+ * "Native attn_bias" additive bias on the logits, per key and per head per key).  With
+ * off = Nk - Nq the score of query i and key j of head h in batch b is, in this order:
+ *   s = scale * q_i . k_j
+ *   s = softcap * tanh(s / softcap)                         if softcap > 0
+ *   s = s - alibi_slopes[h] * |i + off - j|                 if alibi_slopes != NULL
+ *   s = s + bias[b * bias_stride_b + h * bias_stride_h + j]  if bias != NULL
+ * then keys outside the causal / window rule, and keys in a block with
+ *   block_mask[b * mask_stride_b + h * mask_stride_h + (i / block_q) * mask_k_blocks
+ *              + j / block_k] == 0
+ * are removed before the softmax; whole key tiles with no computed block are skipped.
+ * All pointers are device memory (NULL = feature off); strides are in elements (0
+ * broadcasts over batch or head). */
+typedef struct {
+    float softcap;                 /* 0 = off, else > 0 and finite */
+    const float* alibi_slopes;     /* [Hq] float32 or NULL */
+    const float* bias;             /* float32, keys contiguous, or NULL */
+    long long bias_stride_b, bias_stride_h;
+    const uint8_t* block_mask;     /* uint8 (0 = skip) or NULL */
+    long long mask_stride_b, mask_stride_h;
+    int mask_q_blocks;             /* >= ceil(Nq / block_q) rows of key blocks per (b, h) */
+    int mask_k_blocks;             /* >= ceil(Nk / block_k) key blocks per row */
+    int block_q, block_k;          /* positive multiples of 32 */
+    int32_t* tile_log;             /* optional per-tile record, as for mfa_fwd_tilelog */
+} mfa_fwd_ext_args;
+
+/* Dense forward (layouts and conventions of mfa_fwd) with the modifiers of *ext.  The
+ * tile record (ext->tile_log) lists, per (b, h, query tile), the first visited key tile,
+ * the number visited, how many were masked element-wise and one past the last visited.
+ * With a block mask, Nk must be at most 131072 (2048 key tiles per query tile) and
+ * mfa_last_dispatch reports planned = -1.
+ * Errors: those of mfa_fwd, plus MFA_ERR_NULL (ext NULL), MFA_ERR_ARG (softcap < 0 or
+ * not finite, block sizes not positive multiples of 32, mask dimensions too small,
+ * negative strides), MFA_ERR_OVERFLOW (Nk too large for a block mask). */
+int mfa_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+                int causal, int win_left, int win_right, const mfa_fwd_ext_args* ext,
+                int dtype, void* stream);
 
 /* Forward pass over packed variable-length sequences (mlx-mfa 2.5.2 feature list:
  * "Variable-length", packed sequences delimited by cu_seqlens; the page's note that
@@ -260,7 +303,8 @@ int mfa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pag
 typedef struct {
     char kernel[96];      /* kernel name of the main launch */
     int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward,
-                             4 = packed queries over a paged cache, 5 = multi-token decode */
+                             4 = packed queries over a paged cache, 5 = multi-token decode,
+                             6 = forward with modifiers / block mask */
     int BM, BN, waves;    /* forward tile configuration */
     int grid[3];          /* main launch grid */
     int block;            /* threads per workgroup */

@@ -176,6 +176,43 @@ def test_fwd_varlen_paged_validation(kw, code):
     assert fwd_paged(**kw) == code
 
 
+def fwd_ext(ext_kw, **kw):
+    import ctypes
+    e = ea.mfa_fwd_ext_args()
+    for k_, v_ in ext_kw.items():
+        setattr(e, k_, v_)
+    a = dict(q=A1, k=A2, v=A3, out=A4, lse=A5, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, D=128, scale=0.1,
+             causal=0, left=-1, right=-1, dtype=0, stream=None)
+    a.update(kw)
+    return ea.lib().mfa_fwd_ext(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"], a["causal"],
+                                a["left"], a["right"], ctypes.byref(e), a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("ext_kw,kw,code", [
+    (dict(softcap=-1.0), {}, -13), (dict(softcap=float("inf")), {}, -13),
+    (dict(softcap=float("nan")), {}, -13),
+    (dict(block_mask=0x90000, block_q=16, block_k=32, mask_q_blocks=4, mask_k_blocks=2), {}, -13),
+    (dict(block_mask=0x90000, block_q=32, block_k=48, mask_q_blocks=2, mask_k_blocks=2), {}, -13),
+    (dict(block_mask=0x90000, block_q=32, block_k=32, mask_q_blocks=1, mask_k_blocks=2), {}, -13),
+    (dict(block_mask=0x90000, block_q=32, block_k=32, mask_q_blocks=2, mask_k_blocks=1), {}, -13),
+    (dict(block_mask=0x90000, block_q=32, block_k=32, mask_q_blocks=2, mask_k_blocks=8192,
+          mask_stride_h=-1), {}, -13),
+    (dict(block_mask=0x90000, block_q=32, block_k=32, mask_q_blocks=2, mask_k_blocks=8192),
+     dict(Nk=200000), -10),
+    (dict(bias=0x90002), {}, -12), (dict(alibi_slopes=0x90001), {}, -12),
+    (dict(bias=0x90000, bias_stride_b=-4), {}, -13),
+    ({}, dict(D=96), -4), ({}, dict(q=None), -1), ({}, dict(Hq=3), -3),
+])
+def test_fwd_ext_validation(ext_kw, kw, code):
+    assert fwd_ext(ext_kw, **kw) == code
+
+
+def test_fwd_ext_null_args():
+    assert ea.lib().mfa_fwd_ext(A1, A2, A3, A4, A5, 1, 4, 2, 64, 64, 128, 0.1, 0, -1, -1, None, 0,
+                                None) == -1
+
+
 def dec(**kw):
     a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, out=0x60000, lse=0x70000, B=2, Hq=8, Hkv=2, D=128,
              page_size=16, num_pages=10, max_pages=4, scale=0.1, num_splits=0, ws=0x80000,
