@@ -267,6 +267,20 @@ def varlen_inputs(Hq: int, Hkv: int, D: int, dtype: str, seed: int, *, B: int | 
     return VarlenInputs(q, k, v, cu_q, cu_k, dtype)
 
 
+def block_mask_inputs(B: int, H: int, Nq: int, Nk: int, block_q: int, block_k: int,
+                      density: float, seed: int, diagonal: bool = True) -> np.ndarray:
+    """A seeded random block mask ``[B, H, ceil(Nq/block_q), ceil(Nk/block_k)]`` (uint8):
+    each block is on with probability ``density`` (uniform draws in one call, after which
+    the diagonal blocks are set when ``diagonal``)."""
+    rng = np.random.default_rng(seed)
+    nqb, nkb = -(-Nq // block_q), -(-Nk // block_k)
+    bm = (rng.random((B, H, nqb, nkb)) < density).astype(np.uint8)
+    if diagonal:
+        d = np.arange(min(nqb, nkb))
+        bm[:, :, d, d] = 1
+    return bm
+
+
 # The benchmark workloads.  Shapes follow the mlx-mfa "Performance" table
 # (B=2, H=8, f16, D=128, causal / window 512), its GQA statement (Hq a multiple of
 # Hkv), and the MXFlashAttn paged split-KV decode setting (pages of 16 tokens,
@@ -291,6 +305,11 @@ CONFIGS = {
     # speculative verification: 4 new tokens per sequence over the decode workload's cache
     8: dict(name="paged_multi_query_decode", B=16, Nq=4, Hq=32, Hkv=8, D=128, dtype=BF16,
             page_size=16, len_lo=1024, len_hi=32768, seed=108),
+    # block-sparse causal prefill (mlx-mfa "Block-sparse attention"): 128 x 128 blocks
+    # on with probability 1/4, plus the diagonal
+    9: dict(name="block_sparse_causal_prefill", B=1, Hq=16, Hkv=16, Nq=16384, Nk=16384, D=128,
+            dtype=F16, causal=True, left=-1, right=-1, block_q=128, block_k=128, density=0.25,
+            seed=109),
     7: dict(name="paged_chunked_prefill", B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True,
             left=-1, right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
             ctx_hi=16384, seed=107),

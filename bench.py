@@ -11,7 +11,9 @@ block-table entries used and seq_lens), and the packed variable-length causal pr
 (``mfa_fwd_varlen``, 16 sequences of 256..4096 tokens, TFLOP/s over visible pairs), and
 chunked prefill over the paged cache (``mfa_fwd_varlen_paged``, 8 sequences, new chunks
 of 512..2048 tokens after 1024..16384 cached ones), and the 4-token verification decode
-(``mfa_decode_paged_multi`` over the decode workload's cache shape, HBM GB/s).
+(``mfa_decode_paged_multi`` over the decode workload's cache shape, HBM GB/s), and the
+block-sparse causal prefill (``mfa_fwd_ext`` with a 25%-dense 128 x 128 block mask,
+TFLOP/s over the computed visible pairs).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
 workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
@@ -19,7 +21,7 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8,9] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -334,6 +336,58 @@ def bench_multi(step, steps):
     }
 
 
+def block_sparse_pairs(bm, Nq, Nk, bq, bk):
+    """Visible (query, key) pairs of a causal (Nq == Nk) attention under a block mask with
+    square blocks: a block below the diagonal holds bq * bk pairs, a diagonal block
+    bq (bq + 1) / 2 (full blocks only)."""
+    assert Nq == Nk and bq == bk and Nq % bq == 0
+    r = np.arange(bm.shape[-2])[:, None]
+    c = np.arange(bm.shape[-1])[None, :]
+    per_block = np.where(c < r, bq * bk, np.where(c == r, bq * (bq + 1) // 2, 0))
+    return int((bm.astype(np.int64) * per_block).sum())
+
+
+def setup_sparse():
+    """Device inputs and one step (one mfa_fwd_ext call) of the block-sparse prefill."""
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(9)
+    x = A.config_inputs(9)
+    bm = A.block_mask_inputs(c["B"], c["Hq"], c["Nq"], c["Nk"], c["block_q"], c["block_k"],
+                             c["density"], c["seed"] + 1000)
+    q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
+    bmd = torch.from_numpy(bm).to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def step():
+        ea.mfa_fwd_ext(q, k, v, scale=c["scale"], causal=True, block_mask=bmd, block_q=c["block_q"],
+                       block_k=c["block_k"], out=out, lse=lse)
+
+    step.pairs = block_sparse_pairs(bm, c["Nq"], c["Nk"], c["block_q"], c["block_k"])
+    step.density = float(bm.mean())
+    return step
+
+
+def bench_sparse(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(9)
+    ms, wall = time_calls(step, steps)
+    info = ea.mfa_last_dispatch()
+    flop = 4.0 * c["D"] * step.pairs
+    tf = flop / (ms * 1e-3) / 1e12
+    dense = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], True, -1, -1) * c["B"] * c["Hq"]
+    return {
+        "workload": f"{c['name']} B={c['B']} H={c['Hq']} N={c['Nq']} D={c['D']} {c['dtype']} causal, "
+                    f"{c['block_q']}x{c['block_k']} block mask, {step.density:.3f} of blocks on "
+                    f"({step.pairs / (dense / (4.0 * c['D'])):.3f} of the causal pairs)",
+        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config9", "fwd")},
+        "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
+    }
+
+
 def cpu_baseline(budget_s=10.0):
     """The float64 oracle on this host over whole heads of the dense causal prefill."""
     import oracle
@@ -367,7 +421,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5,6,7,8")
+    ap.add_argument("--workloads", default="2,3,4,5,6,7,8,9")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -386,7 +440,7 @@ def main():
     wl = [int(s) for s in args.workloads.split(",") if s]
     if 2 not in wl:
         wl = [2] + wl
-    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi}
+    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi, 9: setup_sparse}
     steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
@@ -404,6 +458,8 @@ def main():
             res[i] = bench_chunked(steps[i], args.steps)
         elif i == 8:
             res[i] = bench_multi(steps[i], args.steps)
+        elif i == 9:
+            res[i] = bench_sparse(steps[i], args.steps)
         else:
             res[i] = bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)
