@@ -13,6 +13,8 @@ tile by tile:
   is the materialised form of the forward pass (mlx-bun ``flash-attention.ts``:
   the ``manualSdpa`` reference and the forward shader's online softmax, which
   reaches the same result up to rounding).
+* ``attention_backward``: the gradients dQ, dK, dV of ``attention`` for an upstream
+  gradient dO (mlx-bun backward: D-vector, dK/dV and dQ passes).
 * ``attention_ext``: the same with softcap, ALiBi, an additive per-key bias and a
   block-sparse mask (mlx-mfa "Softcap", "ALiBi", "Block-sparse attention", "attn_bias").
 * ``attention_varlen``: the same for sequences of different lengths packed along the
@@ -35,11 +37,12 @@ Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed
 forms, invariants, a pure-Python scalar implementation (``oracle.scalar``) and
 PyTorch's float64 CPU attention routine.  No function here is "parity unpinned".
 """
-from .reference import (attention, attention_ext, attention_probs, attention_varlen,
+from .reference import (attention, attention_backward, attention_ext, attention_probs,
+                        attention_varlen,
                         attention_varlen_paged,
                         decode_paged, decode_paged_multi, gather_paged, lse_merge, visible,
                         visited_tiles, widen, window_bounds)
 
-__all__ = ["attention", "attention_ext", "attention_probs", "attention_varlen", "attention_varlen_paged",
+__all__ = ["attention", "attention_backward", "attention_ext", "attention_probs", "attention_varlen", "attention_varlen_paged",
            "decode_paged", "decode_paged_multi", "gather_paged", "lse_merge", "visible",
            "visited_tiles", "widen", "window_bounds"]

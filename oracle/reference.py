@@ -130,6 +130,46 @@ def attention(q, k, v, scale: float, causal: bool = False, left: int = -1,
     return O, L
 
 
+def attention_backward(q, k, v, dout, scale: float, causal: bool = False, left: int = -1,
+                       right: int = -1):
+    """Gradients of ``attention``'s O with respect to Q, K, V, float64 (mlx-bun
+    flash-attention.ts backward: the D-vector, dK/dV and dQ passes).
+
+    With P the attention probabilities of the forward (masked keys have P = 0) and
+    ``dO = dout``:
+    ``dV = P^T dO``, ``dP = dO V^T``, ``D_i = sum_d dO_id O_id`` (= sum_j P_ij dP_ij),
+    ``dS = P * (dP - D)``, ``dQ = scale * dS K``, ``dK = scale * dS^T Q``.
+    With grouped query heads, dK and dV of a KV head sum the contributions of its ``g``
+    query heads.  Rows with no visible key contribute nothing.  Returns ``(dQ, dK, dV)``
+    shaped like ``q``, ``k``, ``v``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    ii = np.arange(Nq)[:, None]
+    jj = np.arange(Nk)[None, :]
+    vis = visible(ii, jj, Nq, Nk, causal, left, right)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            _, _, p = _rows_attention(q[b, h], k[b, kv], v[b, kv], scale, vis)
+            o = p @ v[b, kv]
+            dp = dout[b, h] @ v[b, kv].T
+            dvec = (dout[b, h] * o).sum(axis=1)
+            ds = p * (dp - dvec[:, None])
+            dq[b, h] = scale * (ds @ k[b, kv])
+            dk[b, kv] += scale * (ds.T @ q[b, h])
+            dv[b, kv] += p.T @ dout[b, h]
+    return dq, dk, dv
+
+
 def attention_ext(q, k, v, scale: float, causal: bool = False, left: int = -1, right: int = -1,
                   softcap: float = 0.0, alibi_slopes=None, bias=None, block_mask=None,
                   block_q: int = 0, block_k: int = 0, rows=None):

@@ -499,13 +499,77 @@ def pin_ext_limits_and_blocks():
     np.testing.assert_allclose(Lc, np.log(10.0), atol=1e-8)
 
 
+def pin_backward_torch_autograd():
+    # the gradients equal torch's float64 autograd through its SDPA routine (dense, causal,
+    # GQA through SDPA's own head mapping, and a window given as a boolean mask)
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v = _rand((2, 4, 11, 8), 110), _rand((2, 2, 13, 8), 111), _rand((2, 2, 13, 8), 112)
+    do = _rand((2, 4, 11, 8), 113)
+    for causal, left, right in ((False, -1, -1), (True, -1, -1), (False, 3, 1)):
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.45, causal, left, right)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+        mask = None
+        if causal:
+            from torch.nn.attention.bias import causal_lower_right
+            mask = causal_lower_right(11, 13)._materialize()
+        elif left >= 0:
+            i = torch.arange(11)[:, None] + 2
+            j = torch.arange(13)[None, :]
+            mask = (j >= i - left) & (j <= i + right)
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.45, enable_gqa=True)
+        o.backward(torch.from_numpy(do))
+        np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_backward_finite_differences():
+    # central differences of L = sum(dO * O) through the oracle's forward, on every input
+    # element of a tiny causal GQA problem with Nq < Nk
+    q, k, v = _rand((1, 2, 3, 4), 114), _rand((1, 1, 5, 4), 115), _rand((1, 1, 5, 4), 116)
+    do = _rand((1, 2, 3, 4), 117)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.8, causal=True)
+
+    def loss(qq, kk, vv):
+        return float((oracle.attention(qq, kk, vv, 0.8, causal=True)[0] * do).sum())
+
+    eps = 1e-6
+    for x, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            up = loss(*args)
+            args[which][idx] -= 2 * eps
+            num[idx] = (up - loss(*args)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, atol=1e-7, rtol=0)
+
+
+def pin_backward_masked_keys_and_rows():
+    # keys no row sees get zero dK and dV; rows that see no key get zero dQ (causal Nq > Nk);
+    # a row that sees a single key has P = 1 there, so dS = dP - D = 0 and its dQ is zero
+    q, k, v = _rand((1, 1, 6, 3), 118), _rand((1, 1, 4, 3), 119), _rand((1, 1, 4, 3), 120)
+    do = _rand((1, 1, 6, 3), 121)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.5, causal=True)
+    assert np.all(dq[0, 0, :2] == 0)
+    assert np.all(np.abs(dq[0, 0, 2]) < 1e-15)
+    assert np.all(np.abs(dq[0, 0, 3:]).sum(axis=1) > 0)
+    # Nq = 3, Nk = 4, off = 1, causal with window (0, 0): row i sees key i + 1 only, so
+    # key 0 is seen by no row
+    dq, dk, dv = oracle.attention_backward(q[:, :, :3], k, v, do[:, :, :3], 0.5, True, 0, 0)
+    assert np.all(dk[0, 0, 0] == 0) and np.all(dv[0, 0, 0] == 0)
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
         pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
         pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged,
-        pin_decode_multi, pin_ext_scalar, pin_ext_bias_torch, pin_ext_limits_and_blocks]
+        pin_decode_multi, pin_ext_scalar, pin_ext_bias_torch, pin_ext_limits_and_blocks,
+        pin_backward_torch_autograd, pin_backward_finite_differences,
+        pin_backward_masked_keys_and_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -620,6 +684,24 @@ def _mut_varlen_paged_context_only(q, k_pages, v_pages, block_table, seq_lens_k,
 
 _ORIG_VARLEN_PAGED = OA.attention_varlen_paged
 _ORIG_EXT = OA.attention_ext
+_ORIG_BWD = OA.attention_backward
+
+
+def _mut_bwd_no_dvec(q, k, v, dout, scale, causal=False, left=-1, right=-1):
+    # plausible mistake: dS = P * dP (the D-vector term dropped)
+    q64, k64, v64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    dq, dk, dv = _ORIG_BWD(q64, k64, v64, do64, scale, causal, left, right)
+    O, _ = OA.attention(q64, k64, v64, scale, causal, left, right)
+    # adding back the removed term: dQ gains scale * D_i * sum_j P_ij K_j = scale * D_i * (P K)_i
+    Ok, _ = OA.attention(q64, k64, k64, scale, causal, left, right)
+    dvec = (do64 * O).sum(axis=-1, keepdims=True)
+    return dq + scale * dvec * Ok, dk, dv
+
+
+def _mut_bwd_no_scale_dk(q, k, v, dout, scale, causal=False, left=-1, right=-1):
+    # plausible mistake: dK without the softmax scale
+    dq, dk, dv = _ORIG_BWD(q, k, v, dout, scale, causal, left, right)
+    return dq, dk / scale, dv
 
 
 def _mut_ext_softcap_unscaled(q, k, v, scale, causal=False, left=-1, right=-1, softcap=0.0,
@@ -688,6 +770,8 @@ MUTATIONS = {
     "ext_softcap_unscaled": ("attention_ext", _mut_ext_softcap_unscaled),
     "ext_alibi_sign": ("attention_ext", _mut_ext_alibi_sign),
     "ext_block_transposed": ("attention_ext", _mut_ext_block_transposed),
+    "bwd_no_dvec": ("attention_backward", _mut_bwd_no_dvec),
+    "bwd_unscaled_dk": ("attention_backward", _mut_bwd_no_scale_dk),
 }
 
 
