@@ -75,6 +75,9 @@ _SIGS = {
                                     _I, _F, _I, _I, _I, _I, _VP, _VP]),
     "mfa_fwd_varlen_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
                                   _I, _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
+    "mfa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "mfa_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I, _I, _I,
+                     _I, _I, _I, _F, _I, _I, _I, _I, _VP]),
     "mfa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "mfa_decode_multi_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "mfa_decode_paged_multi": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
@@ -230,6 +233,40 @@ def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left:
 
 def mfa_fwd_tilelog(q, k, v, tile_log, **kw):
     return mfa_fwd(q, k, v, tile_log=tile_log, **kw)
+
+
+def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = False,
+            win_left: int = -1, win_right: int = -1, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass on torch tensors: the gradients (dq, dk, dv) of ``mfa_fwd``'s output
+    for upstream gradient ``dout``.  ``out`` and ``lse`` are the forward's results for the
+    same q, k, v, scale and mask arguments.  ``workspace`` is allocated here when absent.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    for t, n in ((out, "out"), (dout, "dout")):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib().mfa_bwd_workspace_bytes(B, Hq, Nq))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mfa_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                         _dev(dout, "dout"), _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"),
+                         _dev(dv, "dv"), _dev(workspace, "workspace"), wbytes, B, Hq, Hkv, Nq, Nk,
+                         D, float(scale), int(bool(causal)), int(win_left), int(win_right), dt,
+                         _stream(q)), "mfa_bwd")
+    return dq, dk, dv
 
 
 def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_left: int = -1,
@@ -494,7 +531,7 @@ def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: fl
 
 
 __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_fwd_tilelog",
-           "mfa_fwd_ext", "mfa_fwd_ext_args", "mfa_fwd_varlen", "mfa_fwd_varlen_paged",
+           "mfa_fwd_ext", "mfa_fwd_ext_args", "mfa_bwd", "mfa_fwd_varlen", "mfa_fwd_varlen_paged",
            "mfa_decode_paged_multi",
            "mfa_decode_multi_workspace_bytes",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",

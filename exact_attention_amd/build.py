@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmfa.so")
 
-SOURCES = ["mfa_api.cpp", "mfa_fwd.hip", "mfa_decode.hip"]
+SOURCES = ["mfa_api.cpp", "mfa_fwd.hip", "mfa_decode.hip", "mfa_bwd.hip"]
 
 # Packed-fp32 VALU instructions are disabled for the device code (hipcc would
 # otherwise form them from ordinary float code).

@@ -302,6 +302,39 @@ int mfa_fwd_ext(const void* q, const void* k, const void* v, void* out, float* l
                       win_right, dtype, stream, ext->tile_log, ext);
 }
 
+size_t mfa_bwd_workspace_bytes(int B, int Hq, int Nq) {
+    if (B < 1 || Hq < 1 || Nq < 1) return 0;
+    return (size_t)2 * (size_t)B * (size_t)Hq * (size_t)Nq * sizeof(float);
+}
+
+int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+            int causal, int win_left, int win_right, int dtype, void* stream) {
+    if (!out || !dout || !lse || !dq || !dk || !dv) return MFA_ERR_NULL;
+    int st = check_fwd(q, k, v, dq, nullptr, B, Hq, Hkv, Nq, Nk, D, scale, causal, win_left,
+                       win_right, dtype);
+    if (st) return st;
+    if (!aligned16(out) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) ||
+        ((uintptr_t)lse & 3u))
+        return MFA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < mfa_bwd_workspace_bytes(B, Hq, Nq)) return MFA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MFA_ERR_ALIGN;
+    if ((int64_t)((Nk + 127) / 128) > 0x7fffffffLL || (int64_t)B * Hkv > 65535 || (int64_t)B * Hq > 65535)
+        return MFA_ERR_OVERFLOW;
+    MfaBwdProblem p{q, k, v, out, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, Nq, Nk, D,
+                    scale, causal, win_left, win_right, dtype};
+    mfa_dispatch_info info;
+    memset(&info, 0, sizeof(info));
+    info.op = 7;
+    info.planned = -1;
+    st = mfa_bwd_launch(p, (hipStream_t)stream, &info);
+    if (st) return st;
+    g_last = info;
+    g_have_last = true;
+    return MFA_OK;
+}
+
 int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                     int Hq, int Hkv, int Nq, int Nk, int D, float scale, int causal,
                     int win_left, int win_right, int dtype, void* stream, int32_t* tile_log) {

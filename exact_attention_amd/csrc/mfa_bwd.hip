@@ -1,0 +1,516 @@
+// Backward pass of exact attention for gfx950: dQ, dK, dV from Q, K, V, the forward's
+// output O, its row log-sum-exp and the upstream gradient dO, in the three passes of the
+// FlashAttention-2 backward of the mlx-bun flash-attention.ts page:
+//   prep:  D_i = sum_d dO_id O_id per query row, and the LSE in the log2 domain;
+//   dK/dV: per key tile, over the query tiles (and the g query heads of a KV head):
+//          P = exp(scale S - LSE), dP = dO V^T, dS = P (dP - D),
+//          dV += P^T dO, dK += scale dS^T Q;
+//   dQ:    per query tile, over the key tiles: the same P and dS, dQ += scale dS K.
+// The probabilities are recomputed from the saved LSE (no running maximum is needed: P <= 1),
+// dQ is accumulated by its own pass rather than with atomics, so every result is
+// deterministic, and every product runs on the 32x32x16 MFMA:
+//   dK/dV pass, one wave = 32 keys (its K^T operand in registers, its V rows in LDS):
+//     S = Q K^T and dP = dO V^T with the query rows fed in key_perm order, so that each
+//     lane owns one key column and runs of 8 consecutive query rows; the packed P and dS
+//     are then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//     operands come from transposing LDS reads of the Q and dO tiles.
+//   dQ pass, one wave = 32 query rows (its Q^T and dO^T operands in registers):
+//     S^T = K Q^T and dP^T = V dO^T with the key rows in key_perm order, then
+//     dQ^T += K^T dS^T with K^T from transposing reads of the K tile.
+// Tiles stream through LDS with direct global -> LDS loads, double-buffered.  A wave skips
+// a 32 x 32 block holding no visible (query, key) pair.
+#include "mfa_device.h"
+#include "mfa_geometry.h"
+#include "mfa_internal.h"
+#include "mfa_tile.h"
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* lse2;    // [B, Hq, Nq]: LSE * log2(e), +inf for rows with no visible key
+    float* dvec;    // [B, Hq, Nq]: D_i
+    int B, Hq, Hkv, Nq, Nk, g;
+    float scale;       // signed
+    float scale_log2;  // scale * log2(e)
+    MfaMask mask;
+};
+
+// ---- prep: D_i and LSE in the log2 domain --------------------------------------------
+// 16 lanes per query row (D / 16 elements each, one 8- or 16-byte load of O and of dO),
+// reduced within the 16-lane DPP row.
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void mfa_bwd_prep_kernel(BwdArgs a) {
+    constexpr int PER = D / 16;
+    const long long rows = (long long)a.B * a.Hq * a.Nq;
+    const long long row = (long long)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+    const int c = threadIdx.x & 15;
+    float acc = 0.f;
+    if (row < rows) {
+        const size_t base = (size_t)row * D + c * PER;
+        if constexpr (PER == 8) {
+            const mfa_u32x4 o4 = *(const mfa_u32x4*)(a.o + base);
+            const mfa_u32x4 d4 = *(const mfa_u32x4*)(a.dout + base);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc += mfa_lo<DT>(o4[e]) * mfa_lo<DT>(d4[e]) + mfa_hi<DT>(o4[e]) * mfa_hi<DT>(d4[e]);
+        } else {
+            const mfa_u32x2 o2 = *(const mfa_u32x2*)(a.o + base);
+            const mfa_u32x2 d2 = *(const mfa_u32x2*)(a.dout + base);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                acc += mfa_lo<DT>(o2[e]) * mfa_lo<DT>(d2[e]) + mfa_hi<DT>(o2[e]) * mfa_hi<DT>(d2[e]);
+        }
+    }
+    acc = mfa_row16_sum(acc);
+    if (row < rows && c == 0) {
+        a.dvec[row] = acc;
+        const float l = a.lse[row];
+        a.lse2[row] = l == -MFA_INF ? MFA_INF : l * 1.4426950408889634f;
+    }
+}
+
+// Visibility of a 32 x 32 block (rows r0 .. r0 + 31 < Nq at least partly, keys
+// c0 .. c0 + 31): any visible pair, and every pair visible.  The row bounds of the mask
+// grow by at most one per row, so the first row's low end and the last row's high end
+// decide whether any pair is visible.
+__device__ __forceinline__ bool block_any(const MfaMask& m, int Nq, int r0, int c0) {
+    if (r0 >= Nq || c0 >= m.Nk) return false;
+    const int r1 = min(r0 + 31, Nq - 1);
+    const int64_t c1 = c0 + 31 < m.Nk ? c0 + 31 : m.Nk - 1;
+    return mfa_row_hi(m, r1) >= c0 && mfa_row_lo(m, r0) <= c1;
+}
+__device__ __forceinline__ bool block_all(const MfaMask& m, int Nq, int r0, int c0) {
+    return r0 + 31 < Nq && mfa_tile_full(m, 32, 32, r0 / 32, c0 / 32);
+}
+
+// ---- dK, dV ------------------------------------------------------------------------
+// Workgroup = 128 keys of one (batch, KV head), one wave per 32 keys.  Steps = (query
+// head of the group, 32-row query tile) over the tiles that see any of the 128 keys.
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
+    constexpr int KCH = D / 8;            // 16-byte chunks per row
+    constexpr int NKB = D / 16;           // k-steps over D
+    constexpr int NDB = D / 32;           // 32-row blocks of dK^T / dV^T
+    constexpr int TROWS = 32;             // query rows per step
+    constexpr int TILE = TROWS * D;       // 16-bit elements of a Q or dO tile
+    constexpr int RPB = 64 / KCH;         // rows per 1 KiB block
+    constexpr int LOADS = TROWS / RPB / 4;   // direct loads per wave per tile
+    __shared__ __attribute__((aligned(1024))) uint16_t sv[128 * D];          // V rows
+    __shared__ __attribute__((aligned(1024))) uint16_t sq[2][2 * TILE];      // Q, dO tiles
+    __shared__ __attribute__((aligned(16))) float sl[2][2 * 64];            // lse2, dvec
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g32 = lane >> 5;
+    const int l32 = lane & 31;
+    const int kt = blockIdx.x;
+    const int bk = blockIdx.y;            // b * Hkv + kvh
+    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+    const int k0 = kt * 128;
+    const int kw0 = k0 + wave * 32;       // this wave's first key
+    const size_t kv_base = (size_t)bk * a.Nk * D;
+
+    // V rows of the workgroup's 128 keys -> LDS (rows past Nk read as zero), and this
+    // wave's K^T operand: lane (key l32, k-group g32) holds K[key][16 kb + 8 g32 .. +7]
+    {
+        // (k0 < Nk; a clamp from both sides would become a vector med3 and put the
+        // resource in vector registers)
+        const auto rv = mfa_rsrc(a.v + kv_base + (size_t)k0 * D, (uint32_t)min(a.Nk - k0, 128) * D * 2);
+#pragma unroll
+        for (int i = 0; i < 128 * KCH / kThreads; ++i) {
+            const int slot = (i * 4 + wave) * 64 + lane;     // 16-byte slot of the tile
+            const int row = slot / KCH, phys = slot % KCH;
+            mfa_load16_lds(rv, sv + (i * 4 + wave) * 512, (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2);
+        }
+    }
+    mfa_u32x4 kb_op[NKB];
+    {
+        const auto rk = mfa_rsrc(a.k + kv_base, (uint32_t)a.Nk * D * 2);
+        const uint32_t off = ((uint32_t)(kw0 + l32) * D + g32 * 8) * 2;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kb_op[kb] = mfa_load16(rk, off + kb * 32);
+    }
+
+    // query rows that see any of the 128 keys: [q_lo, q_hi]
+    const MfaMask& m = a.mask;
+    const int off32 = (int)m.off;
+    const int d_lo = m.left < 0 ? INT_MIN : -m.left;
+    const int d_hi = m.right_eff < 0 ? INT_MAX : m.right_eff;
+    const int k1 = min(k0 + 127, a.Nk - 1);
+    int64_t q_lo = 0, q_hi = a.Nq - 1;
+    if (m.right_eff >= 0) q_lo = max((int64_t)0, (int64_t)k0 - m.off - m.right_eff);
+    if (m.left >= 0) q_hi = min((int64_t)a.Nq - 1, (int64_t)k1 - m.off + m.left);
+    const int t_lo = (int)(q_lo / TROWS);
+    const int n_t = q_hi >= q_lo ? (int)(q_hi / TROWS) - t_lo + 1 : 0;
+    const int n_steps = n_t * a.g;
+
+    mfa_f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        dkt[i] = mfa_f32x16{};
+        dvt[i] = mfa_f32x16{};
+    }
+
+    // direct loads of step j: Q and dO rows of tile t (32 rows), lse2 and dvec
+    auto issue = [&](int j, int buf) {
+        const int hh = j / n_t, t = t_lo + j - hh * n_t;
+        const int h = kvh * a.g + hh;
+        const int q0 = t * TROWS;
+        const size_t row0 = ((size_t)(b * a.Hq + h) * a.Nq + q0);
+        const uint32_t bytes = (uint32_t)min(a.Nq - q0, TROWS) * D * 2;   // q0 < Nq
+        const auto rq = mfa_rsrc(a.q + row0 * D, bytes);
+        const auto rd = mfa_rsrc(a.dout + row0 * D, bytes);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int blk = i * 4 + wave;
+            const int row = blk * RPB + lane / KCH, phys = lane % KCH;
+            const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
+            mfa_load16_lds(rq, &sq[buf][blk * 512], off);
+            mfa_load16_lds(rd, &sq[buf][TILE + blk * 512], off);
+        }
+        if (wave == 0) {
+            const uint32_t nb = (uint32_t)min(a.Nq - q0, 64) * 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(mfa_rsrc(a.lse2 + row0, nb),
+                (__attribute__((address_space(3))) void*)&sl[buf][0], 4, (uint32_t)lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(mfa_rsrc(a.dvec + row0, nb),
+                (__attribute__((address_space(3))) void*)&sl[buf][64], 4, (uint32_t)lane * 4, 0, 0, 0);
+        }
+    };
+
+    // per-lane LDS addresses: A-operand rows of S = Q K^T / dP = dO V^T (query row
+    // key_perm(l32), chunk 2 kb + g32); transposing reads of Q^T / dO^T (lane group qg:
+    // columns 16 (qg % 2) .. +15 of a 32-column block, query rows 8 (qg / 2) .. +3 (+4));
+    // B operand of dP (V row of this lane's key, chunk 2 kb + g32)
+    // (the two transposing reads of a k-group are 4 rows apart, where the row swizzle
+    // differs, so each has its own address; 16- and 32-row offsets leave it unchanged)
+    int a_rd[NKB], t_rd[NDB], t_rd4[NDB], v_rd[NKB];
+    {
+        const int row = key_perm(l32);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
+        const int qg = lane >> 4, i = lane & 15;
+        const int trow = 8 * (qg >> 1) + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
+            t_rd[db] = trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
+            t_rd4[db] = (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
+        }
+        const int vrow = wave * 32 + l32;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) v_rd[kb] = vrow * D + swz_rows<KCH>(vrow, 2 * kb + g32) * 8;
+    }
+
+    if (n_steps > 0) issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): V rows, K operand, first tile
+    __syncthreads();
+
+    for (int j = 0; j < n_steps; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < n_steps) issue(j + 1, buf ^ 1);
+        const int hh = j / n_t, t = t_lo + j - hh * n_t;
+        const int q0 = t * TROWS;
+        if (block_any(m, a.Nq, q0, kw0)) {   // uniform per wave
+            const uint16_t* tq = &sq[buf][0];
+            const uint16_t* td = &sq[buf][TILE];
+            mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                s = mfa_mfma32<DT>(lds_read16(tq + a_rd[kb]), kb_op[kb], s);
+                dp = mfa_mfma32<DT>(lds_read16(td + a_rd[kb]), lds_read16(sv + v_rd[kb]), dp);
+            }
+            // register r of this lane: query row q0 + 16 (r / 8) + 8 g32 + r % 8, key kw0 + l32
+            const bool full = block_all(m, a.Nq, q0, kw0);
+            const int key = kw0 + l32;
+            const bool key_ok = key < a.Nk;
+            mfa_u32x4 pp[2], dsp[2];
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) {
+                const int rr = 16 * hk + 8 * g32;   // first of this run's 8 query rows
+                const mfa_f32x4 l0 = lds_read_f4(&sl[buf][rr]), l1 = lds_read_f4(&sl[buf][rr + 4]);
+                const mfa_f32x4 d0 = lds_read_f4(&sl[buf][64 + rr]), d1 = lds_read_f4(&sl[buf][64 + rr + 4]);
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float pv[2], dv2[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = 2 * e2 + u;         // 0..7 within the run
+                        const int r = 8 * hk + e;
+                        const float lse2 = e < 4 ? l0[e] : l1[e - 4];
+                        const float dvv = e < 4 ? d0[e] : d1[e - 4];
+                        // visible iff 0 <= key < Nk, qi < Nq and d_lo <= key - qi - off <= d_hi
+                        // (bitwise, not short-circuit, so that no branch is made); a masked
+                        // pair's exponent is -inf and the exp itself gives 0
+                        const int qi = q0 + rr + e;
+                        const int dd = key - qi - off32;
+                        const bool vis = full | (key_ok & (qi < a.Nq) & (dd >= d_lo) & (dd <= d_hi));
+                        const float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
+                        const float p = mfa_exp2(vis ? x : -MFA_INF);
+                        pv[u] = p;
+                        dv2[u] = p * (dp[r] - dvv);
+                    }
+                    pp[hk][e2] = mfa_pack2<DT>(pv[0], pv[1]);
+                    dsp[hk][e2] = mfa_pack2<DT>(dv2[0], dv2[1]);
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS (k-steps over the two runs of 16 query rows)
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int ofs = hk * 16 * D;
+                    const mfa_u32x2 a0 = lds_read_tr(td + t_rd[db] + ofs), a1 = lds_read_tr(td + t_rd4[db] + ofs);
+                    dvt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, pp[hk], dvt[db]);
+                    const mfa_u32x2 b0 = lds_read_tr(tq + t_rd[db] + ofs), b1 = lds_read_tr(tq + t_rd4[db] + ofs);
+                    dkt[db] = mfa_mfma32<DT>(mfa_u32x4{b0[0], b0[1], b1[0], b1[1]}, dsp[hk], dkt[db]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next step's tiles landed
+        block_barrier();
+    }
+
+    // write dK = scale (dK^T)^T and dV: register r of block db holds d = 32 db + 8 (r / 4)
+    // + 4 g32 + r % 4 of key kw0 + l32; runs of 4 consecutive d are one 8-byte store
+    const int key = kw0 + l32;
+    if (key < a.Nk) {
+        uint16_t* dkp = a.dk + kv_base + (size_t)key * D;
+        uint16_t* dvp = a.dv + kv_base + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * g32;
+                mfa_u32x2 wk, wv;
+                wk[0] = mfa_pack2<DT>(dkt[db][4 * r4] * a.scale, dkt[db][4 * r4 + 1] * a.scale);
+                wk[1] = mfa_pack2<DT>(dkt[db][4 * r4 + 2] * a.scale, dkt[db][4 * r4 + 3] * a.scale);
+                wv[0] = mfa_pack2<DT>(dvt[db][4 * r4], dvt[db][4 * r4 + 1]);
+                wv[1] = mfa_pack2<DT>(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]);
+                *(mfa_u32x2*)(dkp + d) = wk;
+                *(mfa_u32x2*)(dvp + d) = wv;
+            }
+    }
+}
+
+// ---- dQ ----------------------------------------------------------------------------
+// Workgroup = 128 query rows of one (batch, head), one wave per 32 rows; K and V tiles of
+// 64 keys over the key tiles the query tile sees (the forward's tile range).
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
+    constexpr int KCH = D / 8;
+    constexpr int NKB = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int BN = 64;
+    constexpr int TILE = BN * D;
+    constexpr int RPB = 64 / KCH;
+    constexpr int LOADS = BN / RPB / 4;
+    __shared__ __attribute__((aligned(1024))) uint16_t st[2][2 * TILE];   // K, V tiles
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g32 = lane >> 5;
+    const int l32 = lane & 31;
+    const int qt = blockIdx.x;
+    const int bh = blockIdx.y;
+    const int b = bh / a.Hq, h = bh - b * a.Hq;
+    const int kvh = h / a.g;
+    const int qw0 = qt * 128 + wave * 32;   // this wave's first query row
+    const int qrow = qw0 + l32;
+    const size_t q_base = (size_t)bh * a.Nq * D;
+    const size_t kv_base = (size_t)(b * a.Hkv + kvh) * a.Nk * D;
+
+    // Q^T and dO^T operands: lane (query l32, k-group g32) holds row[16 kb + 8 g32 .. +7]
+    mfa_u32x4 qb[NKB], db_op[NKB];
+    {
+        const auto rq = mfa_rsrc(a.q + q_base, (uint32_t)a.Nq * D * 2);
+        const auto rd = mfa_rsrc(a.dout + q_base, (uint32_t)a.Nq * D * 2);
+        const uint32_t off = ((uint32_t)qrow * D + g32 * 8) * 2;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            qb[kb] = mfa_load16(rq, off + kb * 32);
+            db_op[kb] = mfa_load16(rd, off + kb * 32);
+        }
+    }
+    const bool qvalid = qrow < a.Nq;
+    const float lse2 = qvalid ? a.lse2[(size_t)bh * a.Nq + qrow] : MFA_INF;
+    const float dvv = qvalid ? a.dvec[(size_t)bh * a.Nq + qrow] : 0.f;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    const MfaMask& m = a.mask;
+    const int64_t rlo64 = mfa_row_lo(m, qrow), rhi64 = mfa_row_hi(m, qrow);
+    const int row_lo = rlo64 > a.Nk ? a.Nk : (int)rlo64;
+    const int row_hi = rhi64 < -1 ? -1 : (int)rhi64;
+
+    int t_lo, t_hi;
+    mfa_tile_range(m, a.Nq, 128, BN, qt, &t_lo, &t_hi);
+    const int n = t_hi - t_lo;
+
+    mfa_f32x16 dqt[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqt[i] = mfa_f32x16{};
+
+    auto issue = [&](int kt, int buf) {
+        const int kk0 = kt * BN;
+        const uint32_t bytes = (uint32_t)max(a.Nk - kk0, 0) * D * 2;
+        const auto rk = mfa_rsrc(a.k + kv_base + (size_t)kk0 * D, bytes);
+        const auto rv = mfa_rsrc(a.v + kv_base + (size_t)kk0 * D, bytes);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int blk = i * 4 + wave;
+            const int row = blk * RPB + lane / KCH, phys = lane % KCH;
+            const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
+            mfa_load16_lds(rk, &st[buf][blk * 512], off);
+            mfa_load16_lds(rv, &st[buf][TILE + blk * 512], off);
+        }
+    };
+
+    // A-operand rows of S^T = K Q^T and dP^T = V dO^T (key row key_perm(l32) of a 32-key
+    // block, chunk 2 kb + g32); transposing reads of K^T (lane group qg: columns 16 (qg % 2)
+    // .. +15 of a 32-column block, keys 8 (qg / 2) .. +3 (+4))
+    int a_rd[NKB], t_rd[NDB], t_rd4[NDB];
+    {
+        const int row = key_perm(l32);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
+        const int qg = lane >> 4, i = lane & 15;
+        const int trow = 8 * (qg >> 1) + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
+            t_rd[db] = trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
+            t_rd4[db] = (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
+        }
+    }
+
+    if (n > 0) issue(t_lo, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+        const int buf = j & 1;
+        const int kt = t_lo + j;
+        if (j + 1 < n) issue(kt + 1, buf ^ 1);
+        const uint16_t* tk = &st[buf][0];
+        const uint16_t* tv = &st[buf][TILE];
+#pragma unroll
+        for (int nb = 0; nb < BN / 32; ++nb) {
+            const int c0 = kt * BN + nb * 32;
+            if (!block_any(m, a.Nq, qw0, c0)) continue;   // uniform per wave
+            const bool full = block_all(m, a.Nq, qw0, c0);
+            mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                s = mfa_mfma32<DT>(lds_read16(tk + a_rd[kb] + nb * 32 * D), qb[kb], s);
+                dp = mfa_mfma32<DT>(lds_read16(tv + a_rd[kb] + nb * 32 * D), db_op[kb], dp);
+            }
+            // register r: key c0 + 16 (r / 8) + 8 g32 + r % 8, query row qrow
+            mfa_u32x4 dsp[2];
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float w[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int r = 8 * hk + 2 * e2 + u;
+                        const int key = c0 + 16 * hk + 8 * g32 + 2 * e2 + u;
+                        const bool vis = full | (qvalid & (key >= row_lo) & (key <= row_hi));
+                        const float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
+                        const float p = mfa_exp2(vis ? x : -MFA_INF);
+                        w[u] = p * (dp[r] - dvv);
+                    }
+                    dsp[hk][e2] = mfa_pack2<DT>(w[0], w[1]);
+                }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int ofs = (nb * 32 + hk * 16) * D;
+                    const mfa_u32x2 a0 = lds_read_tr(tk + t_rd[db] + ofs), a1 = lds_read_tr(tk + t_rd4[db] + ofs);
+                    dqt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, dsp[hk], dqt[db]);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        block_barrier();
+    }
+
+    if (qvalid) {
+        uint16_t* dqp = a.dq + q_base + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * g32;
+                mfa_u32x2 w;
+                w[0] = mfa_pack2<DT>(dqt[db][4 * r4] * a.scale, dqt[db][4 * r4 + 1] * a.scale);
+                w[1] = mfa_pack2<DT>(dqt[db][4 * r4 + 2] * a.scale, dqt[db][4 * r4 + 3] * a.scale);
+                *(mfa_u32x2*)(dqp + d) = w;
+            }
+    }
+}
+
+template <int D, int DT>
+int launch(const BwdArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
+    const long long rows = (long long)a.B * a.Hq * a.Nq;
+    const dim3 g0((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)));
+    hipLaunchKernelGGL((mfa_bwd_prep_kernel<D, DT>), g0, dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
+    const dim3 g1((unsigned)((a.Nk + 127) / 128), (unsigned)(a.B * a.Hkv));
+    hipLaunchKernelGGL((mfa_bwd_dkv_kernel<D, DT>), g1, dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
+    const dim3 g2((unsigned)((a.Nq + 127) / 128), (unsigned)(a.B * a.Hq));
+    hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_bwd_dkv_kernel+mfa_bwd_dq_kernel<D=%d,%s>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16");
+    info->grid[0] = (int)g1.x;
+    info->grid[1] = (int)g1.y;
+    info->grid[2] = 1;
+    info->block = kThreads;
+    info->waves = 4;
+    info->BM = 32;
+    info->BN = 128;
+    info->n_launches = 3;
+    return MFA_OK;
+}
+
+}  // namespace
+
+int mfa_bwd_launch(const MfaBwdProblem& p, hipStream_t stream, mfa_dispatch_info* info) {
+    BwdArgs a;
+    a.q = (const uint16_t*)p.q;
+    a.k = (const uint16_t*)p.k;
+    a.v = (const uint16_t*)p.v;
+    a.o = (const uint16_t*)p.out;
+    a.dout = (const uint16_t*)p.dout;
+    a.lse = p.lse;
+    a.dq = (uint16_t*)p.dq;
+    a.dk = (uint16_t*)p.dk;
+    a.dv = (uint16_t*)p.dv;
+    a.lse2 = (float*)p.workspace;
+    a.dvec = a.lse2 + (size_t)p.B * p.Hq * p.Nq;
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.Nq = p.Nq;
+    a.Nk = p.Nk;
+    a.g = p.Hq / p.Hkv;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * 1.4426950408889634f;
+    a.mask = mfa_make_mask(p.Nq, p.Nk, p.causal, p.left, p.right);
+    if (p.D == 128)
+        return p.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, info) : launch<128, MFA_DT_BF16>(a, stream, info);
+    return p.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, info) : launch<64, MFA_DT_BF16>(a, stream, info);
+}

@@ -59,6 +59,7 @@
 #include "mfa_device.h"
 #include "mfa_geometry.h"
 #include "mfa_internal.h"
+#include "mfa_tile.h"
 
 namespace {
 
@@ -104,65 +105,14 @@ struct FwdArgs {
 
 constexpr int kMaxList = 2048;   // visited key tiles a block-sparse query tile may list
 
-template <int N>
-struct MfaInt {
-    static constexpr int value = N;
-};
-
-// K row (within a 32-key block) fed to A-operand row i.
-__device__ __forceinline__ int key_perm(int i) {
-    return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
-}
-
 template <int D>
 struct Tile {
     static constexpr int KCH = D / 8;                   // 16-byte chunks per row
     static constexpr int ELEMS = kBN * D;               // 16-bit elements per K or V tile
     static constexpr int LOADS = kBN * KCH / kGroupThreads;  // 16-byte direct loads per thread
-    // XOR swizzles on 16-byte chunks (rows are unpadded so that a wave's direct load
-    // fills 1 KiB of consecutive LDS).  K: the 16 rows one MFMA operand read touches at
-    // a logical chunk land in 16 distinct bank groups.  V: the 4 rows x 32 bytes of a
-    // transposing read land in distinct banks.
-    __device__ static __forceinline__ int k_phys(int row, int ch) {
-        return (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
-    }
-    __device__ static __forceinline__ int v_phys(int row, int ch) {
-        return (KCH == 16) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
-    }
+    __device__ static __forceinline__ int k_phys(int row, int ch) { return swz_rows<KCH>(row, ch); }
+    __device__ static __forceinline__ int v_phys(int row, int ch) { return swz_tr<KCH>(row, ch); }
 };
-
-// Workgroup barrier of the tile pipeline.  __syncthreads() also fences memory, which
-// waits for every outstanding load, including direct-to-LDS copies meant to stay in
-// flight; here each wave has already waited for the copies the next stage reads
-// (vmcnt), waits for its own LDS reads to return (lgkmcnt(0): no buffer is refilled
-// while a read of it is pending) and then meets the others.  The empty asm statements
-// keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// LDS operand reads of the key loop.  The restrict-qualified parameter gives each read
-// an alias scope of its own; without one the compiler orders every LDS read after all
-// direct-to-LDS copies still in flight (a vmcnt(0) before the read), which the tile
-// pipeline already orders itself with vmcnt waits and barriers.
-__device__ __forceinline__ mfa_u32x4 lds_read16(const uint16_t* __restrict__ p) {
-    typedef __attribute__((address_space(3))) const mfa_u32x4 lds_u32x4;
-    return *(lds_u32x4*)p;
-}
-__device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
-    return mfa_lds_read_tr16(p);
-}
-__device__ __forceinline__ int lds_read_i32(const int* __restrict__ p) {
-    typedef __attribute__((address_space(3))) const int lds_i32;
-    return *(lds_i32*)p;
-}
-__device__ __forceinline__ mfa_f32x4 lds_read_f4(const float* __restrict__ p) {
-    typedef __attribute__((address_space(3))) const mfa_f32x4 lds_f32x4;
-    return *(lds_f32x4*)p;
-}
 
 // Sequence s of a pack: tokens [cu[s], cu[s+1]) clamped into [0, total] and to at most
 // max_len of them, so that every access stays inside the packed tensors whatever the

@@ -50,6 +50,23 @@ struct MfaDecodeProblem {
     int multi;           // 1: the multi-token kernel (mfa_decode_paged_multi)
 };
 
+struct MfaBwdProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    void* workspace;     // 2 * B * Hq * Nq floats
+    int B, Hq, Hkv, Nq, Nk, D;
+    float scale;
+    int causal, left, right;
+    int dtype;
+};
+
 // Compute units of the current device (cached per device).
 int mfa_num_cus();
 
@@ -57,6 +74,8 @@ int mfa_fwd_bm();
 int mfa_fwd_bn(int D);
 int mfa_fwd_groups(long long q_tiles, int Hq, int num_cus);
 int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
+
+int mfa_bwd_launch(const MfaBwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
 
 int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits);
 int mfa_decode_launch(const MfaDecodeProblem& p, hipStream_t stream, mfa_dispatch_info* info);

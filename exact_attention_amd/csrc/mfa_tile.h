@@ -1,0 +1,68 @@
+// Tile-level building blocks shared by the forward and backward kernels: the row order
+// fed to a 32x32x16 MFMA A operand, the XOR swizzles of LDS tiles, LDS operand reads with
+// their own alias scope, and the bare workgroup barrier of the tile pipelines.
+#pragma once
+#include "mfa_device.h"
+
+namespace {
+
+template <int N>
+struct MfaInt {
+    static constexpr int value = N;
+};
+
+// Row of a 32-row block fed to A-operand row i.  With this order, accumulator register r
+// of lane half g (lane / 32) holds row 16 * (r / 8) + 8 * g + r % 8: every lane then owns
+// runs of 8 consecutive rows, which is the k-group layout of an operand of the next
+// product (two k-steps of 16).
+__device__ __forceinline__ int key_perm(int i) {
+    return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
+}
+
+// XOR swizzles on the 16-byte chunks of an LDS tile with KCH chunks per row (rows are not
+// padded, so that a wave's direct load fills 1 KiB of consecutive LDS).  Row reads: the
+// 16 rows one MFMA operand read touches at a logical chunk land in 16 distinct bank
+// groups.  Transposing reads: the 4 rows x 32 bytes of one read land in distinct banks.
+template <int KCH>
+__device__ __forceinline__ int swz_rows(int row, int ch) {
+    return (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
+}
+template <int KCH>
+__device__ __forceinline__ int swz_tr(int row, int ch) {
+    return (KCH == 16) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
+}
+
+// Workgroup barrier of the tile pipelines.  __syncthreads() also fences memory, which
+// waits for every outstanding load, including direct-to-LDS copies meant to stay in
+// flight; here each wave has already waited for the copies the next stage reads
+// (vmcnt), waits for its own LDS reads to return (lgkmcnt(0): no buffer is refilled
+// while a read of it is pending) and then meets the others.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS operand reads.  The restrict-qualified parameter gives each read an alias scope of
+// its own; without one the compiler orders every LDS read after all direct-to-LDS copies
+// still in flight (a vmcnt(0) before the read), which the tile pipelines already order
+// themselves with vmcnt waits and barriers.
+__device__ __forceinline__ mfa_u32x4 lds_read16(const uint16_t* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const mfa_u32x4 lds_u32x4;
+    return *(lds_u32x4*)p;
+}
+__device__ __forceinline__ mfa_u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
+    return mfa_lds_read_tr16(p);
+}
+__device__ __forceinline__ int lds_read_i32(const int* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const int lds_i32;
+    return *(lds_i32*)p;
+}
+__device__ __forceinline__ mfa_f32x4 lds_read_f4(const float* __restrict__ p) {
+    typedef __attribute__((address_space(3))) const mfa_f32x4 lds_f32x4;
+    return *(lds_f32x4*)p;
+}
+
+}  // namespace

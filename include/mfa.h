@@ -13,6 +13,7 @@
  *                     "Sliding window", "Native GQA").
  *   mfa_fwd_ext       the same with softcap, ALiBi, an additive key bias and a
  *                     block-sparse mask (mlx-mfa "Softcap", "ALiBi", "Block-sparse").
+ *   mfa_bwd           the backward pass of mfa_fwd (dQ, dK, dV from the saved LSE).
  *   mfa_fwd_varlen    the same forward over packed sequences of different lengths
  *                     delimited by cu_seqlens (mlx-mfa "Variable-length"), each
  *                     sequence masked on its own lengths.
@@ -236,6 +237,29 @@ int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages
                          int max_pages_per_seq, float scale,
                          int causal, int win_left, int win_right, int dtype, void* stream);
 
+/* Bytes of workspace mfa_bwd needs (0 if an argument is < 1). */
+size_t mfa_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/* Backward pass of mfa_fwd: the gradients of O with respect to Q, K and V for an
+ * upstream gradient dO (the FlashAttention-2 backward of the mlx-bun flash-attention.ts
+ * page: D-vector, dK/dV and dQ passes recomputing P from the saved LSE).  With P the
+ * forward's probabilities (masked keys have P = 0):
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * and with grouped query heads dK, dV of a KV head sum over its Hq / Hkv query heads.
+ *   q, out, dout, dq  [B, Hq, Nq, D] dtype     k, v, dk, dv  [B, Hkv, Nk, D] dtype
+ *   lse               [B, Hq, Nq] float32 as written by mfa_fwd for the same arguments
+ *   scale, causal, win_left, win_right: as passed to mfa_fwd
+ *   workspace         at least mfa_bwd_workspace_bytes(B, Hq, Nq) bytes of device memory
+ *                     (contents on entry do not matter)
+ * dq, dk, dv are written in full (zeros where no visible pair contributes), rounded to
+ * nearest even from fp32 accumulation.  The result is deterministic: no atomics.
+ * Errors: those of mfa_fwd, plus MFA_ERR_WORKSPACE. */
+int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+            int causal, int win_left, int win_right, int dtype, void* stream);
+
 /* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).
  * Returns 0 if the arguments are invalid. */
 size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
@@ -298,13 +322,13 @@ int mfa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pag
                            int max_pages_per_seq, float scale, int num_splits,
                            void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
-/* What the last successful launch on this host thread ran/* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
+/* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
  * record: backend, operation, selection and split fields). */
 typedef struct {
     char kernel[96];      /* kernel name of the main launch */
     int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward,
                              4 = packed queries over a paged cache, 5 = multi-token decode,
-                             6 = forward with modifiers / block mask */
+                             6 = forward with modifiers / block mask, 7 = backward */
     int BM, BN, waves;    /* forward tile configuration */
     int grid[3];          /* main launch grid */
     int block;            /* threads per workgroup */

@@ -213,6 +213,33 @@ def test_fwd_ext_null_args():
                                 None) == -1
 
 
+def bwd(**kw):
+    a = dict(q=A1, k=A2, v=A3, o=A4, do=A5, lse=0x60000, dq=0x70000, dk=0x80000, dv=0x90000,
+             ws=0xa0000, ws_bytes=1 << 20, B=1, Hq=4, Hkv=2, Nq=64, Nk=80, D=128, scale=0.1,
+             causal=1, left=-1, right=-1, dtype=1, stream=None)
+    a.update(kw)
+    return ea.lib().mfa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["ws"], a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                            a["Nk"], a["D"], a["scale"], a["causal"], a["left"], a["right"],
+                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(do=None), -1), (dict(lse=None), -1),
+    (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1), (dict(dtype=3), -5),
+    (dict(D=80), -4), (dict(Nq=0), -2), (dict(Hq=3), -3), (dict(left=-4), -6),
+    (dict(scale=float("nan")), -7), (dict(ws=None), -8), (dict(ws_bytes=2 * 4 * 64 * 4 - 1), -8),
+    (dict(dk=0x80008), -12), (dict(lse=0x60002), -12), (dict(causal=5), -13),
+])
+def test_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    assert ea.lib().mfa_bwd_workspace_bytes(2, 8, 4096) == 2 * 2 * 8 * 4096 * 4
+    assert ea.lib().mfa_bwd_workspace_bytes(0, 8, 4096) == 0
+
+
 def dec(**kw):
     a = dict(q=A1, kp=A2, vp=A3, bt=A4, sl=A5, out=0x60000, lse=0x70000, B=2, Hq=8, Hkv=2, D=128,
              page_size=16, num_pages=10, max_pages=4, scale=0.1, num_splits=0, ws=0x80000,
