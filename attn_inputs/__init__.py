@@ -76,6 +76,12 @@ def dense_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, dtype: str
     return DenseInputs(q, k, v, dtype)
 
 
+def grad_inputs(B: int, Hq: int, Nq: int, D: int, dtype: str, seed: int) -> np.ndarray:
+    """Upstream gradient dO: standard normal, rounded to `dtype`; uint16 bits [B, Hq, Nq, D]."""
+    rng = np.random.default_rng(seed)
+    return _normal_bits(rng, (B, Hq, Nq, D), dtype)
+
+
 @dataclass
 class PagedInputs:
     q: np.ndarray            # uint16 bits [B, Hq, D]
@@ -310,6 +316,10 @@ CONFIGS = {
     9: dict(name="block_sparse_causal_prefill", B=1, Hq=16, Hkv=16, Nq=16384, Nk=16384, D=128,
             dtype=F16, causal=True, left=-1, right=-1, block_q=128, block_k=128, density=0.25,
             seed=109),
+    # training step after the prefill: the backward over the dense causal prefill shape,
+    # in bf16 (the mlx-bun page's backward; upstream gradient from grad_inputs)
+    10: dict(name="dense_causal_backward", B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128,
+             dtype=BF16, causal=True, left=-1, right=-1, seed=110),
     7: dict(name="paged_chunked_prefill", B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True,
             left=-1, right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
             ctx_hi=16384, seed=107),

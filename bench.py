@@ -13,7 +13,9 @@ chunked prefill over the paged cache (``mfa_fwd_varlen_paged``, 8 sequences, new
 of 512..2048 tokens after 1024..16384 cached ones), and the 4-token verification decode
 (``mfa_decode_paged_multi`` over the decode workload's cache shape, HBM GB/s), and the
 block-sparse causal prefill (``mfa_fwd_ext`` with a 25%-dense 128 x 128 block mask,
-TFLOP/s over the computed visible pairs).
+TFLOP/s over the computed visible pairs), and the backward over the dense causal prefill
+shape in bf16 (``mfa_bwd``: prep, dK/dV and dQ launches; TFLOP/s at 10*D FLOP per visible
+pair).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
 workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
@@ -21,7 +23,7 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8,9] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8,9,10] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -388,6 +390,47 @@ def bench_sparse(step, steps):
     }
 
 
+def setup_backward():
+    """Device inputs, the forward's O and LSE, and one step (one mfa_bwd call) of the
+    backward over the dense causal prefill shape."""
+    import torch
+    import exact_attention_amd as ea
+    c = A.config(10)
+    x = A.config_inputs(10)
+    q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
+    do = to_dev(A.grad_inputs(c["B"], c["Hq"], c["Nq"], c["D"], c["dtype"], c["seed"] + 1000),
+                c["dtype"])
+    out, lse = ea.mfa_fwd(q, k, v, scale=c["scale"], causal=c["causal"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(int(ea.lib().mfa_bwd_workspace_bytes(c["B"], c["Hq"], c["Nq"])),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        ea.mfa_bwd(q, k, v, out, do, lse, scale=c["scale"], causal=c["causal"], dq=dq, dk=dk,
+                   dv=dv, workspace=ws)
+
+    return step
+
+
+def bench_backward(step, steps):
+    import exact_attention_amd as ea
+    c = A.config(10)
+    ms, wall = time_calls(step, steps)
+    info = ea.mfa_last_dispatch()
+    # 10 D FLOP per visible pair: the five products S = Q K^T, dP = dO V^T, dV = P^T dO,
+    # dQ = dS K and dK = dS^T Q (2 D each)
+    flop = 10.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], -1, -1) * c["B"] * c["Hq"]
+    tf = flop / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['Nq']} D={c['D']} "
+                    f"{c['dtype']} causal=1 (prep + dK/dV + dQ launches)",
+        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_MFMA_F16, "traffic": None},
+        "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
+    }
+
+
 def cpu_baseline(budget_s=10.0):
     """The float64 oracle on this host over whole heads of the dense causal prefill."""
     import oracle
@@ -421,7 +464,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5,6,7,8,9")
+    ap.add_argument("--workloads", default="2,3,4,5,6,7,8,9,10")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -440,7 +483,8 @@ def main():
     wl = [int(s) for s in args.workloads.split(",") if s]
     if 2 not in wl:
         wl = [2] + wl
-    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi, 9: setup_sparse}
+    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi, 9: setup_sparse,
+             10: setup_backward}
     steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
@@ -460,6 +504,8 @@ def main():
             res[i] = bench_multi(steps[i], args.steps)
         elif i == 9:
             res[i] = bench_sparse(steps[i], args.steps)
+        elif i == 10:
+            res[i] = bench_backward(steps[i], args.steps)
         else:
             res[i] = bench_prefill(i, steps[i], args.steps)
         print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)

@@ -26,7 +26,33 @@
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kThreads = 256;   // 4 waves (prep)
+constexpr int kThreads8 = 512;  // 8 waves (dK/dV and dQ)
+
+// Offset of the second transposing read of a k-group, 4 rows below the first (t_rd[db]).
+// The row swizzle flips one chunk bit between the two rows: with 16 chunks a row that bit
+// is bit 2 of the chunk index, set exactly in the odd 32-column blocks, so the distance is
+// the constant 4 D -+ 32 and needs no register; with 8 chunks it depends on the lane and
+// the precomputed t_rd4 is used.
+template <int D>
+__device__ __forceinline__ int tr4_addr(const int* t_rd, const int* t_rd4, int db) {
+    if constexpr (D == 128) return t_rd[db] + 4 * D + ((db & 1) ? -32 : 32);
+    else return t_rd4[db];
+}
+
+// Workgroups are handed to the 8 XCDs in turn (id % 8).  When the count divides evenly,
+// renumber them so that XCD x runs the contiguous logical range [x n / 8, (x + 1) n / 8):
+// the workgroups of one (batch, head) then share that XCD's L2, and each XCD still starts
+// its range in order.
+__device__ __forceinline__ int xcd_logical_id(int n) {
+    const int id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+    return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
+__device__ __forceinline__ void lds_write_f4(float* __restrict__ p, mfa_f32x4 v) {
+    typedef __attribute__((address_space(3))) mfa_f32x4 lds_f32x4;
+    *(lds_f32x4*)p = v;
+}
 
 struct BwdArgs {
     const uint16_t* q;
@@ -95,44 +121,62 @@ __device__ __forceinline__ bool block_all(const MfaMask& m, int Nq, int r0, int 
 }
 
 // ---- dK, dV ------------------------------------------------------------------------
-// Workgroup = 128 keys of one (batch, KV head), one wave per 32 keys.  Steps = (query
-// head of the group, 32-row query tile) over the tiles that see any of the 128 keys.
+// Workgroup = 128 keys of one (batch, KV head), 8 waves: wave w owns the 32 keys
+// 32 (w % 4) .. +31 and the steps of parity w / 4, so that the two 4-wave halves walk
+// alternate steps side by side (the heaviest workgroup of a causal mask then takes half as
+// long) and add their partial dK / dV through LDS at the end, in a fixed order.  Steps =
+// (query head of the group, 32-row query tile) over the tiles that see any of the 128 keys.
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
     constexpr int KCH = D / 8;            // 16-byte chunks per row
     constexpr int NKB = D / 16;           // k-steps over D
     constexpr int NDB = D / 32;           // 32-row blocks of dK^T / dV^T
     constexpr int TROWS = 32;             // query rows per step
     constexpr int TILE = TROWS * D;       // 16-bit elements of a Q or dO tile
     constexpr int RPB = 64 / KCH;         // rows per 1 KiB block
-    constexpr int LOADS = TROWS / RPB / 4;   // direct loads per wave per tile
-    __shared__ __attribute__((aligned(1024))) uint16_t sv[128 * D];          // V rows
-    __shared__ __attribute__((aligned(1024))) uint16_t sq[2][2 * TILE];      // Q, dO tiles
-    __shared__ __attribute__((aligned(16))) float sl[2][2 * 64];            // lse2, dvec
+    constexpr int LOADS = TROWS / RPB / 4;   // direct loads per wave per tile (4 waves a step)
+    // V in the register layout of the B operand of dP: 1 KiB block (32-key block, k-step)
+    // holds lane (key l32, k-group g32)'s 16 bytes at 16 * lane
+    __shared__ __attribute__((aligned(1024))) uint16_t sv[128 * D];
+    // the two pipeline buffers are separate objects, picked by a compile-time index, so
+    // that the compiler sees that a copy into one never touches reads from the other
+    // (per buffer: parity 0 Q, dO, then parity 1 Q, dO; lse2 and dvec likewise)
+    __shared__ __attribute__((aligned(1024))) uint16_t sq0[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sq1[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float sl0[2 * 2 * 64];
+    __shared__ __attribute__((aligned(16))) float sl1[2 * 2 * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kblk = wave & 3;            // key block of this wave
+    const int par = wave >> 2;            // step parity of this wave
+    const int pw = wave & 3;              // wave index within its half
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
-    const int kt = blockIdx.x;
-    const int bk = blockIdx.y;            // b * Hkv + kvh
+    const MfaMask& m = a.mask;
+    const int nkt = (a.Nk + 127) >> 7;
+    const int lid = xcd_logical_id(nkt * a.B * a.Hkv);
+    const int bk = lid / nkt;             // b * Hkv + kvh
+    // causal masks give the low key tiles the most query rows: they start first (a mask
+    // bounded on the left only is the mirror image)
+    const int kt = (m.left >= 0 && m.right_eff < 0) ? nkt - 1 - (lid - bk * nkt) : lid - bk * nkt;
     const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
     const int k0 = kt * 128;
-    const int kw0 = k0 + wave * 32;       // this wave's first key
+    const int kw0 = k0 + kblk * 32;       // this wave's first key
     const size_t kv_base = (size_t)bk * a.Nk * D;
 
-    // V rows of the workgroup's 128 keys -> LDS (rows past Nk read as zero), and this
-    // wave's K^T operand: lane (key l32, k-group g32) holds K[key][16 kb + 8 g32 .. +7]
+    // V of the workgroup's 128 keys -> LDS in operand layout (keys past Nk read as zero),
+    // and this wave's K^T operand: lane (key l32, k-group g32) holds K[key][16 kb + 8 g32 .. +7]
     {
         // (k0 < Nk; a clamp from both sides would become a vector med3 and put the
         // resource in vector registers)
         const auto rv = mfa_rsrc(a.v + kv_base + (size_t)k0 * D, (uint32_t)min(a.Nk - k0, 128) * D * 2);
 #pragma unroll
-        for (int i = 0; i < 128 * KCH / kThreads; ++i) {
-            const int slot = (i * 4 + wave) * 64 + lane;     // 16-byte slot of the tile
-            const int row = slot / KCH, phys = slot % KCH;
-            mfa_load16_lds(rv, sv + (i * 4 + wave) * 512, (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2);
+        for (int i = 0; i < 128 * KCH / kThreads8; ++i) {
+            const int blk = i * 8 + wave;                     // 32-key block * NKB + k-step
+            const int row = (blk / NKB) * 32 + l32, col = (blk % NKB) * 16 + g32 * 8;
+            mfa_load16_lds(rv, sv + blk * 512, (uint32_t)(row * D + col) * 2);
         }
     }
     mfa_u32x4 kb_op[NKB];
@@ -144,7 +188,6 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
     }
 
     // query rows that see any of the 128 keys: [q_lo, q_hi]
-    const MfaMask& m = a.mask;
     const int off32 = (int)m.off;
     const int d_lo = m.left < 0 ? INT_MIN : -m.left;
     const int d_hi = m.right_eff < 0 ? INT_MAX : m.right_eff;
@@ -155,6 +198,11 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
     const int t_lo = (int)(q_lo / TROWS);
     const int n_t = q_hi >= q_lo ? (int)(q_hi / TROWS) - t_lo + 1 : 0;
     const int n_steps = n_t * a.g;
+    const int n_iter = (n_steps + 1) >> 1;   // iteration i: steps 2 i and 2 i + 1
+    // step j = (query head hh of the group, tile): the tiles of a head are walked from the
+    // last down, so that under a causal mask every key tile of the head reads the same
+    // query tiles at about the same time (they are shared through L2)
+    auto step_tile = [&](int j, int hh) { return t_lo + n_t - 1 - (j - hh * n_t); };
 
     mfa_f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -163,9 +211,15 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
         dvt[i] = mfa_f32x16{};
     }
 
-    // direct loads of step j: Q and dO rows of tile t (32 rows), lse2 and dvec
-    auto issue = [&](int j, int buf) {
-        const int hh = j / n_t, t = t_lo + j - hh * n_t;
+    // direct loads of this half's step of iteration i (when it exists): Q and dO rows of
+    // tile t (32 rows), lse2 and dvec
+    const int pofs = par * 2 * TILE;      // this half's tiles within a buffer
+    auto issue = [&](int i, auto bufc) {
+        uint16_t* dst = (decltype(bufc)::value == 0 ? sq0 : sq1) + pofs;
+        float* dl = (decltype(bufc)::value == 0 ? sl0 : sl1) + par * 128;
+        const int j = 2 * i + par;
+        if (j >= n_steps) return;
+        const int hh = j / n_t, t = step_tile(j, hh);
         const int h = kvh * a.g + hh;
         const int q0 = t * TROWS;
         const size_t row0 = ((size_t)(b * a.Hq + h) * a.Nq + q0);
@@ -173,74 +227,74 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
         const auto rq = mfa_rsrc(a.q + row0 * D, bytes);
         const auto rd = mfa_rsrc(a.dout + row0 * D, bytes);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int blk = i * 4 + wave;
+        for (int l = 0; l < LOADS; ++l) {
+            const int blk = l * 4 + pw;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
             const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
-            mfa_load16_lds(rq, &sq[buf][blk * 512], off);
-            mfa_load16_lds(rd, &sq[buf][TILE + blk * 512], off);
+            mfa_load16_lds(rq, dst + blk * 512, off);
+            mfa_load16_lds(rd, dst + TILE + blk * 512, off);
         }
-        if (wave == 0) {
+        if (pw == 0) {
             const uint32_t nb = (uint32_t)min(a.Nq - q0, 64) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(mfa_rsrc(a.lse2 + row0, nb),
-                (__attribute__((address_space(3))) void*)&sl[buf][0], 4, (uint32_t)lane * 4, 0, 0, 0);
+                (__attribute__((address_space(3))) void*)dl, 4, (uint32_t)lane * 4, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(mfa_rsrc(a.dvec + row0, nb),
-                (__attribute__((address_space(3))) void*)&sl[buf][64], 4, (uint32_t)lane * 4, 0, 0, 0);
+                (__attribute__((address_space(3))) void*)(dl + 64), 4, (uint32_t)lane * 4, 0, 0, 0);
         }
     };
 
     // per-lane LDS addresses: A-operand rows of S = Q K^T / dP = dO V^T (query row
     // key_perm(l32), chunk 2 kb + g32); transposing reads of Q^T / dO^T (lane group qg:
     // columns 16 (qg % 2) .. +15 of a 32-column block, query rows 8 (qg / 2) .. +3 (+4));
-    // B operand of dP (V row of this lane's key, chunk 2 kb + g32)
-    // (the two transposing reads of a k-group are 4 rows apart, where the row swizzle
-    // differs, so each has its own address; 16- and 32-row offsets leave it unchanged)
-    int a_rd[NKB], t_rd[NDB], t_rd4[NDB], v_rd[NKB];
+    // B operand of dP: this lane's 16 bytes of block (kblk, kb) of the V operand layout
+    // (offsets within a buffer, this half's tiles included; the two transposing reads of a
+    // k-group are 4 rows apart, where the row swizzle differs: see tr4_delta)
+    int a_rd[NKB], t_rd[NDB], t_rd4[NDB];
     {
         const int row = key_perm(l32);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
+        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = pofs + row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
         const int qg = lane >> 4, i = lane & 15;
         const int trow = 8 * (qg >> 1) + (i >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
-            t_rd[db] = trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
-            t_rd4[db] = (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
+            t_rd[db] = pofs + trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
+            t_rd4[db] = pofs + (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
         }
-        const int vrow = wave * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) v_rd[kb] = vrow * D + swz_rows<KCH>(vrow, 2 * kb + g32) * 8;
     }
+    const int v_rd = kblk * NKB * 512 + lane * 8;
 
-    if (n_steps > 0) issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): V rows, K operand, first tile
+    if (n_iter > 0) issue(0, MfaInt<0>{});
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): V rows, K operand, first tiles
     __syncthreads();
 
-    for (int j = 0; j < n_steps; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < n_steps) issue(j + 1, buf ^ 1);
-        const int hh = j / n_t, t = t_lo + j - hh * n_t;
+    const int key = kw0 + l32;
+    const bool key_ok = key < a.Nk;
+    auto iter = [&](int i, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        if (i + 1 < n_iter) issue(i + 1, MfaInt<buf ^ 1>{});
+        const int j = 2 * i + par;
+        const int hh = j / n_t, t = step_tile(j, hh);
         const int q0 = t * TROWS;
-        if (block_any(m, a.Nq, q0, kw0)) {   // uniform per wave
-            const uint16_t* tq = &sq[buf][0];
-            const uint16_t* td = &sq[buf][TILE];
+        if (j < n_steps && block_any(m, a.Nq, q0, kw0)) {   // uniform per wave
+            const uint16_t* tq = buf == 0 ? sq0 : sq1;   // + pofs, folded into the offsets
+            const uint16_t* td = tq + TILE;
+            const float* tl = (buf == 0 ? sl0 : sl1) + par * 128;
             mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 s = mfa_mfma32<DT>(lds_read16(tq + a_rd[kb]), kb_op[kb], s);
-                dp = mfa_mfma32<DT>(lds_read16(td + a_rd[kb]), lds_read16(sv + v_rd[kb]), dp);
+                dp = mfa_mfma32<DT>(lds_read16(td + a_rd[kb]), lds_read16(sv + v_rd + kb * 512), dp);
             }
             // register r of this lane: query row q0 + 16 (r / 8) + 8 g32 + r % 8, key kw0 + l32
             const bool full = block_all(m, a.Nq, q0, kw0);
-            const int key = kw0 + l32;
-            const bool key_ok = key < a.Nk;
             mfa_u32x4 pp[2], dsp[2];
 #pragma unroll
             for (int hk = 0; hk < 2; ++hk) {
                 const int rr = 16 * hk + 8 * g32;   // first of this run's 8 query rows
-                const mfa_f32x4 l0 = lds_read_f4(&sl[buf][rr]), l1 = lds_read_f4(&sl[buf][rr + 4]);
-                const mfa_f32x4 d0 = lds_read_f4(&sl[buf][64 + rr]), d1 = lds_read_f4(&sl[buf][64 + rr + 4]);
+                const mfa_f32x4 l0 = lds_read_f4(tl + rr), l1 = lds_read_f4(tl + rr + 4);
+                const mfa_f32x4 d0 = lds_read_f4(tl + 64 + rr), d1 = lds_read_f4(tl + 64 + rr + 4);
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     float pv[2], dv2[2];
@@ -271,21 +325,60 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int ofs = hk * 16 * D;
-                    const mfa_u32x2 a0 = lds_read_tr(td + t_rd[db] + ofs), a1 = lds_read_tr(td + t_rd4[db] + ofs);
+                    const int t4 = tr4_addr<D>(t_rd, t_rd4, db);
+                    const mfa_u32x2 a0 = lds_read_tr(td + t_rd[db] + ofs), a1 = lds_read_tr(td + t4 + ofs);
                     dvt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, pp[hk], dvt[db]);
-                    const mfa_u32x2 b0 = lds_read_tr(tq + t_rd[db] + ofs), b1 = lds_read_tr(tq + t_rd4[db] + ofs);
+                    const mfa_u32x2 b0 = lds_read_tr(tq + t_rd[db] + ofs), b1 = lds_read_tr(tq + t4 + ofs);
                     dkt[db] = mfa_mfma32<DT>(mfa_u32x4{b0[0], b0[1], b1[0], b1[1]}, dsp[hk], dkt[db]);
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next step's tiles landed
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next iteration's tiles landed
         block_barrier();
+    };
+    for (int i = 0; i < n_iter; i += 2) {
+        iter(i, MfaInt<0>{});
+        if (i + 1 < n_iter) iter(i + 1, MfaInt<1>{});
     }
+
+    // the odd-step half hands its partial sums to the even-step half through LDS (the
+    // tile buffers, free now: no copy is in flight), dK^T first, then dV^T; the first
+    // half of the 32-column blocks goes through one buffer, the second through the other
+    static_assert(sizeof(sq0) >= 4 * (NDB / 2) * 16 * 64 * sizeof(float), "exchange buffer");
+    auto exchange = [&](mfa_f32x16 (&acc)[NDB]) {
+        if (par == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float* red = (float*)(db < NDB / 2 ? sq0 : sq1);
+                    const int idx = ((kblk * (NDB / 2) + db % (NDB / 2)) * 4 + r4) * 64 + lane;
+                    lds_write_f4(red + idx * 4, mfa_f32x4{acc[db][4 * r4], acc[db][4 * r4 + 1],
+                                                          acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]});
+                }
+        }
+        block_barrier();
+        if (par == 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float* red = (const float*)(db < NDB / 2 ? sq0 : sq1);
+                    const int idx = ((kblk * (NDB / 2) + db % (NDB / 2)) * 4 + r4) * 64 + lane;
+                    const mfa_f32x4 o = lds_read_f4(red + idx * 4);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[db][4 * r4 + c] += o[c];
+                }
+        }
+        block_barrier();
+    };
+    exchange(dkt);
+    exchange(dvt);
+    if (par == 1) return;
 
     // write dK = scale (dK^T)^T and dV: register r of block db holds d = 32 db + 8 (r / 4)
     // + 4 g32 + r % 4 of key kw0 + l32; runs of 4 consecutive d are one 8-byte store
-    const int key = kw0 + l32;
-    if (key < a.Nk) {
+    if (key_ok) {
         uint16_t* dkp = a.dk + kv_base + (size_t)key * D;
         uint16_t* dvp = a.dv + kv_base + (size_t)key * D;
 #pragma unroll
@@ -305,29 +398,39 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ---- dQ ----------------------------------------------------------------------------
-// Workgroup = 128 query rows of one (batch, head), one wave per 32 rows; K and V tiles of
-// 64 keys over the key tiles the query tile sees (the forward's tile range).
+// Workgroup = 128 query rows of one (batch, head), 8 waves: wave w owns the 32 rows
+// 32 (w % 4) .. +31 and the 32-key half w / 4 of every 64-key K / V tile, over the key
+// tiles the query tile sees (the forward's tile range); the two halves add their partial
+// dQ through LDS at the end, in a fixed order.
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     constexpr int KCH = D / 8;
     constexpr int NKB = D / 16;
     constexpr int NDB = D / 32;
     constexpr int BN = 64;
     constexpr int TILE = BN * D;
     constexpr int RPB = 64 / KCH;
-    constexpr int LOADS = BN / RPB / 4;
-    __shared__ __attribute__((aligned(1024))) uint16_t st[2][2 * TILE];   // K, V tiles
+    constexpr int LOADS = BN / RPB / 8;
+    // the two pipeline buffers are separate objects (see the dK/dV kernel)
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * TILE];   // K, V tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rblk = wave & 3;            // row block of this wave
+    const int kh = wave >> 2;             // key half of every tile
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
-    const int qt = blockIdx.x;
-    const int bh = blockIdx.y;
+    const MfaMask& m = a.mask;
+    const int nqt = (a.Nq + 127) >> 7;
+    const int lid = xcd_logical_id(nqt * a.B * a.Hq);
+    const int bh = lid / nqt;
+    // causal masks give the last query tiles the most keys: they start first
+    const int qt = (m.right_eff >= 0 && m.left < 0) ? nqt - 1 - (lid - bh * nqt) : lid - bh * nqt;
     const int b = bh / a.Hq, h = bh - b * a.Hq;
     const int kvh = h / a.g;
-    const int qw0 = qt * 128 + wave * 32;   // this wave's first query row
+    const int qw0 = qt * 128 + rblk * 32;   // this wave's first query row
     const int qrow = qw0 + l32;
     const size_t q_base = (size_t)bh * a.Nq * D;
     const size_t kv_base = (size_t)(b * a.Hkv + kvh) * a.Nk * D;
@@ -348,7 +451,6 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
     const float lse2 = qvalid ? a.lse2[(size_t)bh * a.Nq + qrow] : MFA_INF;
     const float dvv = qvalid ? a.dvec[(size_t)bh * a.Nq + qrow] : 0.f;
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    const MfaMask& m = a.mask;
     const int64_t rlo64 = mfa_row_lo(m, qrow), rhi64 = mfa_row_hi(m, qrow);
     const int row_lo = rlo64 > a.Nk ? a.Nk : (int)rlo64;
     const int row_hi = rhi64 < -1 ? -1 : (int)rhi64;
@@ -361,31 +463,32 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqt[i] = mfa_f32x16{};
 
-    auto issue = [&](int kt, int buf) {
+    auto issue = [&](int kt, auto bufc) {
+        uint16_t* dst = decltype(bufc)::value == 0 ? st0 : st1;
         const int kk0 = kt * BN;
         const uint32_t bytes = (uint32_t)max(a.Nk - kk0, 0) * D * 2;
         const auto rk = mfa_rsrc(a.k + kv_base + (size_t)kk0 * D, bytes);
         const auto rv = mfa_rsrc(a.v + kv_base + (size_t)kk0 * D, bytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int blk = i * 4 + wave;
+            const int blk = i * 8 + wave;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
             const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
-            mfa_load16_lds(rk, &st[buf][blk * 512], off);
-            mfa_load16_lds(rv, &st[buf][TILE + blk * 512], off);
+            mfa_load16_lds(rk, dst + blk * 512, off);
+            mfa_load16_lds(rv, dst + TILE + blk * 512, off);
         }
     };
 
-    // A-operand rows of S^T = K Q^T and dP^T = V dO^T (key row key_perm(l32) of a 32-key
-    // block, chunk 2 kb + g32); transposing reads of K^T (lane group qg: columns 16 (qg % 2)
-    // .. +15 of a 32-column block, keys 8 (qg / 2) .. +3 (+4))
+    // A-operand rows of S^T = K Q^T and dP^T = V dO^T (key row key_perm(l32) of this
+    // wave's 32-key half, chunk 2 kb + g32); transposing reads of K^T (lane group qg:
+    // columns 16 (qg % 2) .. +15 of a 32-column block, keys 8 (qg / 2) .. +3 (+4))
     int a_rd[NKB], t_rd[NDB], t_rd4[NDB];
     {
-        const int row = key_perm(l32);
+        const int row = kh * 32 + key_perm(l32);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
         const int qg = lane >> 4, i = lane & 15;
-        const int trow = 8 * (qg >> 1) + (i >> 2);
+        const int trow = kh * 32 + 8 * (qg >> 1) + (i >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
@@ -394,25 +497,23 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
         }
     }
 
-    if (n > 0) issue(t_lo, 0);
+    if (n > 0) issue(t_lo, MfaInt<0>{});
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    for (int j = 0; j < n; ++j) {
-        const int buf = j & 1;
+    auto iter = [&](int j, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const int kt = t_lo + j;
-        if (j + 1 < n) issue(kt + 1, buf ^ 1);
-        const uint16_t* tk = &st[buf][0];
-        const uint16_t* tv = &st[buf][TILE];
-#pragma unroll
-        for (int nb = 0; nb < BN / 32; ++nb) {
-            const int c0 = kt * BN + nb * 32;
-            if (!block_any(m, a.Nq, qw0, c0)) continue;   // uniform per wave
+        if (j + 1 < n) issue(kt + 1, MfaInt<buf ^ 1>{});
+        const uint16_t* tk = buf == 0 ? st0 : st1;
+        const uint16_t* tv = tk + TILE;
+        const int c0 = kt * BN + kh * 32;
+        if (block_any(m, a.Nq, qw0, c0)) {   // uniform per wave
             const bool full = block_all(m, a.Nq, qw0, c0);
             mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                s = mfa_mfma32<DT>(lds_read16(tk + a_rd[kb] + nb * 32 * D), qb[kb], s);
-                dp = mfa_mfma32<DT>(lds_read16(tv + a_rd[kb] + nb * 32 * D), db_op[kb], dp);
+                s = mfa_mfma32<DT>(lds_read16(tk + a_rd[kb]), qb[kb], s);
+                dp = mfa_mfma32<DT>(lds_read16(tv + a_rd[kb]), db_op[kb], dp);
             }
             // register r: key c0 + 16 (r / 8) + 8 g32 + r % 8, query row qrow
             mfa_u32x4 dsp[2];
@@ -437,14 +538,47 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_bwd_dq_kernel(BwdArgs a) {
             for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int ofs = (nb * 32 + hk * 16) * D;
-                    const mfa_u32x2 a0 = lds_read_tr(tk + t_rd[db] + ofs), a1 = lds_read_tr(tk + t_rd4[db] + ofs);
+                    const int ofs = hk * 16 * D;
+                    const mfa_u32x2 a0 = lds_read_tr(tk + t_rd[db] + ofs),
+                                    a1 = lds_read_tr(tk + tr4_addr<D>(t_rd, t_rd4, db) + ofs);
                     dqt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, dsp[hk], dqt[db]);
                 }
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);
         block_barrier();
+    };
+    for (int j = 0; j < n; j += 2) {
+        iter(j, MfaInt<0>{});
+        if (j + 1 < n) iter(j + 1, MfaInt<1>{});
     }
+
+    // the second key half hands its partial dQ^T to the first through LDS (the tile
+    // buffers, free now; the first half of the 32-column blocks through one, the second
+    // through the other)
+    static_assert(sizeof(st0) >= 4 * (NDB / 2) * 16 * 64 * sizeof(float), "exchange buffer");
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float* red = (float*)(db < NDB / 2 ? st0 : st1);
+                const int idx = ((rblk * (NDB / 2) + db % (NDB / 2)) * 4 + r4) * 64 + lane;
+                lds_write_f4(red + idx * 4, mfa_f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1],
+                                                      dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]});
+            }
+    }
+    block_barrier();
+    if (kh == 1) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float* red = (const float*)(db < NDB / 2 ? st0 : st1);
+            const int idx = ((rblk * (NDB / 2) + db % (NDB / 2)) * 4 + r4) * 64 + lane;
+            const mfa_f32x4 o = lds_read_f4(red + idx * 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dqt[db][4 * r4 + c] += o[c];
+        }
 
     if (qvalid) {
         uint16_t* dqp = a.dq + q_base + (size_t)qrow * D;
@@ -468,18 +602,18 @@ int launch(const BwdArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
     hipLaunchKernelGGL((mfa_bwd_prep_kernel<D, DT>), g0, dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     const dim3 g1((unsigned)((a.Nk + 127) / 128), (unsigned)(a.B * a.Hkv));
-    hipLaunchKernelGGL((mfa_bwd_dkv_kernel<D, DT>), g1, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mfa_bwd_dkv_kernel<D, DT>), g1, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     const dim3 g2((unsigned)((a.Nq + 127) / 128), (unsigned)(a.B * a.Hq));
-    hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     snprintf(info->kernel, sizeof(info->kernel), "mfa_bwd_dkv_kernel+mfa_bwd_dq_kernel<D=%d,%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16");
     info->grid[0] = (int)g1.x;
     info->grid[1] = (int)g1.y;
     info->grid[2] = 1;
-    info->block = kThreads;
-    info->waves = 4;
+    info->block = kThreads8;
+    info->waves = 8;
     info->BM = 32;
     info->BN = 128;
     info->n_launches = 3;

@@ -88,3 +88,14 @@ def test_paged_varlen_layout():
     assert len(set(used.tolist())) == len(used) == 7
     c = A.config(7)
     assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (8, 32, 8, 128, 16)
+
+
+def test_grad_inputs_and_backward_config():
+    c = A.config(10)
+    assert (c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"]) == (2, 8, 8, 4096, 4096, 128)
+    assert c["dtype"] == "bf16" and c["causal"]
+    g0 = A.grad_inputs(1, 2, 64, 128, "bf16", 5)
+    g1 = A.grad_inputs(1, 2, 64, 128, "bf16", 5)
+    assert g0.shape == (1, 2, 64, 128) and g0.dtype == np.uint16 and np.array_equal(g0, g1)
+    x = (g0.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    assert abs(x.mean()) < 0.05 and 0.95 < x.std() < 1.05
