@@ -199,10 +199,16 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
     const int n_t = q_hi >= q_lo ? (int)(q_hi / TROWS) - t_lo + 1 : 0;
     const int n_steps = n_t * a.g;
     const int n_iter = (n_steps + 1) >> 1;   // iteration i: steps 2 i and 2 i + 1
-    // step j = (query head hh of the group, tile): the tiles of a head are walked from the
-    // last down, so that under a causal mask every key tile of the head reads the same
-    // query tiles at about the same time (they are shared through L2)
-    auto step_tile = [&](int j, int hh) { return t_lo + n_t - 1 - (j - hh * n_t); };
+    // step j = hh n_t + r: query head hh of the group, tile t_lo + n_t - 1 - r.  The tiles
+    // of a head are walked from the last down, so that under a causal mask every key tile
+    // of the head reads the same query tiles at about the same time (shared through L2).
+    // (hh, r) of this half's current step is carried from step to step (j grows by 2)
+    // instead of dividing.
+    int hh_c = 0, r_c = par;
+    while (r_c >= n_t && n_t > 0) {
+        r_c -= n_t;
+        ++hh_c;
+    }
 
     mfa_f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -211,15 +217,13 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
         dvt[i] = mfa_f32x16{};
     }
 
-    // direct loads of this half's step of iteration i (when it exists): Q and dO rows of
-    // tile t (32 rows), lse2 and dvec
     const int pofs = par * 2 * TILE;      // this half's tiles within a buffer
-    auto issue = [&](int i, auto bufc) {
+    // direct loads of step (hh, r) (it exists): Q and dO rows of its tile (32 rows), lse2
+    // and dvec
+    auto issue = [&](int hh, int r, auto bufc) {
         uint16_t* dst = (decltype(bufc)::value == 0 ? sq0 : sq1) + pofs;
         float* dl = (decltype(bufc)::value == 0 ? sl0 : sl1) + par * 128;
-        const int j = 2 * i + par;
-        if (j >= n_steps) return;
-        const int hh = j / n_t, t = step_tile(j, hh);
+        const int t = t_lo + n_t - 1 - r;
         const int h = kvh * a.g + hh;
         const int q0 = t * TROWS;
         const size_t row0 = ((size_t)(b * a.Hq + h) * a.Nq + q0);
@@ -249,11 +253,15 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
     // B operand of dP: this lane's 16 bytes of block (kblk, kb) of the V operand layout
     // (offsets within a buffer, this half's tiles included; the two transposing reads of a
     // k-group are 4 rows apart, where the row swizzle differs: see tr4_delta)
-    int a_rd[NKB], t_rd[NDB], t_rd4[NDB];
+    // The A-operand offset of k-step kb is a_b + ((2 kb) ^ a_x) * 8: the row swizzle splits
+    // into a lane term (in a_b) and one that XORs the k-step's chunk pair; it is formed
+    // at each read (two VALU) rather than held in NKB registers.
+    int a_b, a_x, t_rd[NDB], t_rd4[NDB];
     {
         const int row = key_perm(l32);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = pofs + row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
+        const int x = KCH == 16 ? (row & 15) : ((row >> 1) & 7);
+        a_x = x & (KCH - 2);
+        a_b = pofs + row * D + (g32 ^ (x & 1)) * 8;
         const int qg = lane >> 4, i = lane & 15;
         const int trow = 8 * (qg >> 1) + (i >> 2);
 #pragma unroll
@@ -265,60 +273,79 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
     }
     const int v_rd = kblk * NKB * 512 + lane * 8;
 
-    if (n_iter > 0) issue(0, MfaInt<0>{});
+    if (par < n_steps) issue(hh_c, r_c, MfaInt<0>{});
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): V rows, K operand, first tiles
     __syncthreads();
 
     const int key = kw0 + l32;
     const bool key_ok = key < a.Nk;
+    // P and dS of the 32 x 32 block, packed as B operands (register r of this lane: query
+    // row q0 + 16 (r / 8) + 8 g32 + r % 8, key kw0 + l32); MASKED = 0 for a block whose
+    // pairs are all visible
+    auto probs = [&](auto maskc, const mfa_f32x16& s, const mfa_f32x16& dp, const float* tl,
+                     int q0, mfa_u32x4 (&pp)[2], mfa_u32x4 (&dsp)[2]) {
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+            const int rr = 16 * hk + 8 * g32;   // first of this run's 8 query rows
+            const mfa_f32x4 l0 = lds_read_f4(tl + rr), l1 = lds_read_f4(tl + rr + 4);
+            const mfa_f32x4 d0 = lds_read_f4(tl + 64 + rr), d1 = lds_read_f4(tl + 64 + rr + 4);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float pv[2], dv2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = 2 * e2 + u;         // 0..7 within the run
+                    const int r = 8 * hk + e;
+                    const float lse2 = e < 4 ? l0[e] : l1[e - 4];
+                    const float dvv = e < 4 ? d0[e] : d1[e - 4];
+                    float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
+                    if constexpr (decltype(maskc)::value) {
+                        // visible iff 0 <= key < Nk, qi < Nq and d_lo <= key - qi - off <=
+                        // d_hi (bitwise, not short-circuit, so that no branch is made); a
+                        // masked pair's exponent is -inf and the exp itself gives 0
+                        const int qi = q0 + rr + e;
+                        const int dd = key - qi - off32;
+                        const bool vis = key_ok & (qi < a.Nq) & (dd >= d_lo) & (dd <= d_hi);
+                        x = vis ? x : -MFA_INF;
+                    }
+                    const float p = mfa_exp2(x);
+                    pv[u] = p;
+                    dv2[u] = p * (dp[r] - dvv);
+                }
+                pp[hk][e2] = mfa_pack2<DT>(pv[0], pv[1]);
+                dsp[hk][e2] = mfa_pack2<DT>(dv2[0], dv2[1]);
+            }
+        }
+    };
     auto iter = [&](int i, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        if (i + 1 < n_iter) issue(i + 1, MfaInt<buf ^ 1>{});
+        // this half's next step (hh_n, r_n): j + 2
+        int hh_n = hh_c, r_n = r_c + 2;
+        while (r_n >= n_t) {
+            r_n -= n_t;
+            ++hh_n;
+        }
+        if (2 * i + 2 + par < n_steps) issue(hh_n, r_n, MfaInt<buf ^ 1>{});
         const int j = 2 * i + par;
-        const int hh = j / n_t, t = step_tile(j, hh);
-        const int q0 = t * TROWS;
+        const int q0 = (t_lo + n_t - 1 - r_c) * TROWS;
         if (j < n_steps && block_any(m, a.Nq, q0, kw0)) {   // uniform per wave
             const uint16_t* tq = buf == 0 ? sq0 : sq1;   // + pofs, folded into the offsets
             const uint16_t* td = tq + TILE;
             const float* tl = (buf == 0 ? sl0 : sl1) + par * 128;
+            int ax = a_x;
+            asm volatile("" : "+v"(ax));   // keep the per-step offsets from being hoisted
             mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                s = mfa_mfma32<DT>(lds_read16(tq + a_rd[kb]), kb_op[kb], s);
-                dp = mfa_mfma32<DT>(lds_read16(td + a_rd[kb]), lds_read16(sv + v_rd + kb * 512), dp);
+                const int ao = a_b + (((2 * kb) ^ ax) << 3);
+                s = mfa_mfma32<DT>(lds_read16(tq + ao), kb_op[kb], s);
+                dp = mfa_mfma32<DT>(lds_read16(td + ao), lds_read16(sv + v_rd + kb * 512), dp);
             }
-            // register r of this lane: query row q0 + 16 (r / 8) + 8 g32 + r % 8, key kw0 + l32
-            const bool full = block_all(m, a.Nq, q0, kw0);
             mfa_u32x4 pp[2], dsp[2];
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk) {
-                const int rr = 16 * hk + 8 * g32;   // first of this run's 8 query rows
-                const mfa_f32x4 l0 = lds_read_f4(tl + rr), l1 = lds_read_f4(tl + rr + 4);
-                const mfa_f32x4 d0 = lds_read_f4(tl + 64 + rr), d1 = lds_read_f4(tl + 64 + rr + 4);
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float pv[2], dv2[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = 2 * e2 + u;         // 0..7 within the run
-                        const int r = 8 * hk + e;
-                        const float lse2 = e < 4 ? l0[e] : l1[e - 4];
-                        const float dvv = e < 4 ? d0[e] : d1[e - 4];
-                        // visible iff 0 <= key < Nk, qi < Nq and d_lo <= key - qi - off <= d_hi
-                        // (bitwise, not short-circuit, so that no branch is made); a masked
-                        // pair's exponent is -inf and the exp itself gives 0
-                        const int qi = q0 + rr + e;
-                        const int dd = key - qi - off32;
-                        const bool vis = full | (key_ok & (qi < a.Nq) & (dd >= d_lo) & (dd <= d_hi));
-                        const float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
-                        const float p = mfa_exp2(vis ? x : -MFA_INF);
-                        pv[u] = p;
-                        dv2[u] = p * (dp[r] - dvv);
-                    }
-                    pp[hk][e2] = mfa_pack2<DT>(pv[0], pv[1]);
-                    dsp[hk][e2] = mfa_pack2<DT>(dv2[0], dv2[1]);
-                }
-            }
+            if (block_all(m, a.Nq, q0, kw0))
+                probs(MfaInt<0>{}, s, dp, tl, q0, pp, dsp);
+            else
+                probs(MfaInt<1>{}, s, dp, tl, q0, pp, dsp);
             // dV^T += dO^T P, dK^T += Q^T dS (k-steps over the two runs of 16 query rows)
 #pragma unroll
             for (int hk = 0; hk < 2; ++hk) {
@@ -333,6 +360,8 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
                 }
             }
         }
+        hh_c = hh_n;
+        r_c = r_n;
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next iteration's tiles landed
         block_barrier();
     };
@@ -500,6 +529,30 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     if (n > 0) issue(t_lo, MfaInt<0>{});
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
+    // dS^T of the 32 x 32 block packed as the B operand (register r: key c0 + 16 (r / 8) +
+    // 8 g32 + r % 8, query row qrow); MASKED = 0 for a block whose pairs are all visible
+    auto dscores = [&](auto maskc, const mfa_f32x16& s, const mfa_f32x16& dp, int c0,
+                       mfa_u32x4 (&dsp)[2]) {
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float w[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = 8 * hk + 2 * e2 + u;
+                    float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
+                    if constexpr (decltype(maskc)::value) {
+                        const int key = c0 + 16 * hk + 8 * g32 + 2 * e2 + u;
+                        const bool vis = qvalid & (key >= row_lo) & (key <= row_hi);
+                        x = vis ? x : -MFA_INF;
+                    }
+                    const float p = mfa_exp2(x);
+                    w[u] = p * (dp[r] - dvv);
+                }
+                dsp[hk][e2] = mfa_pack2<DT>(w[0], w[1]);
+            }
+    };
     auto iter = [&](int j, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         const int kt = t_lo + j;
@@ -508,31 +561,17 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
         const uint16_t* tv = tk + TILE;
         const int c0 = kt * BN + kh * 32;
         if (block_any(m, a.Nq, qw0, c0)) {   // uniform per wave
-            const bool full = block_all(m, a.Nq, qw0, c0);
             mfa_f32x16 s = mfa_f32x16{}, dp = mfa_f32x16{};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 s = mfa_mfma32<DT>(lds_read16(tk + a_rd[kb]), qb[kb], s);
                 dp = mfa_mfma32<DT>(lds_read16(tv + a_rd[kb]), db_op[kb], dp);
             }
-            // register r: key c0 + 16 (r / 8) + 8 g32 + r % 8, query row qrow
             mfa_u32x4 dsp[2];
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float w[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int r = 8 * hk + 2 * e2 + u;
-                        const int key = c0 + 16 * hk + 8 * g32 + 2 * e2 + u;
-                        const bool vis = full | (qvalid & (key >= row_lo) & (key <= row_hi));
-                        const float x = __builtin_fmaf(s[r], a.scale_log2, -lse2);
-                        const float p = mfa_exp2(vis ? x : -MFA_INF);
-                        w[u] = p * (dp[r] - dvv);
-                    }
-                    dsp[hk][e2] = mfa_pack2<DT>(w[0], w[1]);
-                }
+            if (block_all(m, a.Nq, qw0, c0))
+                dscores(MfaInt<0>{}, s, dp, c0, dsp);
+            else
+                dscores(MfaInt<1>{}, s, dp, c0, dsp);
             // dQ^T += K^T dS^T
 #pragma unroll
             for (int hk = 0; hk < 2; ++hk)
