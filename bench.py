@@ -52,8 +52,9 @@ METRIC = "attn fwd TFLOP/s (D=128 causal fp16) + paged decode HBM GB/s, % roofli
 # while the sources are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "fwd": ["mfa_fwd.hip", "mfa_device.h", "mfa_geometry.h"],
+    "fwd": ["mfa_fwd.hip", "mfa_device.h", "mfa_geometry.h", "mfa_tile.h"],
     "decode": ["mfa_decode.hip", "mfa_device.h"],
+    "bwd": ["mfa_bwd.hip", "mfa_device.h", "mfa_geometry.h", "mfa_tile.h"],
 }
 
 
@@ -426,7 +427,8 @@ def bench_backward(step, steps):
                     f"{c['dtype']} causal=1 (prep + dK/dV + dQ launches)",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": None},
+                     "frac": tf / PEAK_MFMA_F16,
+                     "traffic": measured_traffic("bwd_config10", "bwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 

@@ -9,7 +9,7 @@
 // The probabilities are recomputed from the saved LSE (no running maximum is needed: P <= 1),
 // dQ is accumulated by its own pass rather than with atomics, so every result is
 // deterministic, and every product runs on the 32x32x16 MFMA:
-//   dK/dV pass, one wave = 32 keys (its K^T operand in registers, its V rows in LDS):
+//   dK/dV pass, one wave = 32 keys (its K^T operand in registers, V in LDS):
 //     S = Q K^T and dP = dO V^T with the query rows fed in key_perm order, so that each
 //     lane owns one key column and runs of 8 consecutive query rows; the packed P and dS
 //     are then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
@@ -17,8 +17,12 @@
 //   dQ pass, one wave = 32 query rows (its Q^T and dO^T operands in registers):
 //     S^T = K Q^T and dP^T = V dO^T with the key rows in key_perm order, then
 //     dQ^T += K^T dS^T with K^T from transposing reads of the K tile.
-// Tiles stream through LDS with direct global -> LDS loads, double-buffered.  A wave skips
-// a 32 x 32 block holding no visible (query, key) pair.
+// Workgroups have 8 waves in two halves that split the steps (dK/dV: alternate query
+// tiles; dQ: the two 32-key halves of each key tile) and add their partial sums through
+// LDS at the end.  Tiles stream through LDS with direct global -> LDS loads, one step
+// ahead; the workgroups of one (batch, head) run on one XCD and walk the shared tiles in
+// the same order, so the copies hit L2.  A wave skips a 32 x 32 block holding no visible
+// (query, key) pair, and masks only blocks that are not wholly visible.
 #include "mfa_device.h"
 #include "mfa_geometry.h"
 #include "mfa_internal.h"

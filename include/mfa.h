@@ -31,7 +31,7 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensors are caller-owned, contiguous, 16-byte aligned device memory.  The
- *   library allocates no device memory; the decode workspace is passed in.
+ *   library allocates no device memory; the decode and backward workspaces are passed in.
  * - Element type: 16-bit storage, MFA_F16 (IEEE half) or MFA_BF16 (bfloat16), the
  *   same for Q, K, V and O.  LSE is float32.  All arithmetic accumulates in fp32.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
