@@ -33,16 +33,25 @@ namespace {
 constexpr int kThreads = 256;   // 4 waves (prep)
 constexpr int kThreads8 = 512;  // 8 waves (dK/dV and dQ)
 
-// Offset of the second transposing read of a k-group, 4 rows below the first (t_rd[db]).
-// The row swizzle flips one chunk bit between the two rows: with 16 chunks a row that bit
-// is bit 2 of the chunk index, set exactly in the odd 32-column blocks, so the distance is
-// the constant 4 D -+ 32 and needs no register; with 8 chunks it depends on the lane and
-// the precomputed t_rd4 is used.
-template <int D>
-__device__ __forceinline__ int tr4_addr(const int* t_rd, const int* t_rd4, int db) {
-    if constexpr (D == 128) return t_rd[db] + 4 * D + ((db & 1) ? -32 : 32);
-    else return t_rd4[db];
+// Layout of the Q / dO (dK/dV pass) and K / V (dQ pass) tiles in LDS: 16-byte chunk ch of
+// row r sits at chunk ch ^ x(r).  The tiles are read two ways: as row operands (16 lanes,
+// the 16 rows of a 16-row block, one chunk each: x must be a bijection on those rows) and
+// transposed (16 lanes over 4 consecutive rows, two adjacent chunks each, and the 16 lanes
+// beside them two chunks further: the rows must differ in the chunk bits above bit 1).
+// With 16 chunks a row (one row spans the 64 banks) x(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+// meets both; with 8 chunks (two rows per 64 banks) the same holds for x = h((r >> 1) & 7),
+// h(s) = ((s & 1) << 2) | (s >> 1).  The plain row swizzle ch ^ (r & 15) would put rows 4k
+// and 4k + 1 of a transposing read on the same banks.
+template <int KCH>
+__device__ __forceinline__ int bwd_x(int row) {
+    if constexpr (KCH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else {
+        const int s = (row >> 1) & 7;
+        return ((s & 1) << 2) | (s >> 1);
+    }
 }
+template <int KCH>
+__device__ __forceinline__ int bwd_swz(int row, int ch) { return ch ^ bwd_x<KCH>(row); }
 
 // Workgroups are handed to the 8 XCDs in turn (id % 8).  When the count divides evenly,
 // renumber them so that XCD x runs the contiguous logical range [x n / 8, (x + 1) n / 8):
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
         for (int l = 0; l < LOADS; ++l) {
             const int blk = l * 4 + pw;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
-            const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
+            const uint32_t off = (uint32_t)(row * D + bwd_swz<KCH>(row, phys) * 8) * 2;
             mfa_load16_lds(rq, dst + blk * 512, off);
             mfa_load16_lds(rd, dst + TILE + blk * 512, off);
         }
@@ -251,19 +260,19 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
         }
     };
 
-    // per-lane LDS addresses: A-operand rows of S = Q K^T / dP = dO V^T (query row
-    // key_perm(l32), chunk 2 kb + g32); transposing reads of Q^T / dO^T (lane group qg:
-    // columns 16 (qg % 2) .. +15 of a 32-column block, query rows 8 (qg / 2) .. +3 (+4));
-    // B operand of dP: this lane's 16 bytes of block (kblk, kb) of the V operand layout
-    // (offsets within a buffer, this half's tiles included; the two transposing reads of a
-    // k-group are 4 rows apart, where the row swizzle differs: see tr4_delta)
-    // The A-operand offset of k-step kb is a_b + ((2 kb) ^ a_x) * 8: the row swizzle splits
-    // into a lane term (in a_b) and one that XORs the k-step's chunk pair; it is formed
-    // at each read (two VALU) rather than held in NKB registers.
-    int a_b, a_x, t_rd[NDB], t_rd4[NDB];
+    // per-lane LDS addresses (offsets within a buffer, this half's tiles included):
+    // A-operand rows of S = Q K^T / dP = dO V^T (query row key_perm(l32), chunk 2 kb + g32);
+    // transposing reads of Q^T / dO^T (lane group qg: columns 16 (qg % 2) .. +15 of a
+    // 32-column block, query rows 8 (qg / 2) .. +3, and 4 rows further at t_rd + t4, where
+    // the layout flips chunk bit 0: t4 = 4 D -+ 8 by this lane's chunk parity);
+    // B operand of dP: this lane's 16 bytes of block (kblk, kb) of the V operand layout.
+    // The A-operand offset of k-step kb is a_b + ((2 kb) ^ a_x) * 8: the layout splits into
+    // a lane term (in a_b) and one that XORs the k-step's chunk pair; it is formed at each
+    // read (two VALU) rather than held in NKB registers.
+    int a_b, a_x, t_rd[NDB], t4;
     {
         const int row = key_perm(l32);
-        const int x = KCH == 16 ? (row & 15) : ((row >> 1) & 7);
+        const int x = bwd_x<KCH>(row);
         a_x = x & (KCH - 2);
         a_b = pofs + row * D + (g32 ^ (x & 1)) * 8;
         const int qg = lane >> 4, i = lane & 15;
@@ -271,9 +280,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
-            t_rd[db] = pofs + trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
-            t_rd4[db] = pofs + (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
+            t_rd[db] = pofs + trow * D + bwd_swz<KCH>(trow, col >> 3) * 8 + (col & 7);
         }
+        t4 = 4 * D + (((i >> 1) & 1) ? -8 : 8);
     }
     const int v_rd = kblk * NKB * 512 + lane * 8;
 
@@ -356,10 +365,10 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int ofs = hk * 16 * D;
-                    const int t4 = tr4_addr<D>(t_rd, t_rd4, db);
-                    const mfa_u32x2 a0 = lds_read_tr(td + t_rd[db] + ofs), a1 = lds_read_tr(td + t4 + ofs);
+                    const int t2 = t_rd[db] + t4;
+                    const mfa_u32x2 a0 = lds_read_tr(td + t_rd[db] + ofs), a1 = lds_read_tr(td + t2 + ofs);
                     dvt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, pp[hk], dvt[db]);
-                    const mfa_u32x2 b0 = lds_read_tr(tq + t_rd[db] + ofs), b1 = lds_read_tr(tq + t4 + ofs);
+                    const mfa_u32x2 b0 = lds_read_tr(tq + t_rd[db] + ofs), b1 = lds_read_tr(tq + t2 + ofs);
                     dkt[db] = mfa_mfma32<DT>(mfa_u32x4{b0[0], b0[1], b1[0], b1[1]}, dsp[hk], dkt[db]);
                 }
             }
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < LOADS; ++i) {
             const int blk = i * 8 + wave;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
-            const uint32_t off = (uint32_t)(row * D + swz_rows<KCH>(row, phys) * 8) * 2;
+            const uint32_t off = (uint32_t)(row * D + bwd_swz<KCH>(row, phys) * 8) * 2;
             mfa_load16_lds(rk, dst + blk * 512, off);
             mfa_load16_lds(rv, dst + TILE + blk * 512, off);
         }
@@ -515,19 +524,20 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     // A-operand rows of S^T = K Q^T and dP^T = V dO^T (key row key_perm(l32) of this
     // wave's 32-key half, chunk 2 kb + g32); transposing reads of K^T (lane group qg:
     // columns 16 (qg % 2) .. +15 of a 32-column block, keys 8 (qg / 2) .. +3 (+4))
-    int a_rd[NKB], t_rd[NDB], t_rd4[NDB];
+    // (the second transposing read of a k-group is 4 rows further, at t_rd + t4)
+    int a_rd[NKB], t_rd[NDB], t4;
     {
         const int row = kh * 32 + key_perm(l32);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_rows<KCH>(row, 2 * kb + g32) * 8;
+        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + bwd_swz<KCH>(row, 2 * kb + g32) * 8;
         const int qg = lane >> 4, i = lane & 15;
         const int trow = kh * 32 + 8 * (qg >> 1) + (i >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
-            t_rd[db] = trow * D + swz_rows<KCH>(trow, col >> 3) * 8 + (col & 7);
-            t_rd4[db] = (trow + 4) * D + swz_rows<KCH>(trow + 4, col >> 3) * 8 + (col & 7);
+            t_rd[db] = trow * D + bwd_swz<KCH>(trow, col >> 3) * 8 + (col & 7);
         }
+        t4 = 4 * D + (((i >> 1) & 1) ? -8 : 8);
     }
 
     if (n > 0) issue(t_lo, MfaInt<0>{});
@@ -583,7 +593,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
                 for (int db = 0; db < NDB; ++db) {
                     const int ofs = hk * 16 * D;
                     const mfa_u32x2 a0 = lds_read_tr(tk + t_rd[db] + ofs),
-                                    a1 = lds_read_tr(tk + tr4_addr<D>(t_rd, t_rd4, db) + ofs);
+                                    a1 = lds_read_tr(tk + t_rd[db] + t4 + ofs);
                     dqt[db] = mfa_mfma32<DT>(mfa_u32x4{a0[0], a0[1], a1[0], a1[1]}, dsp[hk], dqt[db]);
                 }
         }
