@@ -33,26 +33,8 @@ namespace {
 constexpr int kThreads = 256;   // 4 waves (prep)
 constexpr int kThreads8 = 512;  // 8 waves (dK/dV and dQ)
 
-// Layout of the Q / dO (dK/dV pass) and K / V (dQ pass) tiles in LDS: 16-byte chunk ch of
-// row r sits at chunk ch ^ x(r).  The tiles are read two ways: as row operands (16 lanes,
-// the 16 rows of a 16-row block, one chunk each: x must be a bijection on those rows) and
-// transposed (16 lanes over 4 consecutive rows, two adjacent chunks each, and the 16 lanes
-// beside them two chunks further: the rows must differ in the chunk bits above bit 1).
-// With 16 chunks a row (one row spans the 64 banks) x(r) = ((r & 3) << 2) | ((r >> 2) & 3)
-// meets both; with 8 chunks (two rows per 64 banks) the same holds for x = h((r >> 1) & 7),
-// h(s) = ((s & 1) << 2) | (s >> 1).  The plain row swizzle ch ^ (r & 15) would put rows 4k
-// and 4k + 1 of a transposing read on the same banks.
-template <int KCH>
-__device__ __forceinline__ int bwd_x(int row) {
-    if constexpr (KCH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else {
-        const int s = (row >> 1) & 7;
-        return ((s & 1) << 2) | (s >> 1);
-    }
-}
-template <int KCH>
-__device__ __forceinline__ int bwd_swz(int row, int ch) { return ch ^ bwd_x<KCH>(row); }
-
+// The Q / dO (dK/dV pass) and K / V (dQ pass) tiles are read as row operands and
+// transposed: they use the swz_both layout.
 // Workgroups are handed to the 8 XCDs in turn (id % 8).  When the count divides evenly,
 // renumber them so that XCD x runs the contiguous logical range [x n / 8, (x + 1) n / 8):
 // the workgroups of one (batch, head) then share that XCD's L2, and each XCD still starts
@@ -247,7 +229,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
         for (int l = 0; l < LOADS; ++l) {
             const int blk = l * 4 + pw;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
-            const uint32_t off = (uint32_t)(row * D + bwd_swz<KCH>(row, phys) * 8) * 2;
+            const uint32_t off = (uint32_t)(row * D + swz_both<KCH>(row, phys) * 8) * 2;
             mfa_load16_lds(rq, dst + blk * 512, off);
             mfa_load16_lds(rd, dst + TILE + blk * 512, off);
         }
@@ -272,7 +254,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
     int a_b, a_x, t_rd[NDB], t4;
     {
         const int row = key_perm(l32);
-        const int x = bwd_x<KCH>(row);
+        const int x = swz_x<KCH>(row);
         a_x = x & (KCH - 2);
         a_b = pofs + row * D + (g32 ^ (x & 1)) * 8;
         const int qg = lane >> 4, i = lane & 15;
@@ -280,9 +262,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
-            t_rd[db] = pofs + trow * D + bwd_swz<KCH>(trow, col >> 3) * 8 + (col & 7);
+            t_rd[db] = pofs + trow * D + swz_both<KCH>(trow, col >> 3) * 8 + (col & 7);
         }
-        t4 = 4 * D + (((i >> 1) & 1) ? -8 : 8);
+        t4 = tr4_delta<D>(lane);
     }
     const int v_rd = kblk * NKB * 512 + lane * 8;
 
@@ -515,7 +497,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < LOADS; ++i) {
             const int blk = i * 8 + wave;
             const int row = blk * RPB + lane / KCH, phys = lane % KCH;
-            const uint32_t off = (uint32_t)(row * D + bwd_swz<KCH>(row, phys) * 8) * 2;
+            const uint32_t off = (uint32_t)(row * D + swz_both<KCH>(row, phys) * 8) * 2;
             mfa_load16_lds(rk, dst + blk * 512, off);
             mfa_load16_lds(rv, dst + TILE + blk * 512, off);
         }
@@ -529,15 +511,15 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     {
         const int row = kh * 32 + key_perm(l32);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + bwd_swz<KCH>(row, 2 * kb + g32) * 8;
+        for (int kb = 0; kb < NKB; ++kb) a_rd[kb] = row * D + swz_both<KCH>(row, 2 * kb + g32) * 8;
         const int qg = lane >> 4, i = lane & 15;
         const int trow = kh * 32 + 8 * (qg >> 1) + (i >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int col = db * 32 + 16 * (qg & 1) + 4 * (i & 3);
-            t_rd[db] = trow * D + bwd_swz<KCH>(trow, col >> 3) * 8 + (col & 7);
+            t_rd[db] = trow * D + swz_both<KCH>(trow, col >> 3) * 8 + (col & 7);
         }
-        t4 = 4 * D + (((i >> 1) & 1) ? -8 : 8);
+        t4 = tr4_delta<D>(lane);
     }
 
     if (n > 0) issue(t_lo, MfaInt<0>{});

@@ -111,7 +111,7 @@ struct Tile {
     static constexpr int ELEMS = kBN * D;               // 16-bit elements per K or V tile
     static constexpr int LOADS = kBN * KCH / kGroupThreads;  // 16-byte direct loads per thread
     __device__ static __forceinline__ int k_phys(int row, int ch) { return swz_rows<KCH>(row, ch); }
-    __device__ static __forceinline__ int v_phys(int row, int ch) { return swz_tr<KCH>(row, ch); }
+    __device__ static __forceinline__ int v_phys(int row, int ch) { return swz_both<KCH>(row, ch); }
 };
 
 // Sequence s of a pack: tokens [cu[s], cu[s+1]) clamped into [0, total] and to at most
@@ -451,7 +451,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
     // V^T (PV A operand) via transposing reads: lane group qg = lane / 16 covers
     // columns 16*(qg%2) .. +15 of a 32-column block and keys 8*(qg/2) .. +3 (+4 for the
-    // second read); lane i of the group addresses row i/4, columns 4*(i%4) .. +3.
+    // second read, v4 further); lane i of the group addresses row i/4, columns 4*(i%4) .. +3.
+    const int v4 = tr4_delta<D>(lane);
     int v_rd[NDB];
     {
         const int qg = lane >> 4, i = lane & 15;
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const mfa_u32x2 l2 = lds_read_tr(base + v_rd[db] + kofs);
-                    const mfa_u32x2 h2 = lds_read_tr(base + v_rd[db] + kofs + 4 * D);
+                    const mfa_u32x2 h2 = lds_read_tr(base + v_rd[db] + kofs + v4);
                     vop[db] = mfa_u32x4{l2[0], l2[1], h2[0], h2[1]};
                 }
 #pragma unroll

@@ -32,6 +32,35 @@ __device__ __forceinline__ int swz_tr(int row, int ch) {
     return (KCH == 16) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
 }
 
+// A layout for tiles read both ways, and for transposing reads by 32 lanes at once:
+// chunk ch of row r sits at ch ^ x(r).  Row reads need x to be a bijection on each block
+// of 16 rows; a transposing read covers 4 consecutive rows with two adjacent chunks per
+// 16 lanes, the 16 lanes beside them two chunks further, so the 4 rows must differ in the
+// chunk bits above bit 1.  With 16 chunks a row (a row spans the 64 banks)
+// x(r) = ((r & 3) << 2) | ((r >> 2) & 3) meets both; with 8 chunks (two rows per 64 banks)
+// x = h((r >> 1) & 7), h(s) = ((s & 1) << 2) | (s >> 1).  (swz_rows puts rows 4k and
+// 4k + 1 of a transposing read on the same banks; swz_tr separates them within 16 lanes
+// but not across 32.)  x depends on row % 16 only.  Between a transposing read and the
+// one 4 rows below it the layout flips chunk bit 0, so the second read is
+// tr4_delta elements further, by the lane's chunk parity.
+template <int KCH>
+__device__ __forceinline__ int swz_x(int row) {
+    if constexpr (KCH == 16) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        const int s = (row >> 1) & 7;
+        return ((s & 1) << 2) | (s >> 1);
+    }
+}
+template <int KCH>
+__device__ __forceinline__ int swz_both(int row, int ch) { return ch ^ swz_x<KCH>(row); }
+// (lane i of a 16-lane group of the transposing read pattern: rows 8 (group / 2) + i / 4,
+// columns 32 db + 16 (group % 2) + 4 (i % 4))
+template <int D>
+__device__ __forceinline__ int tr4_delta(int lane) {
+    return 4 * D + ((((lane & 15) >> 1) & 1) ? -8 : 8);
+}
+
 // Workgroup barrier of the tile pipelines.  __syncthreads() also fences memory, which
 // waits for every outstanding load, including direct-to-LDS copies meant to stay in
 // flight; here each wave has already waited for the copies the next stage reads
