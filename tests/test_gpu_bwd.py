@@ -115,3 +115,16 @@ def test_dense_causal_prefill_shape_two_heads(dtype):
         refs = oracle.attention_backward(qf, kf, vf, dof, scale, True)
         check((f"dQ[{b},{h}]", f"dK[{b},{h}]", f"dV[{b},{h}]"),
               [to_f64(t[sl], dtype) for t in (dq, dk, dv)], refs, dtype)
+
+
+def test_gqa_long_sequence_one_kv_group():
+    # GQA at a long sequence (B=1, Hq=8, Hkv=2, N=8192, bf16, causal): the oracle recomputes
+    # KV head 0's whole group of 4 query heads (its dK, dV sum over all four), which checks
+    # the group accumulation over the long descending walk of the dK/dV pass
+    x, dob, scale, (dq, dk, dv) = grads_case(1, 8, 2, 8192, 8192, 128, "bf16", 21, True)
+    sq, skv = (slice(0, 1), slice(0, 4)), (slice(0, 1), slice(0, 1))
+    qf, dof = (oracle.widen(t[sq], "bf16") for t in (x.q, dob))
+    kf, vf = (oracle.widen(t[skv], "bf16") for t in (x.k, x.v))
+    refs = oracle.attention_backward(qf, kf, vf, dof, scale, True)
+    check(("dQ[heads 0-3]", "dK[kv 0]", "dV[kv 0]"),
+          [to_f64(dq[sq], "bf16"), to_f64(dk[skv], "bf16"), to_f64(dv[skv], "bf16")], refs, "bf16")
