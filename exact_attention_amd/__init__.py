@@ -185,6 +185,25 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _need(t, shape, dtype, name):
+    """Shape and dtype of a tensor the caller passes in: the C ABI sees only pointers and the
+    sizes given here, so every buffer must hold exactly what those sizes say."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)} "
+                         f"(got {t.dtype} {tuple(t.shape)})")
+
+
+def _need_tile_log(tile_log, B, Hq, Nq, D, dtype):
+    """tile_log holds B * Hq * n_q_tiles * 4 int32 (n_q_tiles from the host plan)."""
+    torch = _torch()
+    if tile_log.dtype != torch.int32:
+        raise TypeError("tile_log must be int32")
+    plan, _ = mfa_plan_fwd(Nq, Nq, D, dtype, with_ranges=False)
+    need = B * Hq * plan["n_q_tiles"] * 4
+    if tile_log.numel() < need:
+        raise ValueError(f"tile_log must hold at least {need} int32 (B * Hq * n_q_tiles * 4)")
+
+
 def _stream(t):
     torch = _torch()
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -218,6 +237,8 @@ def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left:
         raise ValueError("lse must be float32 [B, Hq, Nq]")
     if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must match q")
+    if tile_log is not None:
+        _need_tile_log(tile_log, B, Hq, Nq, D, dt)
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
             _dev(lse, "lse") if lse is not None else None,
             B, Hq, Hkv, Nq, Nk, D, float(scale), int(bool(causal)), int(win_left),
@@ -225,8 +246,6 @@ def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left:
     if tile_log is None:
         _check(lib().mfa_fwd(*args), "mfa_fwd")
     else:
-        if tile_log.dtype != torch.int32:
-            raise TypeError("tile_log must be int32")
         _check(lib().mfa_fwd_tilelog(*args, _dev(tile_log, "tile_log")), "mfa_fwd_tilelog")
     return out, lse
 
@@ -245,7 +264,11 @@ def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = 
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q, k, v must be 4-D [B, H, N, D]")
     B, Hq, Nq, D = q.shape
-    _, Hkv, Nk, _ = k.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
     for t, n in ((out, "out"), (dout, "dout")):
         if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
             raise ValueError(f"{n} must match q")
@@ -254,6 +277,9 @@ def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = 
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    for t, like, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is not None:
+            _need(t, like.shape, like.dtype, n)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -285,10 +311,18 @@ def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_l
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q, k, v must be 4-D [B, H, N, D]")
     B, Hq, Nq, D = q.shape
-    _, Hkv, Nk, _ = k.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if out is not None:
+        _need(out, q.shape, q.dtype, "out")
+    if lse is not None:
+        _need(lse, (B, Hq, Nq), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -324,8 +358,7 @@ def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_l
         ext.block_q, ext.block_k = int(block_q), int(block_k)
         keep.append(bm)
     if tile_log is not None:
-        if tile_log.dtype != torch.int32:
-            raise TypeError("tile_log must be int32")
+        _need_tile_log(tile_log, B, Hq, Nq, D, dt)
         ext.tile_log = _dev(tile_log, "tile_log")
     _check(lib().mfa_fwd_ext(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                              _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, Nq, Nk, D,
@@ -370,6 +403,8 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
         raise ValueError("lse must be float32 [Hq, total_q]")
     if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must match q")
+    if tile_log is not None:
+        _need_tile_log(tile_log, B, Hq, max(1, int(max_seqlen_q)), D, dt)
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
             _dev(lse, "lse") if lse is not None else None,
             _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"),
@@ -378,8 +413,6 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     if tile_log is None:
         _check(lib().mfa_fwd_varlen(*args), "mfa_fwd_varlen")
     else:
-        if tile_log.dtype != torch.int32:
-            raise TypeError("tile_log must be int32")
         _check(lib().mfa_fwd_varlen_tilelog(*args, _dev(tile_log, "tile_log")),
                "mfa_fwd_varlen_tilelog")
     return out, lse
@@ -460,6 +493,10 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if out is not None:
+        _need(out, q.shape, q.dtype, "out")
+    if lse is not None:
+        _need(lse, (B, Hq), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -511,6 +548,10 @@ def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: fl
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if out is not None:
+        _need(out, q.shape, q.dtype, "out")
+    if lse is not None:
+        _need(lse, (B, Nq, Hq), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:

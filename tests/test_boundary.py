@@ -319,3 +319,64 @@ def test_last_dispatch_is_per_thread():
     t.start()
     t.join()
     assert out["r"] == -13
+
+
+# ---- the torch binding checks every buffer against the sizes it passes to the C ABI,
+# before touching the device (CPU tensors here: a check that let them through would fail
+# later with "must be a device tensor" instead)
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float16)
+
+
+def _binding_error(fn, *args, match, **kw):
+    with pytest.raises((ValueError, TypeError), match=match):
+        fn(*args, **kw)
+
+
+def test_binding_checks_backward_shapes_and_types():
+    import torch
+    q, k, v = _t(1, 4, 64, 64), _t(1, 2, 80, 64), _t(1, 2, 80, 64)
+    o, do, lse = _t(1, 4, 64, 64), _t(1, 4, 64, 64), _t(1, 4, 64, dtype=torch.float32)
+    _binding_error(ea.mfa_bwd, q, _t(2, 2, 80, 64), _t(2, 2, 80, 64), o, do, lse, match="shape mismatch")
+    _binding_error(ea.mfa_bwd, q, _t(1, 2, 80, 128), _t(1, 2, 80, 128), o, do, lse, match="shape mismatch")
+    _binding_error(ea.mfa_bwd, q, k.bfloat16(), v.bfloat16(), o, do, lse, match="one dtype")
+    _binding_error(ea.mfa_bwd, q, k, v, o, do, lse, dk=_t(1, 2, 64, 64), match="dk must be")
+    _binding_error(ea.mfa_bwd, q, k, v, o, do, lse, dq=_t(1, 4, 64, 64).bfloat16(), match="dq must be")
+    _binding_error(ea.mfa_bwd, q, k, v, o, do, lse, dv=_t(1, 2, 80, 32), match="dv must be")
+
+
+def test_binding_checks_forward_ext_and_tile_logs():
+    import torch
+    q, k, v = _t(1, 4, 300, 128), _t(1, 2, 300, 128), _t(1, 2, 300, 128)
+    _binding_error(ea.mfa_fwd_ext, q, _t(1, 2, 300, 64), _t(1, 2, 300, 64), match="shape mismatch")
+    _binding_error(ea.mfa_fwd_ext, q, k.bfloat16(), v.bfloat16(), match="one dtype")
+    _binding_error(ea.mfa_fwd_ext, q, k, v, out=_t(1, 4, 299, 128), match="out must be")
+    _binding_error(ea.mfa_fwd_ext, q, k, v, lse=_t(1, 4, 300, dtype=torch.float32)[:, :, :10],
+                   match="lse must be")
+    # 300 rows = 3 query tiles: 1 * 4 * 3 * 4 = 48 int32 records
+    short = torch.zeros(47, dtype=torch.int32)
+    _binding_error(ea.mfa_fwd, q, k, v, tile_log=short, match="at least 48")
+    _binding_error(ea.mfa_fwd_ext, q, k, v, tile_log=short, match="at least 48")
+    _binding_error(ea.mfa_fwd, q, k, v, tile_log=torch.zeros(48, dtype=torch.int64), match="int32")
+    # varlen: tiles counted from max_seqlen_q (300 -> 3), B = 2 sequences: 2 * 4 * 3 * 4 = 96
+    cu = torch.tensor([0, 100, 300], dtype=torch.int32)
+    _binding_error(ea.mfa_fwd_varlen, _t(300, 4, 128), _t(300, 2, 128), _t(300, 2, 128), cu, cu,
+                   300, 300, tile_log=torch.zeros(95, dtype=torch.int32), match="at least 96")
+
+
+def test_binding_checks_decode_outputs():
+    import torch
+    q = _t(2, 8, 128).bfloat16()
+    kp = _t(10, 16, 2, 128).bfloat16()
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    _binding_error(ea.mfa_decode_paged, q, kp, kp, bt, sl, out=_t(2, 8, 128), match="out must be")
+    _binding_error(ea.mfa_decode_paged, q, kp, kp, bt, sl, lse=_t(2, 4, dtype=torch.float32),
+                   match="lse must be")
+    q4 = _t(2, 4, 8, 128).bfloat16()
+    _binding_error(ea.mfa_decode_paged_multi, q4, kp, kp, bt, sl, out=_t(2, 4, 8, 64).bfloat16(),
+                   match="out must be")
+    _binding_error(ea.mfa_decode_paged_multi, q4, kp, kp, bt, sl, lse=_t(2, 8, 4, dtype=torch.float32),
+                   match="lse must be")
