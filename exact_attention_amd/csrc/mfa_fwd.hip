@@ -590,6 +590,12 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             load_ids(kt + 3, j + 3 < n, kpid_n);
             load_ids(kt + 2, j + 2 < n, vpid_n);
         }
+        // The first two K operands of S(j+1) (landed before the last barrier) are read now,
+        // so that their LDS latency passes behind the mask, row max and offset raise below
+        // (a read issued after that branch could not be moved above it).
+        const uint16_t* kbase = smem + (P ^ 1) * T::ELEMS;
+        const mfa_u32x4 kpre0 = lds_read16(kbase + k_rd[0]);
+        const mfa_u32x4 kpre1 = lds_read16(kbase + k_rd[1]);
 
         const bool full = use_list ? ((ent >> 28) & 1) != 0 : mfa_tile_full(mask, kBM, BN, qt, kt);
         if (!full) {
@@ -629,26 +635,31 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         // exponentials of S(j), in two phases: phase 0 computes key block 0 of S(j+1)
         // while exponentiating block 1 of S(j); phase 1 computes block 1 of S(j+1)
         // (in the registers block 1 of S(j) just freed) while exponentiating block 0.
-        // The K operands of step t+1 are read from LDS while step t computes.
+        // The K operands are read two steps ahead of their MFMA (a ring of three).
         static_assert(NNB == 2, "two key blocks per tile");
         mfa_u32x4 pop[NNB][2];
-        const uint16_t* kbase = smem + (P ^ 1) * T::ELEMS;
         constexpr int PAIRS = 8 / NKB;   // score pairs exponentiated per MFMA step
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph) {
             const int nbm = ph;          // key block of S(j+1) on the matrix cores
             const int nbe = 1 - ph;      // key block of S(j) on the vector ALUs
             mfa_f32x16 acc = mfa_f32x16{};
-            mfa_u32x4 kop[2];
-            kop[0] = lds_read16(kbase + k_rd[0] + nbm * 32 * D);
+            mfa_u32x4 kop[3];
+            if (ph == 0) {
+                kop[0] = kpre0;
+                kop[1] = kpre1;
+            } else {
+                kop[0] = lds_read16(kbase + k_rd[0] + nbm * 32 * D);
+                kop[1] = lds_read16(kbase + k_rd[1] + nbm * 32 * D);
+            }
 #pragma unroll
             for (int step = 0; step < NKB; ++step) {
                 // K copies: LOADS per stage, LOADS / 2 per phase, at evenly spaced steps
                 if ((step % (2 * NKB / T::LOADS)) == 1)
                     copy_k(rk, MfaInt<P>{}, ph * (T::LOADS / 2) + step / (2 * NKB / T::LOADS));
-                if (step + 1 < NKB)
-                    kop[(step + 1) & 1] = lds_read16(kbase + k_rd[step + 1] + nbm * 32 * D);
-                acc = mfa_mfma32<DT>(kop[step & 1], qreg[step], acc);
+                if (step + 2 < NKB)
+                    kop[(step + 2) % 3] = lds_read16(kbase + k_rd[step + 2] + nbm * 32 * D);
+                acc = mfa_mfma32<DT>(kop[step % 3], qreg[step], acc);
 #pragma unroll
                 for (int e = 0; e < PAIRS; ++e) {
                     const int pr = step * PAIRS + e;   // pair index 0..7 within block nbe
