@@ -35,7 +35,9 @@
  * - Element type: 16-bit storage, MFA_F16 (IEEE half) or MFA_BF16 (bfloat16), the
  *   same for Q, K, V and O.  LSE is float32.  All arithmetic accumulates in fp32.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
- *   call returns without synchronising.
+ *   call returns without synchronising.  A call issues kernel launches only (no
+ *   allocation, memset or synchronisation), so it may be captured in a HIP graph; a
+ *   replay reads whatever the captured buffers hold at that time.
  * - Arguments are validated before anything is launched; on failure a negative
  *   mfa_status is returned and nothing is written.  There is no fallback path.
  * - Visibility (mlx-mfa "Sliding window" feature, window_size=(left, right), -1 =
