@@ -3,6 +3,7 @@ import numpy as np
 
 TOL_O = {"f16": 2e-3, "bf16": 1.5e-2}   # max-abs on O (fp32 accumulation)
 TOL_LSE = 1e-3                          # absolute, on LSE
+U_GRAD = {"f16": 2.0 ** -12, "bf16": 2.0 ** -9}   # unit roundoff of the gradient type
 
 
 def torch_dtype(dtype):
@@ -43,3 +44,20 @@ def assert_close_lse(got: np.ndarray, ref: np.ndarray, what=""):
     err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
     assert err <= TOL_LSE, f"{what}: max |dLSE| = {err:.3e} > {TOL_LSE}"
     return err
+
+
+def assert_close_grads(names, gots, refs, dtype):
+    """Gradients: max |got - ref| <= 8 u times the largest reference magnitude of the
+    group (dQ, dK and dV all scale with |dO|; one of them can be exactly zero, e.g. dQ
+    with a single key)."""
+    M = max(float(np.max(np.abs(r))) if r.size else 0.0 for r in refs)
+    tol = 8 * U_GRAD[dtype] * max(M, 1e-6)
+    bad = []
+    for name, got, ref in zip(names, gots, refs):
+        assert np.all(np.isfinite(got)), f"{name}: non-finite"
+        err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+        m = float(np.max(np.abs(ref))) if ref.size else 0.0
+        print(f"  {name}: max|d|={err:.3e}  max|ref|={m:.3e}  tol={tol:.3e}")
+        if err > tol:
+            bad.append(f"{name}: max |d| = {err:.3e} > {tol:.3e}")
+    assert not bad, "; ".join(bad)

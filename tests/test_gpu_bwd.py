@@ -13,13 +13,12 @@ import pytest
 
 import attn_inputs as A
 import oracle
-from gpu_util import to_bits, to_dev, to_f64
+from gpu_util import assert_close_grads as check
+from gpu_util import to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
 ea = pytest.importorskip("exact_attention_amd")
-
-U = {"f16": 2.0 ** -12, "bf16": 2.0 ** -9}
 
 
 def grads_case(B, Hq, Hkv, Nq, Nk, D, dtype, seed, causal=False, left=-1, right=-1, scale=None):
@@ -39,22 +38,6 @@ def grads_case(B, Hq, Hkv, Nq, Nk, D, dtype, seed, causal=False, left=-1, right=
     info = ea.mfa_last_dispatch()
     assert info["op"] == 7 and info["n_launches"] == 3
     return x, dout_bits, scale, (dq, dk, dv)
-
-
-def check(names, gots, refs, dtype):
-    """8 u times the largest reference gradient magnitude of the three (they all scale
-    with |dO|; a gradient can be exactly zero, e.g. dQ with a single key)."""
-    M = max(float(np.max(np.abs(r))) if r.size else 0.0 for r in refs)
-    tol = 8 * U[dtype] * max(M, 1e-6)
-    bad = []
-    for name, got, ref in zip(names, gots, refs):
-        assert np.all(np.isfinite(got)), f"{name}: non-finite"
-        err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-        m = float(np.max(np.abs(ref))) if ref.size else 0.0
-        print(f"  {name}: max|d|={err:.3e}  max|ref|={m:.3e}  tol={tol:.3e}")
-        if err > tol:
-            bad.append(f"{name}: max |d| = {err:.3e} > {tol:.3e}")
-    assert not bad, "; ".join(bad)
 
 
 def full_check(B, Hq, Hkv, Nq, Nk, D, dtype, seed, causal=False, left=-1, right=-1, scale=None):
