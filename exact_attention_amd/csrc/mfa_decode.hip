@@ -495,83 +495,82 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArg
     }
 }
 
-// One workgroup of 4 waves per (sequence, head).  Wave w merges the splits
-// s = w, w + 4, ...: lane s % 64 holds a split's LSE, the weights are broadcast with
-// readlane and every lane accumulates D/64 columns; the 4 waves are then merged in LDS.
+// One workgroup of 256 threads per (sequence, token, head).  The splits are taken in
+// chunks of ROWS * KPT: thread (row r, column group c) loads the LSE and the 4 columns
+// 4c .. 4c + 3 of splits r, r + ROWS, ... of the chunk, all at once, and keeps a running
+// (max, weight sum, weighted O) for its row, rescaled when a chunk raises the max.  The
+// ROWS rows are then merged in LDS with the same rule:
+//   M = max_r m_r,  W = sum_r 2^(m_r - M) w_r,  O = sum_r 2^(m_r - M) o_r / W.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void mfa_decode_combine_kernel(DecArgs a) {
-    constexpr int PER = D / 64;
-    constexpr int NW = 4;
+    constexpr int TPR = D / 4;          // threads per split row (one float4 each)
+    constexpr int ROWS = 256 / TPR;     // split rows per chunk
+    constexpr int KPT = 8;              // splits per thread per chunk
     const int bh = blockIdx.x;   // (b * nq + n) * Hq + h
     const int b = bh / (a.Hq * a.nq);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+    const int c = t % TPR, r = t / TPR;
     const int L = clamp_len(a.seq_lens[b], a.max_pages);
     const int n_pages_b = (L + kPage - 1) / kPage;
     const int n_used = (n_pages_b + a.chunk_pages - 1) / a.chunk_pages;
     const float* lse_s = a.ws_lse + (size_t)bh * a.S;
-    const float* o_s = a.ws_o + (size_t)bh * a.S * D;
+    const float* o_s = a.ws_o + (size_t)bh * a.S * D + 4 * c;
 
-    // global max of the split LSEs (every wave computes it)
-    float M = -MFA_INF;
-    for (int s = lane; s < n_used; s += 64) M = fmaxf(M, lse_s[s]);
+    float m = -MFA_INF, w = 0.f;
+    mfa_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int base = 0; base < n_used; base += ROWS * KPT) {
+        float ls[KPT];
+        mfa_f32x4 ov[KPT];
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
-    const float M_use = (M == -MFA_INF) ? 0.f : M;
-
-    float acc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    float W = 0.f;
-    // wave w takes splits w, w + NW, ...; 64 of them per pass
-    for (int base = wave; base < n_used; base += 64 * NW) {
-        const int s = base + NW * lane;
-        const float ls = s < n_used ? lse_s[s] : -MFA_INF;
-        const float w = (ls == -MFA_INF) ? 0.f : mfa_exp2(ls - M_use);
-        float wsum = w;
-#pragma unroll
-        for (int x = 32; x >= 1; x >>= 1) wsum += __shfl_xor(wsum, x, 64);
-        W += wsum;
-        const int n = min(64, (n_used - base + NW - 1) / NW);
-#pragma unroll 8
-        for (int k = 0; k < n; ++k) {
-            const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-            const float* src = o_s + (size_t)(base + NW * k) * D + lane * PER;
-            if constexpr (PER == 2) {
-                const float2 v = *(const float2*)src;
-                acc[0] += wk * v.x;
-                acc[1] += wk * v.y;
-            } else {
-                acc[0] += wk * src[0];
-            }
+        for (int k = 0; k < KPT; ++k) {
+            const int s = base + r + ROWS * k;
+            const bool ok = s < n_used;
+            ls[k] = ok ? lse_s[s] : -MFA_INF;
+            ov[k] = ok ? *(const mfa_f32x4*)(o_s + (size_t)s * D) : mfa_f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        float mc = m;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) mc = fmaxf(mc, ls[k]);
+        if (mc == -MFA_INF) continue;   // nothing seen yet (uniform per row)
+        const float f = (m == -MFA_INF) ? 0.f : mfa_exp2(m - mc);
+        w *= f;
+        acc *= f;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const float e = (ls[k] == -MFA_INF) ? 0.f : mfa_exp2(ls[k] - mc);
+            w += e;
+            acc += e * ov[k];
+        }
+        m = mc;
     }
-    __shared__ float sm_acc[NW][D];
-    __shared__ float sm_w[NW];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) sm_acc[wave][lane * PER + i] = acc[i];
-    if (lane == 0) sm_w[wave] = W;
+
+    __shared__ mfa_f32x4 sm_acc[ROWS][TPR];
+    __shared__ float sm_m[ROWS], sm_w[ROWS];
+    sm_acc[r][c] = acc;
+    if (c == 0) {
+        sm_m[r] = m;
+        sm_w[r] = w;
+    }
     __syncthreads();
-    if (wave != 0) return;
+    if (t >= TPR) return;
+    float M = -MFA_INF;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) M = fmaxf(M, sm_m[i]);
+    const float M_use = (M == -MFA_INF) ? 0.f : M;
     float Wt = 0.f;
+    mfa_f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Wt += sm_w[w];
-    float o[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        o[i] = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) o[i] += sm_acc[w][lane * PER + i];
+    for (int i = 0; i < ROWS; ++i) {
+        const float f = (sm_m[i] == -MFA_INF) ? 0.f : mfa_exp2(sm_m[i] - M_use);
+        Wt += f * sm_w[i];
+        o += f * sm_acc[i][t];
     }
     const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
-    uint16_t* op = a.out + (size_t)bh * D + lane * PER;
-    if constexpr (PER == 2) {
-        *(uint32_t*)op = mfa_pack2<DT>(o[0] * inv, o[1] * inv);
-    } else {
-        const uint32_t w2 = mfa_pack2<DT>(o[0] * inv, 0.f);
-        *op = (uint16_t)(w2 & 0xffffu);
-    }
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = Wt > 0.f ? (M_use + mfa_log2(Wt)) * MFA_LN2 : -MFA_INF;
+    mfa_u32x2 packed;
+    packed[0] = mfa_pack2<DT>(o[0] * inv, o[1] * inv);
+    packed[1] = mfa_pack2<DT>(o[2] * inv, o[3] * inv);
+    *(mfa_u32x2*)(a.out + (size_t)bh * D + 4 * t) = packed;
+    if (a.lse != nullptr && t == 0) a.lse[bh] = Wt > 0.f ? (M_use + mfa_log2(Wt)) * MFA_LN2 : -MFA_INF;
 }
 
 template <int D, int DT, int HPW>
