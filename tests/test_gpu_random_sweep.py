@@ -1,0 +1,230 @@
+"""Seeded random sweep: shapes, head grouping, masks, windows, scales, dtypes and
+sequence layouts drawn at random, every entry point against the oracle (to the same
+tolerances as the fixed cases), at sizes the float64 oracle finishes in about a second.
+Each case prints its draw before the GPU call, so a failure names it."""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as A
+import oracle
+from gpu_util import assert_close_grads, assert_close_lse, assert_close_o, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+ea = pytest.importorskip("exact_attention_amd")
+
+
+def dev_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+def dev_u8(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
+
+
+def draw_common(rng):
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    Hkv = int(rng.integers(1, 4))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    return D, dtype, Hkv * g, Hkv
+
+
+def draw_mask(rng, D):
+    causal = bool(rng.integers(0, 2))
+    left = int(rng.integers(0, 300)) if rng.random() < 0.3 else -1
+    right = int(rng.integers(0, 300)) if rng.random() < 0.3 else -1
+    u = rng.random()
+    scale = 1.0 / math.sqrt(D) if u < 0.5 else (float(rng.uniform(0.02, 0.3)) if u < 0.8
+                                                 else -float(rng.uniform(0.02, 0.2)))
+    return causal, left, right, scale
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("i", range(64))
+def test_random_forward(i):
+    rng = np.random.default_rng(7000 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B, Nq, Nk = int(rng.integers(1, 3)), int(rng.integers(1, 700)), int(rng.integers(1, 700))
+    causal, left, right, scale = draw_mask(rng, D)
+    print(f"mfa_fwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} D={D} {dtype} causal={causal} "
+          f"win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.dense_inputs(B, Hq, Hkv, Nq, Nk, D, dtype, 7100 + i)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right)
+    sync()
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention(qf, kf, vf, scale, causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "O")
+    assert_close_lse(L.cpu().numpy(), Lr, "LSE")
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_backward(i):
+    rng = np.random.default_rng(7200 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B, Nq, Nk = int(rng.integers(1, 3)), int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    causal, left, right, scale = draw_mask(rng, D)
+    print(f"mfa_fwd + mfa_bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} D={D} {dtype} "
+          f"causal={causal} win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.dense_inputs(B, Hq, Hkv, Nq, Nk, D, dtype, 7300 + i)
+    dob = A.grad_inputs(B, Hq, Nq, D, dtype, 7400 + i)
+    q, k, v, do = (to_dev(t, dtype) for t in (x.q, x.k, x.v, dob))
+    O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right)
+    dq, dk, dv = ea.mfa_bwd(q, k, v, O, do, L, scale=scale, causal=causal, win_left=left,
+                            win_right=right)
+    sync()
+    qf, kf, vf, dof = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v, dob))
+    refs = oracle.attention_backward(qf, kf, vf, dof, scale, causal, left, right)
+    assert_close_grads(("dQ", "dK", "dV"), [to_f64(t, dtype) for t in (dq, dk, dv)], refs, dtype)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_varlen(i):
+    rng = np.random.default_rng(7500 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B = int(rng.integers(1, 6))
+    lq = rng.integers(0, 500, size=B)
+    # keys: as many as the queries (self-attention packing) or a longer prefix (chunked)
+    lk = lq + (rng.integers(0, 400, size=B) if rng.random() < 0.5 else 0)
+    causal, left, right, scale = draw_mask(rng, D)
+    print(f"mfa_fwd_varlen Hq={Hq} Hkv={Hkv} D={D} {dtype} lq={lq.tolist()} lk={lk.tolist()} "
+          f"causal={causal} win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.varlen_inputs(Hq, Hkv, D, dtype, 7600 + i, seqlens_q=lq, seqlens_k=lk)
+    if x.q.shape[0] == 0 or x.k.shape[0] == 0:
+        pytest.skip("drew no tokens")
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = ea.mfa_fwd_varlen(q, k, v, dev_i32(x.cu_seqlens_q), dev_i32(x.cu_seqlens_k),
+                             int(max(1, lq.max())), int(max(1, lk.max())), scale=scale,
+                             causal=causal, win_left=left, win_right=right)
+    sync()
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention_varlen(qf, kf, vf, x.cu_seqlens_q, x.cu_seqlens_k, scale, causal,
+                                     left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "varlen O")
+    assert_close_lse(L.cpu().numpy(), Lr, "varlen LSE")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_paged_prefill(i):
+    rng = np.random.default_rng(7700 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B = int(rng.integers(1, 5))
+    lq = rng.integers(1, 300, size=B)
+    ctx = rng.integers(0, 1500, size=B)
+    causal, left, right, scale = draw_mask(rng, D)
+    causal = True if rng.random() < 0.7 else causal
+    print(f"mfa_fwd_varlen_paged Hq={Hq} Hkv={Hkv} D={D} {dtype} lq={lq.tolist()} "
+          f"ctx={ctx.tolist()} causal={causal} win=({left},{right}) scale={scale:.4f}", flush=True)
+    p = A.paged_varlen_inputs(Hq, Hkv, D, dtype, 7800 + i, seqlens_q=lq, ctx_lens=ctx,
+                              extra_pages=int(rng.integers(0, 4)))
+    O, L = ea.mfa_fwd_varlen_paged(to_dev(p.q, dtype), to_dev(p.k_pages, dtype), to_dev(p.v_pages, dtype),
+                                   dev_i32(p.block_table), dev_i32(p.seq_lens_k),
+                                   dev_i32(p.cu_seqlens_q), int(lq.max()), int(p.seq_lens_k.max()),
+                                   scale=scale, causal=causal, win_left=left, win_right=right)
+    sync()
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (p.q, p.k_pages, p.v_pages))
+    Or, Lr = oracle.attention_varlen_paged(qf, kf, vf, p.block_table, p.seq_lens_k, p.cu_seqlens_q,
+                                           scale, p.page_size, causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "paged prefill O")
+    assert_close_lse(L.cpu().numpy(), Lr, "paged prefill LSE")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_decode(i):
+    rng = np.random.default_rng(7900 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B = int(rng.integers(1, 7))
+    hi = int(rng.choice([50, 700, 3000]))
+    splits = int(rng.choice([0, 0, 1, 3, 7]))
+    scale = 1.0 / math.sqrt(D) if rng.random() < 0.7 else float(rng.uniform(0.02, 0.3))
+    p = A.paged_inputs(B, Hq, Hkv, D, dtype, 8000 + i, len_lo=0, len_hi=hi,
+                       extra_pages=int(rng.integers(0, 4)))
+    print(f"mfa_decode_paged B={B} Hq={Hq} Hkv={Hkv} D={D} {dtype} lens={p.seq_lens.tolist()} "
+          f"splits={splits} scale={scale:.4f}", flush=True)
+    O, L = ea.mfa_decode_paged(to_dev(p.q, dtype), to_dev(p.k_pages, dtype), to_dev(p.v_pages, dtype),
+                               dev_i32(p.block_table), dev_i32(p.seq_lens), scale=scale,
+                               num_splits=splits)
+    sync()
+    Or, Lr = oracle.decode_paged(oracle.widen(p.q, dtype), oracle.widen(p.k_pages, dtype),
+                                 oracle.widen(p.v_pages, dtype), p.block_table, p.seq_lens, scale,
+                                 p.page_size)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "decode O")
+    assert_close_lse(L.cpu().numpy(), Lr, "decode LSE")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_multi_decode(i):
+    rng = np.random.default_rng(8100 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B, Nq = int(rng.integers(1, 6)), int(rng.integers(1, 5))
+    hi = int(rng.choice([60, 800, 2500]))
+    splits = int(rng.choice([0, 0, 1, 2, 5]))
+    scale = 1.0 / math.sqrt(D)
+    p = A.paged_multi_inputs(B, Nq, Hq, Hkv, D, dtype, 8200 + i, len_lo=0, len_hi=hi,
+                             extra_pages=int(rng.integers(0, 3)))
+    print(f"mfa_decode_paged_multi B={B} Nq={Nq} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
+          f"lens={p.seq_lens.tolist()} splits={splits}", flush=True)
+    O, L = ea.mfa_decode_paged_multi(to_dev(p.q, dtype), to_dev(p.k_pages, dtype),
+                                     to_dev(p.v_pages, dtype), dev_i32(p.block_table),
+                                     dev_i32(p.seq_lens), scale=scale, num_splits=splits)
+    sync()
+    Or, Lr = oracle.decode_paged_multi(oracle.widen(p.q, dtype), oracle.widen(p.k_pages, dtype),
+                                       oracle.widen(p.v_pages, dtype), p.block_table, p.seq_lens,
+                                       scale, p.page_size)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "multi decode O")
+    assert_close_lse(L.cpu().numpy(), Lr, "multi decode LSE")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_ext(i):
+    rng = np.random.default_rng(8300 + i)
+    D, dtype, Hq, Hkv = draw_common(rng)
+    B, Nq, Nk = int(rng.integers(1, 3)), int(rng.integers(1, 600)), int(rng.integers(1, 600))
+    causal, left, right, scale = draw_mask(rng, D)
+    softcap = float(rng.choice([0.0, 5.0, 30.0]))
+    slopes = 2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq) if rng.random() < 0.4 else None
+    bias = None
+    kind = int(rng.integers(0, 4))
+    if kind == 1:
+        bias = rng.standard_normal(Nk)
+    elif kind == 2:
+        bias = rng.standard_normal((Hq, Nk))
+    elif kind == 3:
+        bias = rng.standard_normal((B, Hq, Nk))
+    bm, bq, bk = None, 0, 0
+    if rng.random() < 0.5:
+        bq, bk = int(rng.choice([32, 64, 128])), int(rng.choice([32, 64, 128]))
+        nqb, nkb = -(-Nq // bq), -(-Nk // bk)
+        bm = (rng.random((B, Hq if rng.random() < 0.5 else 1, nqb, nkb)) < 0.6).astype(np.uint8)
+    print(f"mfa_fwd_ext B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} D={D} {dtype} causal={causal} "
+          f"win=({left},{right}) scale={scale:.4f} softcap={softcap} alibi={slopes is not None} "
+          f"bias={kind} mask={None if bm is None else bm.shape} blocks=({bq},{bk})", flush=True)
+    x = A.dense_inputs(B, Hq, Hkv, Nq, Nk, D, dtype, 8400 + i)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = ea.mfa_fwd_ext(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right,
+                          softcap=softcap, alibi_slopes=None if slopes is None else dev_f32(slopes),
+                          bias=None if bias is None else dev_f32(bias),
+                          block_mask=None if bm is None else dev_u8(bm), block_q=bq, block_k=bk)
+    sync()
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    bias_full = None if bias is None else np.broadcast_to(bias, (B, Hq, Nk))
+    bm_full = None if bm is None else np.broadcast_to(bm, (B, Hq) + bm.shape[-2:])
+    Or, Lr = oracle.attention_ext(qf, kf, vf, scale, causal, left, right, softcap=softcap,
+                                  alibi_slopes=slopes, bias=bias_full, block_mask=bm_full,
+                                  block_q=bq, block_k=bk)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "ext O")
+    assert_close_lse(L.cpu().numpy(), Lr, "ext LSE")
