@@ -80,6 +80,7 @@ struct FwdArgs {
     int n_rounds;    // grid = n_rounds * HB
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
+    int chain;       // 1: each workgroup runs query tile n_q_tiles - 1 - r, then tile r
     float scale_log2_abs;  // |scale| * log2(e)
     MfaMask mask;    // dense layout only (packed sequences build theirs per sequence)
     // packed sequences ([total, H, D] token-major, delimited by cu_seqlens)
@@ -159,6 +160,12 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
 
+    // Chained tiles (dense inputs, two wave groups): a workgroup runs a long causal
+    // query tile and then its complementary short one, so every workgroup has the same
+    // work and the second tile starts without a new workgroup launch.
+    constexpr bool CAN_CHAIN = MODE == 0 && GROUPS == 2 && !TILELOG;
+    const int n_rep = (CAN_CHAIN && a.chain) ? 2 : 1;
+    for (int rep = 0; rep < n_rep; ++rep) {
     // ---- which (query tile, batch, head) -------------------------------------------
     const int id = blockIdx.x;
     const int round = id / a.HB;
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // hands the short tiles to the CUs that finish early.  For packed sequences the
     // rounds count down the end of the tile's key range in BM-key units (below), which
     // orders the tiles of all sequences by causal work, whatever their lengths.
-    int qt = a.n_q_tiles - 1 - round;
+    int qt = rep == 0 ? a.n_q_tiles - 1 - round : round;
     int b, h;
     if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
@@ -751,7 +758,11 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         }
         static_assert(NC * 256 * 4 <= GROUPS * 4 * T::ELEMS * 2, "exchange fits in the tile buffers");
         __syncthreads();
-        if (grp == 1) return;
+        if (grp == 1) {
+            if (n_rep == 1) return;
+            __syncthreads();   // group 0 has read the exchange before the next tile's copies
+            continue;
+        }
         const float m1 = xch[0 * 256 + slot];
         const float l1 = xch[1 * 256 + slot];
         const float M = fmaxf(m_run, m1);
@@ -798,6 +809,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         t[2] = n_edge;
         t[3] = n_all ? last : -1;
     }
+    if (n_rep > 1) __syncthreads();
+    }   // rep
 }
 
 template <int D, int DT, int G, bool TL, int MODE>
@@ -812,7 +825,7 @@ void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
 template <int D, int DT, int MODE>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
-    const dim3 grid((unsigned)a.n_rounds * (unsigned)a.HB);
+    const dim3 grid((unsigned)(a.chain ? a.n_rounds / 2 : a.n_rounds) * (unsigned)a.HB);
     if (groups == 2) {
         if (tilelog) launch_sign<D, DT, 2, true, MODE>(a, grid, stream, neg);
         else launch_sign<D, DT, 2, false, MODE>(a, grid, stream, neg);
@@ -820,10 +833,10 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
         if (tilelog) launch_sign<D, DT, 1, true, MODE>(a, grid, stream, neg);
         else launch_sign<D, DT, 1, false, MODE>(a, grid, stream, neg);
     }
-    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s>", D,
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
              MODE == 3 ? ",ext" : MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
-             tilelog ? ",tilelog" : "", neg ? ",neg" : "");
+             tilelog ? ",tilelog" : "", neg ? ",neg" : "", a.chain ? ",chained" : "");
     info->BM = kBM;
     info->BN = kBN;
     info->waves = groups * kGroupThreads / 64;
@@ -854,7 +867,8 @@ int mfa_fwd_bn(int) { return kBN; }
 // each other's prologue and epilogue, which is best when the grid has many query
 // tiles.  A small grid (at most two workgroups per CU: every workgroup resident at
 // once, so the longest query tile bounds the run) instead gets one 8-wave workgroup
-// per CU whose two groups split the key range of the query tile.
+// per CU whose two groups split the key range of the query tile; for dense inputs with
+// an even number of query tiles such a workgroup then runs two complementary tiles.
 int mfa_fwd_groups(long long q_tiles, int Hq, int num_cus) {
     return q_tiles * Hq <= 2LL * num_cus ? 2 : 1;
 }
@@ -917,6 +931,7 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     long long q_tiles = (long long)a.n_q_tiles * pr.B;
     if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
     const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
+    a.chain = (mode == 0 && groups == 2 && !tl && a.n_q_tiles % 2 == 0) ? 1 : 0;
     if (mode == 3) return launch_dt<3>(pr, a, stream, groups, tl, neg, info);
     if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
     if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);

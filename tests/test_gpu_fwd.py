@@ -90,6 +90,30 @@ def test_both_workgroup_layouts(case):
             assert_close_lse(L[:, h:h + 1].cpu().numpy(), Lr, f"LSE H={H} h={h}")
 
 
+@pytest.mark.parametrize("case", [
+    # Hq, Hkv, Nq, Nk, D, dtype, causal, left, right, chained
+    (4, 4, 512, 512, 128, "f16", True, -1, -1, True),      # 4 tiles: pairs (3, 0), (2, 1)
+    (4, 2, 400, 400, 128, "bf16", True, -1, -1, True),     # partial last tile, GQA
+    (2, 2, 256, 700, 64, "f16", True, -1, -1, True),       # Nq < Nk (bottom-right)
+    (2, 1, 512, 512, 128, "bf16", False, -1, -1, True),    # no mask: equal tiles
+    (4, 4, 768, 768, 128, "f16", True, 200, 0, True),      # window
+    (2, 2, 384, 384, 128, "f16", True, -1, -1, False),     # 3 tiles: not chained
+])
+def test_chained_tiles(case):
+    # a small grid of 8-wave workgroups with an even number of query tiles runs two
+    # complementary query tiles per workgroup; every row against the oracle
+    Hq, Hkv, Nq, Nk, D, dtype, causal, left, right, chained = case
+    x = A.dense_inputs(1, Hq, Hkv, Nq, Nk, D, dtype, 60 + Nq + Hq)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = run(q, k, v, 1 / math.sqrt(D), causal, left, right)
+    info = ea.mfa_last_dispatch()
+    assert "groups=2" in info["kernel"] and (",chained" in info["kernel"]) == chained, info["kernel"]
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention(qf, kf, vf, 1 / math.sqrt(D), causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "chained O")
+    assert_close_lse(L.cpu().numpy(), Lr, "chained LSE")
+
+
 def test_fully_masked_rows_exact():
     import torch
     x = A.dense_inputs(1, 2, 2, 300, 90, 128, "f16", 5)
