@@ -65,6 +65,7 @@ struct BwdArgs {
     float scale;       // signed
     float scale_log2;  // scale * log2(e)
     MfaMask mask;
+    int chain_q;       // 1: a dQ workgroup runs query tile qt, then nqt - 1 - qt
 };
 
 // ---- prep: D_i and LSE in the log2 domain --------------------------------------------
@@ -448,10 +449,17 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     const int l32 = lane & 31;
     const MfaMask& m = a.mask;
     const int nqt = (a.Nq + 127) >> 7;
-    const int lid = xcd_logical_id(nqt * a.B * a.Hq);
-    const int bh = lid / nqt;
+    // Chained tiles: a workgroup runs a query tile and then its mirror image
+    // nqt - 1 - qt, so that under a causal mask every workgroup has the same work and the
+    // second tile starts without a new workgroup launch.
+    const int n_rep = a.chain_q ? 2 : 1;
+    const int n_units = nqt / n_rep;
+    const int lid = xcd_logical_id(n_units * a.B * a.Hq);
+    const int bh = lid / n_units;
+    for (int rep = 0; rep < n_rep; ++rep) {
     // causal masks give the last query tiles the most keys: they start first
-    const int qt = (m.right_eff >= 0 && m.left < 0) ? nqt - 1 - (lid - bh * nqt) : lid - bh * nqt;
+    const int qt_first = (m.right_eff >= 0 && m.left < 0) ? nqt - 1 - (lid - bh * n_units) : lid - bh * n_units;
+    const int qt = rep == 0 ? qt_first : nqt - 1 - qt_first;
     const int b = bh / a.Hq, h = bh - b * a.Hq;
     const int kvh = h / a.g;
     const int qw0 = qt * 128 + rblk * 32;   // this wave's first query row
@@ -603,7 +611,11 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
             }
     }
     block_barrier();
-    if (kh == 1) return;
+    if (kh == 1) {
+        if (n_rep == 1) return;
+        block_barrier();   // the other half has read the exchange (next tile's copies)
+        continue;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -628,6 +640,8 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
                 *(mfa_u32x2*)(dqp + d) = w;
             }
     }
+    if (n_rep > 1) block_barrier();
+    }   // rep
 }
 
 template <int D, int DT>
@@ -639,11 +653,11 @@ int launch(const BwdArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
     const dim3 g1((unsigned)((a.Nk + 127) / 128), (unsigned)(a.B * a.Hkv));
     hipLaunchKernelGGL((mfa_bwd_dkv_kernel<D, DT>), g1, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
-    const dim3 g2((unsigned)((a.Nq + 127) / 128), (unsigned)(a.B * a.Hq));
+    const dim3 g2((unsigned)((a.Nq + 127) / 128 / (a.chain_q ? 2 : 1)), (unsigned)(a.B * a.Hq));
     hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
-    snprintf(info->kernel, sizeof(info->kernel), "mfa_bwd_dkv_kernel+mfa_bwd_dq_kernel<D=%d,%s>", D,
-             DT == MFA_DT_F16 ? "f16" : "bf16");
+    snprintf(info->kernel, sizeof(info->kernel), "mfa_bwd_dkv_kernel+mfa_bwd_dq_kernel<D=%d,%s%s>", D,
+             DT == MFA_DT_F16 ? "f16" : "bf16", a.chain_q ? ",dq chained" : "");
     info->grid[0] = (int)g1.x;
     info->grid[1] = (int)g1.y;
     info->grid[2] = 1;
@@ -679,6 +693,7 @@ int mfa_bwd_launch(const MfaBwdProblem& p, hipStream_t stream, mfa_dispatch_info
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;
     a.mask = mfa_make_mask(p.Nq, p.Nk, p.causal, p.left, p.right);
+    a.chain_q = ((p.Nq + 127) / 128) % 2 == 0 ? 1 : 0;
     if (p.D == 128)
         return p.dtype == MFA_F16 ? launch<128, MFA_DT_F16>(a, stream, info) : launch<128, MFA_DT_BF16>(a, stream, info);
     return p.dtype == MFA_F16 ? launch<64, MFA_DT_F16>(a, stream, info) : launch<64, MFA_DT_BF16>(a, stream, info);
