@@ -287,64 +287,67 @@ def block_mask_inputs(B: int, H: int, Nq: int, Nk: int, block_q: int, block_k: i
     return bm
 
 
-# The benchmark workloads.  Shapes follow the mlx-mfa "Performance" table
+# The benchmark workloads, by name.  Shapes follow the mlx-mfa "Performance" table
 # (B=2, H=8, f16, D=128, causal / window 512), its GQA statement (Hq a multiple of
 # Hkv), and the MXFlashAttn paged split-KV decode setting (pages of 16 tokens,
 # Hq=32, Hkv=8, D=128).
-CONFIGS = {
-    1: dict(name="tiny_dense", B=1, Hq=2, Hkv=2, Nq=128, Nk=128, D=64, dtype=F16,
-            causal=False, left=-1, right=-1, seed=101),
-    2: dict(name="dense_causal_prefill", B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128,
-            dtype=F16, causal=True, left=-1, right=-1, seed=102),
-    3: dict(name="gqa_causal_long_prefill", B=1, Hq=32, Hkv=8, Nq=16384, Nk=16384,
-            D=128, dtype=BF16, causal=True, left=-1, right=-1, seed=103),
-    4: dict(name="sliding_window_causal", B=2, Hq=8, Hkv=8, Nq=8192, Nk=8192, D=128,
-            dtype=F16, causal=True, left=512, right=0, seed=104),
-    5: dict(name="paged_splitkv_decode", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
-            page_size=16, len_lo=1024, len_hi=32768, seed=105),
+WORKLOADS = {
+    "tiny_dense": dict(B=1, Hq=2, Hkv=2, Nq=128, Nk=128, D=64, dtype=F16, causal=False, left=-1,
+                       right=-1, seed=101),
+    "dense_causal_prefill": dict(B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128, dtype=F16, causal=True,
+                                 left=-1, right=-1, seed=102),
+    "gqa_causal_long_prefill": dict(B=1, Hq=32, Hkv=8, Nq=16384, Nk=16384, D=128, dtype=BF16,
+                                    causal=True, left=-1, right=-1, seed=103),
+    "sliding_window_causal": dict(B=2, Hq=8, Hkv=8, Nq=8192, Nk=8192, D=128, dtype=F16, causal=True,
+                                  left=512, right=0, seed=104),
+    "paged_splitkv_decode": dict(B=16, Hq=32, Hkv=8, D=128, dtype=BF16, page_size=16, len_lo=1024,
+                                 len_hi=32768, seed=105),
     # packed variable-length causal prefill (mlx-mfa "Variable-length" feature): a
     # serving-style mix of prompt lengths, GQA heads of the long-context workload
-    6: dict(name="packed_varlen_causal_prefill", B=16, Hq=32, Hkv=8, D=128, dtype=BF16,
-            causal=True, left=-1, right=-1, len_lo=256, len_hi=4096, seed=106),
+    "packed_varlen_causal_prefill": dict(B=16, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True, left=-1,
+                                         right=-1, len_lo=256, len_hi=4096, seed=106),
     # chunked prefill over the paged cache (mlx-mfa "Paged + packed varlen queries"):
     # new chunks of 512..2048 tokens after 1024..16384 cached ones, pages of 16
+    "paged_chunked_prefill": dict(B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True, left=-1,
+                                  right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
+                                  ctx_hi=16384, seed=107),
     # speculative verification: 4 new tokens per sequence over the decode workload's cache
-    8: dict(name="paged_multi_query_decode", B=16, Nq=4, Hq=32, Hkv=8, D=128, dtype=BF16,
-            page_size=16, len_lo=1024, len_hi=32768, seed=108),
+    "paged_multi_query_decode": dict(B=16, Nq=4, Hq=32, Hkv=8, D=128, dtype=BF16, page_size=16,
+                                     len_lo=1024, len_hi=32768, seed=108),
     # block-sparse causal prefill (mlx-mfa "Block-sparse attention"): 128 x 128 blocks
     # on with probability 1/4, plus the diagonal
-    9: dict(name="block_sparse_causal_prefill", B=1, Hq=16, Hkv=16, Nq=16384, Nk=16384, D=128,
-            dtype=F16, causal=True, left=-1, right=-1, block_q=128, block_k=128, density=0.25,
-            seed=109),
+    "block_sparse_causal_prefill": dict(B=1, Hq=16, Hkv=16, Nq=16384, Nk=16384, D=128, dtype=F16,
+                                        causal=True, left=-1, right=-1, block_q=128, block_k=128,
+                                        density=0.25, seed=109),
     # training step after the prefill: the backward over the dense causal prefill shape,
     # in bf16 (the mlx-bun page's backward; upstream gradient from grad_inputs)
-    10: dict(name="dense_causal_backward", B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128,
-             dtype=BF16, causal=True, left=-1, right=-1, seed=110),
-    7: dict(name="paged_chunked_prefill", B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True,
-            left=-1, right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,
-            ctx_hi=16384, seed=107),
+    "dense_causal_backward": dict(B=2, Hq=8, Hkv=8, Nq=4096, Nk=4096, D=128, dtype=BF16,
+                                  causal=True, left=-1, right=-1, seed=110),
 }
 
 
-def config(i: int) -> dict:
-    c = dict(CONFIGS[i])
+def workload(name: str) -> dict:
+    """The named workload's parameters (a copy), with name and scale = 1 / sqrt(D)."""
+    c = dict(WORKLOADS[name])
+    c["name"] = name
     c["scale"] = 1.0 / math.sqrt(c["D"])
     return c
 
 
-def config_inputs(i: int):
-    c = config(i)
-    if i == 8:
+def workload_inputs(name: str):
+    """The named workload's seeded inputs (the generator its layout calls for)."""
+    c = workload(name)
+    if name == "paged_multi_query_decode":
         return paged_multi_inputs(c["B"], c["Nq"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"],
                                   len_lo=c["len_lo"], len_hi=c["len_hi"], page_size=c["page_size"])
-    if i == 7:
+    if name == "paged_chunked_prefill":
         return paged_varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
                                    new_lo=c["new_lo"], new_hi=c["new_hi"], ctx_lo=c["ctx_lo"],
                                    ctx_hi=c["ctx_hi"], page_size=c["page_size"])
-    if i == 6:
+    if name == "packed_varlen_causal_prefill":
         return varlen_inputs(c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"], B=c["B"],
                              len_lo=c["len_lo"], len_hi=c["len_hi"])
-    if i == 5:
+    if name in ("paged_splitkv_decode",):
         return paged_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["dtype"], c["seed"],
                             len_lo=c["len_lo"], len_hi=c["len_hi"],
                             page_size=c["page_size"])

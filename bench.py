@@ -23,7 +23,8 @@ sides of each timed region.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, and scales to TFLOP/s.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workloads 2,3,4,5,6,7,8,9,10] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--workloads NAME,...] [--no-cpu-baseline]
+(workload names as in attn_inputs.WORKLOADS; default: all but tiny_dense)
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ PEAK_MFMA_F16 = 2500.0   # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 
 METRIC = "attn fwd TFLOP/s (D=128 causal fp16) + paged decode HBM GB/s, % roofline"
+HEAD = "dense_causal_prefill"   # the workload whose throughput is `value`
 
 # HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE / WRITE_SIZE,
 # scaled by a plain copy kernel of known size) is kept in profiles/traffic.json
@@ -119,12 +121,12 @@ def time_calls(fn, steps):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def setup_prefill(i):
-    """Device inputs and one step (one mfa_fwd call) of prefill workload i."""
+def setup_prefill(name):
+    """Device inputs and one step (one mfa_fwd call) of the named dense prefill workload."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(i)
-    x = A.config_inputs(i)
+    c = A.workload(name)
+    x = A.workload_inputs(name)
     q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
@@ -137,9 +139,9 @@ def setup_prefill(i):
     return step
 
 
-def bench_prefill(i, step, steps):
+def bench_prefill(name, step, steps):
     import exact_attention_amd as ea
-    c = A.config(i)
+    c = A.workload(name)
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     flop = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], c["left"], c["right"]) \
@@ -151,7 +153,7 @@ def bench_prefill(i, step, steps):
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": tf / PEAK_MFMA_F16,
-                     "traffic": measured_traffic(f"fwd_config{i}", "fwd")},
+                     "traffic": measured_traffic(name, "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "planned_tiles": info["planned"],
         "dtype": c["dtype"],
     }
@@ -161,8 +163,8 @@ def setup_varlen():
     """Device inputs and one step (one mfa_fwd_varlen call) of the packed workload."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(6)
-    x = A.config_inputs(6)
+    c = A.workload("packed_varlen_causal_prefill")
+    x = A.workload_inputs("packed_varlen_causal_prefill")
     q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
     cq = torch.from_numpy(x.cu_seqlens_q).to("cuda")
     ck = torch.from_numpy(x.cu_seqlens_k).to("cuda")
@@ -181,7 +183,7 @@ def setup_varlen():
 
 def bench_varlen(step, steps):
     import exact_attention_amd as ea
-    c = A.config(6)
+    c = A.workload("packed_varlen_causal_prefill")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     lq, lk = step.lens
@@ -194,7 +196,7 @@ def bench_varlen(step, steps):
                     f"(total {int(lq.sum())} tokens)",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config6", "fwd")},
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("packed_varlen_causal_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -203,8 +205,8 @@ def setup_chunked():
     """Device inputs and one step (one mfa_fwd_varlen_paged call) of the chunked prefill."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(7)
-    p = A.config_inputs(7)
+    c = A.workload("paged_chunked_prefill")
+    p = A.workload_inputs("paged_chunked_prefill")
     q = to_dev(p.q, c["dtype"])
     kp = to_dev(p.k_pages, c["dtype"])
     vp = to_dev(p.v_pages, c["dtype"])
@@ -227,7 +229,7 @@ def setup_chunked():
 
 def bench_chunked(step, steps):
     import exact_attention_amd as ea
-    c = A.config(7)
+    c = A.workload("paged_chunked_prefill")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     lq, lk = step.lens
@@ -240,7 +242,7 @@ def bench_chunked(step, steps):
                     f"cached keys {int(lk.sum())}",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config7", "fwd")},
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("paged_chunked_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -259,8 +261,8 @@ def setup_decode():
     """Device inputs and one step (one mfa_decode_paged call) of the paged decode workload."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(5)
-    p = A.config_inputs(5)
+    c = A.workload("paged_splitkv_decode")
+    p = A.workload_inputs("paged_splitkv_decode")
     q = to_dev(p.q, c["dtype"])
     kp = to_dev(p.k_pages, c["dtype"])
     vp = to_dev(p.v_pages, c["dtype"])
@@ -281,7 +283,7 @@ def setup_decode():
 
 def bench_decode(step, steps):
     import exact_attention_amd as ea
-    c = A.config(5)
+    c = A.workload("paged_splitkv_decode")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"])
@@ -291,7 +293,7 @@ def bench_decode(step, steps):
                     f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
         "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("decode_config5", "decode")},
+                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("paged_splitkv_decode", "decode")},
         "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
         "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
     }
@@ -301,8 +303,8 @@ def setup_multi():
     """Device inputs and one step (one mfa_decode_paged_multi call) of the 4-token decode."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(8)
-    p = A.config_inputs(8)
+    c = A.workload("paged_multi_query_decode")
+    p = A.workload_inputs("paged_multi_query_decode")
     q = to_dev(p.q, c["dtype"])
     kp = to_dev(p.k_pages, c["dtype"])
     vp = to_dev(p.v_pages, c["dtype"])
@@ -323,7 +325,7 @@ def setup_multi():
 
 def bench_multi(step, steps):
     import exact_attention_amd as ea
-    c = A.config(8)
+    c = A.workload("paged_multi_query_decode")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"], c["Nq"])
@@ -333,7 +335,7 @@ def bench_multi(step, steps):
                     f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
         "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("decode_config8", "decode")},
+                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("paged_multi_query_decode", "decode")},
         "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
         "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
     }
@@ -354,8 +356,8 @@ def setup_sparse():
     """Device inputs and one step (one mfa_fwd_ext call) of the block-sparse prefill."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(9)
-    x = A.config_inputs(9)
+    c = A.workload("block_sparse_causal_prefill")
+    x = A.workload_inputs("block_sparse_causal_prefill")
     bm = A.block_mask_inputs(c["B"], c["Hq"], c["Nq"], c["Nk"], c["block_q"], c["block_k"],
                              c["density"], c["seed"] + 1000)
     q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
@@ -374,7 +376,7 @@ def setup_sparse():
 
 def bench_sparse(step, steps):
     import exact_attention_amd as ea
-    c = A.config(9)
+    c = A.workload("block_sparse_causal_prefill")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     flop = 4.0 * c["D"] * step.pairs
@@ -386,7 +388,7 @@ def bench_sparse(step, steps):
                     f"({step.pairs / (dense / (4.0 * c['D'])):.3f} of the causal pairs)",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("fwd_config9", "fwd")},
+                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("block_sparse_causal_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -396,8 +398,8 @@ def setup_backward():
     backward over the dense causal prefill shape."""
     import torch
     import exact_attention_amd as ea
-    c = A.config(10)
-    x = A.config_inputs(10)
+    c = A.workload("dense_causal_backward")
+    x = A.workload_inputs("dense_causal_backward")
     q, k, v = (to_dev(t, c["dtype"]) for t in (x.q, x.k, x.v))
     do = to_dev(A.grad_inputs(c["B"], c["Hq"], c["Nq"], c["D"], c["dtype"], c["seed"] + 1000),
                 c["dtype"])
@@ -415,7 +417,7 @@ def setup_backward():
 
 def bench_backward(step, steps):
     import exact_attention_amd as ea
-    c = A.config(10)
+    c = A.workload("dense_causal_backward")
     ms, wall = time_calls(step, steps)
     info = ea.mfa_last_dispatch()
     # 10 D FLOP per visible pair: the five products S = Q K^T, dP = dO V^T, dV = P^T dO,
@@ -428,7 +430,7 @@ def bench_backward(step, steps):
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": tf / PEAK_MFMA_F16,
-                     "traffic": measured_traffic("bwd_config10", "bwd")},
+                     "traffic": measured_traffic("dense_causal_backward", "bwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -437,8 +439,8 @@ def cpu_baseline(budget_s=10.0):
     """The float64 oracle on this host over whole heads of the dense causal prefill."""
     import oracle
     from threadpoolctl import threadpool_info
-    c = A.config(2)
-    x = A.config_inputs(2)
+    c = A.workload("dense_causal_prefill")
+    x = A.workload_inputs("dense_causal_prefill")
     q, k, v = (oracle.widen(t, c["dtype"]) for t in (x.q, x.k, x.v))
     pairs = visible_pairs(c["Nq"], c["Nk"], True, -1, -1)
     done = 0
@@ -466,7 +468,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="2,3,4,5,6,7,8,9,10")
+    ap.add_argument("--workloads", default=",".join(w for w in A.WORKLOADS if w != "tiny_dense"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -482,37 +484,31 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ea.lib()
 
-    wl = [int(s) for s in args.workloads.split(",") if s]
-    if 2 not in wl:
-        wl = [2] + wl
-    setup = {5: setup_decode, 6: setup_varlen, 7: setup_chunked, 8: setup_multi, 9: setup_sparse,
-             10: setup_backward}
-    steps = {i: (setup[i]() if i in setup else setup_prefill(i)) for i in wl}
+    wl = [s for s in args.workloads.split(",") if s]
+    for name in wl:
+        if name not in A.WORKLOADS:
+            raise SystemExit(f"unknown workload {name!r}; known: {', '.join(A.WORKLOADS)}")
+    if HEAD not in wl:
+        wl = [HEAD] + wl
+    setup = {"paged_splitkv_decode": setup_decode, "packed_varlen_causal_prefill": setup_varlen,
+             "paged_chunked_prefill": setup_chunked, "paged_multi_query_decode": setup_multi,
+             "block_sparse_causal_prefill": setup_sparse, "dense_causal_backward": setup_backward}
+    timed = {"paged_splitkv_decode": bench_decode, "packed_varlen_causal_prefill": bench_varlen,
+             "paged_chunked_prefill": bench_chunked, "paged_multi_query_decode": bench_multi,
+             "block_sparse_causal_prefill": bench_sparse, "dense_causal_backward": bench_backward}
+    steps = {n: (setup[n]() if n in setup else setup_prefill(n)) for n in wl}
     # the W untimed warm-up steps of every workload run first, so that the first timed
     # workload does not meet a GPU still ramping its clocks
-    for i in wl:
+    for n in wl:
         for _ in range(args.warmup):
-            steps[i]()
+            steps[n]()
     torch.cuda.synchronize()
     res = {}
-    for i in wl:
-        if i == 5:
-            res[i] = bench_decode(steps[i], args.steps)
-        elif i == 6:
-            res[i] = bench_varlen(steps[i], args.steps)
-        elif i == 7:
-            res[i] = bench_chunked(steps[i], args.steps)
-        elif i == 8:
-            res[i] = bench_multi(steps[i], args.steps)
-        elif i == 9:
-            res[i] = bench_sparse(steps[i], args.steps)
-        elif i == 10:
-            res[i] = bench_backward(steps[i], args.steps)
-        else:
-            res[i] = bench_prefill(i, steps[i], args.steps)
-        print(f"# workload {i}: " + json.dumps(res[i]), file=sys.stderr, flush=True)
+    for n in wl:
+        res[n] = timed[n](steps[n], args.steps) if n in timed else bench_prefill(n, steps[n], args.steps)
+        print(f"# workload {n}: " + json.dumps(res[n]), file=sys.stderr, flush=True)
 
-    head = res[2]
+    head = res[HEAD]
     line = {
         "metric": METRIC,
         "value": round(head["tflops"], 3),
@@ -533,11 +529,11 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     line["workloads"] = {
-        str(i): {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
-        for i, r in res.items()}
-    if 5 in res:
-        line["decode_gbs"] = round(res[5]["gbs"], 1)
-        line["decode_roofline"] = res[5]["roofline"]
+        n: {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+        for n, r in res.items()}
+    if "paged_splitkv_decode" in res:
+        line["decode_gbs"] = round(res["paged_splitkv_decode"]["gbs"], 1)
+        line["decode_roofline"] = res["paged_splitkv_decode"]["roofline"]
     print(json.dumps(line), flush=True)
 
 

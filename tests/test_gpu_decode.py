@@ -80,15 +80,15 @@ def test_empty_sequence():
     assert_close_lse(L.cpu().numpy()[1:], Lr[1:])
 
 
-def test_config5_full():
-    c = A.config(5)
-    p = A.config_inputs(5)
+def test_paged_decode_workload_full():
+    c = A.workload("paged_splitkv_decode")
+    p = A.workload_inputs("paged_splitkv_decode")
     d = Dev(p)
     O, L = run(d, c["scale"])
     Or, Lr = ref(p, c["scale"])
-    eo = assert_close_o(to_f64(O, "bf16"), Or, "bf16", "config 5")
-    el = assert_close_lse(L.cpu().numpy(), Lr, "config 5")
-    print(f"config 5: max|dO|={eo:.2e} max|dLSE|={el:.2e} seq_lens={p.seq_lens.tolist()}")
+    eo = assert_close_o(to_f64(O, "bf16"), Or, "bf16", "paged decode workload")
+    el = assert_close_lse(L.cpu().numpy(), Lr, "paged decode workload")
+    print(f"paged decode workload: max|dO|={eo:.2e} max|dLSE|={el:.2e} seq_lens={p.seq_lens.tolist()}")
 
 
 def test_split_count_invariance():

@@ -127,8 +127,8 @@ def test_deterministic():
 def test_full_size_verification_workload():
     # 4 new tokens per sequence over the decode workload's cache shape, every row checked
     import torch
-    c = A.config(8)
-    p = A.config_inputs(8)
+    c = A.workload("paged_multi_query_decode")
+    p = A.workload_inputs("paged_multi_query_decode")
     O, L = run(Dev(p), c["scale"])
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all())
     Or, Lr = ref(p, c["scale"])

@@ -37,11 +37,11 @@ def dense_case(B, Hq, Hkv, Nq, Nk, D, dtype, seed, causal, left=-1, right=-1, sc
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_config1_tiny(causal):
-    c = A.config(1)
+def test_tiny_workload(causal):
+    c = A.workload("tiny_dense")
     eo, el = dense_case(c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"], c["dtype"], c["seed"],
                         causal)
-    print(f"config1 causal={causal}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+    print(f"tiny workload causal={causal}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
 
 
 EDGE = [
@@ -218,24 +218,24 @@ def sampled_rows(B, Hq, Nq, n, seed):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_configs_sampled(cfg):
-    c = A.config(cfg)
-    x = A.config_inputs(cfg)
+@pytest.mark.parametrize("name", ["dense_causal_prefill", "gqa_causal_long_prefill", "sliding_window_causal"])
+def test_full_size_workloads_sampled(name):
+    c = A.workload(name)
+    x = A.workload_inputs(name)
     dt = c["dtype"]
     q, k, v = (to_dev(t, dt) for t in (x.q, x.k, x.v))
     O, L = run(q, k, v, c["scale"], c["causal"], c["left"], c["right"])
     import torch
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all())
-    rows = sampled_rows(c["B"], c["Hq"], c["Nq"], 96, cfg)
+    rows = sampled_rows(c["B"], c["Hq"], c["Nq"], 96, c["seed"])
     qf, kf, vf = (oracle.widen(t, dt) for t in (x.q, x.k, x.v))
     Or, Lr = oracle.attention(qf, kf, vf, c["scale"], c["causal"], c["left"], c["right"], rows=rows)
     idx = tuple(np.array(rows).T)
     Og = to_f64(O, dt)[idx]
     Lg = L.cpu().numpy()[idx]
-    eo = assert_close_o(Og, Or, dt, f"config {cfg}")
-    el = assert_close_lse(Lg, Lr, f"config {cfg}")
+    eo = assert_close_o(Og, Or, dt, f"{name}")
+    el = assert_close_lse(Lg, Lr, f"{name}")
     info = ea.mfa_last_dispatch()
     plan, _ = ea.mfa_plan_fwd(c["Nq"], c["Nk"], c["D"], 0, c["causal"], c["left"], c["right"], False)
     assert info["planned"] == plan["visited"] * c["B"] * c["Hq"]
-    print(f"config {cfg}: max|dO|={eo:.2e} max|dLSE|={el:.2e} kernel={info['kernel']}")
+    print(f"{name}: max|dO|={eo:.2e} max|dLSE|={el:.2e} kernel={info['kernel']}")

@@ -180,8 +180,8 @@ def test_full_size_packed_workload_sampled():
     # the packed causal prefill workload at full size, checked on sampled rows: the first,
     # the last and a middle token of every sequence (first and last head) plus random rows
     import torch
-    c = A.config(6)
-    x = A.config_inputs(6)
+    c = A.workload("packed_varlen_causal_prefill")
+    x = A.workload_inputs("packed_varlen_causal_prefill")
     O, L = run(x, c["scale"], c["causal"])
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all())
     cu = x.cu_seqlens_q

@@ -126,8 +126,8 @@ def test_one_token_chunks_match_decode():
 
 def test_full_size_chunked_prefill_sampled():
     import torch
-    c = A.config(7)
-    p = A.config_inputs(7)
+    c = A.workload("paged_chunked_prefill")
+    p = A.workload_inputs("paged_chunked_prefill")
     O, L = run(p, c["scale"], c["causal"])
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all())
     cu = p.cu_seqlens_q

@@ -50,8 +50,8 @@ def test_paged_layout():
     assert np.all(p.v_pages[unused] == A.NAN_BITS["f16"])
 
 
-def test_config5_shape():
-    c = A.config(5)
+def test_paged_decode_workload_shape():
+    c = A.workload("paged_splitkv_decode")
     assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (16, 32, 8, 128, 16)
     assert abs(c["scale"] - 128 ** -0.5) < 1e-15
 
@@ -70,10 +70,10 @@ def test_varlen_layout():
     assert c.cu_seqlens_q.tolist() == [0, 3, 3, 8] and c.cu_seqlens_k.tolist() == [0, 7, 9, 14]
 
 
-def test_config6_shape():
-    c = A.config(6)
+def test_packed_prefill_workload_shape():
+    c = A.workload("packed_varlen_causal_prefill")
     assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["causal"]) == (16, 32, 8, 128, True)
-    x = A.config_inputs(6)
+    x = A.workload_inputs("packed_varlen_causal_prefill")
     L = np.diff(x.cu_seqlens_q)
     assert L.min() >= 256 and L.max() <= 4096 and x.q.shape[1:] == (32, 128)
 
@@ -86,12 +86,12 @@ def test_paged_varlen_layout():
     assert p.block_table.shape == (3, 3) and p.block_table[0, 1] == -1
     used = np.concatenate([p.block_table[b, : -(-int(L) // 16)] for b, L in enumerate(p.seq_lens_k)])
     assert len(set(used.tolist())) == len(used) == 7
-    c = A.config(7)
+    c = A.workload("paged_chunked_prefill")
     assert (c["B"], c["Hq"], c["Hkv"], c["D"], c["page_size"]) == (8, 32, 8, 128, 16)
 
 
-def test_grad_inputs_and_backward_config():
-    c = A.config(10)
+def test_grad_inputs_and_backward_workload():
+    c = A.workload("dense_causal_backward")
     assert (c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"]) == (2, 8, 8, 4096, 4096, 128)
     assert c["dtype"] == "bf16" and c["causal"]
     g0 = A.grad_inputs(1, 2, 64, 128, "bf16", 5)

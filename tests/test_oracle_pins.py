@@ -245,8 +245,8 @@ def pin_visited_tiles():
     assert oracle.visited_tiles(256, 64, 128, 64, True, -1, -1)[0] == []
 
 
-def pin_config4_pairs():
-    # config 4 (N=8192, causal, left=512, right=0): the inclusive reading gives
+def pin_window_workload_pairs():
+    # the sliding-window workload (N=8192, causal, left=512, right=0): the inclusive reading gives
     # min(i, 512) + 1 visible keys per row.
     N, W = 8192, 512
     i = np.arange(N)
@@ -565,7 +565,7 @@ PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_pro
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
         pin_fully_masked_rows, pin_lse_merge_identity, pin_decode_paged, pin_visited_tiles,
-        pin_config4_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
+        pin_window_workload_pairs, pin_varlen_block_diagonal, pin_varlen_lower_right,
         pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged,
         pin_decode_multi, pin_ext_scalar, pin_ext_bias_torch, pin_ext_limits_and_blocks,
         pin_backward_torch_autograd, pin_backward_finite_differences,
