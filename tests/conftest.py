@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests must run on a GPU machine; on a machine without one they are skipped with
+    # GPU tests need an MI355X; on a machine without a GPU they are skipped with
     # a reason rather than silently passing.
     try:
         import torch
