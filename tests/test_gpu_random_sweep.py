@@ -1,7 +1,13 @@
 """Seeded random sweep: shapes, head grouping, masks, windows, scales, dtypes and
-sequence layouts drawn at random, every entry point against the oracle (to the same
-tolerances as the fixed cases), at sizes the float64 oracle finishes in about a second.
-Each case prints its draw before the GPU call, so a failure names it."""
+sequence layouts drawn at random, every entry point against the oracle, at sizes the
+float64 oracle finishes in about a second.  Each case prints its draw before the GPU
+call, so a failure names it.
+
+Tolerances: those of the fixed cases, except that an element of O may also be off by
+what the rounding of the arithmetic allows at its magnitude (gpu_util.assert_close_o with
+the oracle's attention over |V|).  Large scales make the softmax peaked, so O approaches
+single V rows, with |O| above 2.  There one bf16 step (2^-6) alone exceeds the 1.5e-2
+bound, and P rounded to bf16 before P V adds up to 2^-8 of sum_j P_ij |V_jd|."""
 import math
 
 import numpy as np
@@ -54,7 +60,7 @@ def sync():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(128))
 def test_random_forward(i):
     rng = np.random.default_rng(7000 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -68,11 +74,12 @@ def test_random_forward(i):
     sync()
     qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
     Or, Lr = oracle.attention(qf, kf, vf, scale, causal, left, right)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "O")
+    Oa, _ = oracle.attention(qf, kf, np.abs(vf), scale, causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "LSE")
 
 
-@pytest.mark.parametrize("i", range(32))
+@pytest.mark.parametrize("i", range(64))
 def test_random_backward(i):
     rng = np.random.default_rng(7200 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -92,7 +99,7 @@ def test_random_backward(i):
     assert_close_grads(("dQ", "dK", "dV"), [to_f64(t, dtype) for t in (dq, dk, dv)], refs, dtype)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_varlen(i):
     rng = np.random.default_rng(7500 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -114,11 +121,13 @@ def test_random_varlen(i):
     qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
     Or, Lr = oracle.attention_varlen(qf, kf, vf, x.cu_seqlens_q, x.cu_seqlens_k, scale, causal,
                                      left, right)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "varlen O")
+    Oa, _ = oracle.attention_varlen(qf, kf, np.abs(vf), x.cu_seqlens_q, x.cu_seqlens_k, scale, causal,
+                                    left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "varlen O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "varlen LSE")
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_paged_prefill(i):
     rng = np.random.default_rng(7700 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -139,11 +148,13 @@ def test_random_paged_prefill(i):
     qf, kf, vf = (oracle.widen(t, dtype) for t in (p.q, p.k_pages, p.v_pages))
     Or, Lr = oracle.attention_varlen_paged(qf, kf, vf, p.block_table, p.seq_lens_k, p.cu_seqlens_q,
                                            scale, p.page_size, causal, left, right)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "paged prefill O")
+    Oa, _ = oracle.attention_varlen_paged(qf, kf, np.abs(vf), p.block_table, p.seq_lens_k,
+                                          p.cu_seqlens_q, scale, p.page_size, causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "paged prefill O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "paged prefill LSE")
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_decode(i):
     rng = np.random.default_rng(7900 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -159,14 +170,14 @@ def test_random_decode(i):
                                dev_i32(p.block_table), dev_i32(p.seq_lens), scale=scale,
                                num_splits=splits)
     sync()
-    Or, Lr = oracle.decode_paged(oracle.widen(p.q, dtype), oracle.widen(p.k_pages, dtype),
-                                 oracle.widen(p.v_pages, dtype), p.block_table, p.seq_lens, scale,
-                                 p.page_size)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "decode O")
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (p.q, p.k_pages, p.v_pages))
+    Or, Lr = oracle.decode_paged(qf, kf, vf, p.block_table, p.seq_lens, scale, p.page_size)
+    Oa, _ = oracle.decode_paged(qf, kf, np.abs(vf), p.block_table, p.seq_lens, scale, p.page_size)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "decode O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "decode LSE")
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_multi_decode(i):
     rng = np.random.default_rng(8100 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -182,14 +193,14 @@ def test_random_multi_decode(i):
                                      to_dev(p.v_pages, dtype), dev_i32(p.block_table),
                                      dev_i32(p.seq_lens), scale=scale, num_splits=splits)
     sync()
-    Or, Lr = oracle.decode_paged_multi(oracle.widen(p.q, dtype), oracle.widen(p.k_pages, dtype),
-                                       oracle.widen(p.v_pages, dtype), p.block_table, p.seq_lens,
-                                       scale, p.page_size)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "multi decode O")
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (p.q, p.k_pages, p.v_pages))
+    Or, Lr = oracle.decode_paged_multi(qf, kf, vf, p.block_table, p.seq_lens, scale, p.page_size)
+    Oa, _ = oracle.decode_paged_multi(qf, kf, np.abs(vf), p.block_table, p.seq_lens, scale, p.page_size)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "multi decode O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "multi decode LSE")
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_ext(i):
     rng = np.random.default_rng(8300 + i)
     D, dtype, Hq, Hkv = draw_common(rng)
@@ -223,8 +234,9 @@ def test_random_ext(i):
     qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
     bias_full = None if bias is None else np.broadcast_to(bias, (B, Hq, Nk))
     bm_full = None if bm is None else np.broadcast_to(bm, (B, Hq) + bm.shape[-2:])
-    Or, Lr = oracle.attention_ext(qf, kf, vf, scale, causal, left, right, softcap=softcap,
-                                  alibi_slopes=slopes, bias=bias_full, block_mask=bm_full,
-                                  block_q=bq, block_k=bk)
-    assert_close_o(to_f64(O, dtype), Or, dtype, "ext O")
+    kw = dict(softcap=softcap, alibi_slopes=slopes, bias=bias_full, block_mask=bm_full, block_q=bq,
+              block_k=bk)
+    Or, Lr = oracle.attention_ext(qf, kf, vf, scale, causal, left, right, **kw)
+    Oa, _ = oracle.attention_ext(qf, kf, np.abs(vf), scale, causal, left, right, **kw)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "ext O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "ext LSE")

@@ -99,3 +99,17 @@ def test_grad_inputs_and_backward_workload():
     assert g0.shape == (1, 2, 64, 128) and g0.dtype == np.uint16 and np.array_equal(g0, g1)
     x = (g0.astype(np.uint32) << np.uint32(16)).view(np.float32)
     assert abs(x.mean()) < 0.05 and 0.95 < x.std() < 1.05
+
+
+def test_output_step_is_one_ulp():
+    # one step of the output type at |x|: bf16 keeps 8 significant bits, f16 11
+    from gpu_util import output_step
+    xs = np.array([1.0, 1.5, 2.0, 3.99, 4.0, -2.5, 0.25])
+    assert np.array_equal(output_step("bf16", xs), [2 ** -7, 2 ** -7, 2 ** -6, 2 ** -6, 2 ** -5, 2 ** -6, 2 ** -9])
+    assert np.array_equal(output_step("f16", xs), [2 ** -10, 2 ** -10, 2 ** -9, 2 ** -9, 2 ** -8, 2 ** -9, 2 ** -12])
+    # the next representable value above x is x + step (checked through the generators' rounding)
+    for x in (1.0, 2.0, 3.0, 6.0):
+        up = A.round_f32_to_bits(np.float32([x + output_step("bf16", np.array([x]))[0]]), "bf16")
+        same = A.round_f32_to_bits(np.float32([x + 0.49 * output_step("bf16", np.array([x]))[0]]), "bf16")
+        assert up[0] != A.round_f32_to_bits(np.float32([x]), "bf16")[0]
+        assert same[0] == A.round_f32_to_bits(np.float32([x]), "bf16")[0]
