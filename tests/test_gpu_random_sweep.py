@@ -240,3 +240,31 @@ def test_random_ext(i):
     Oa, _ = oracle.attention_ext(qf, kf, np.abs(vf), scale, causal, left, right, **kw)
     assert_close_o(to_f64(O, dtype), Or, dtype, "ext O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy(), Lr, "ext LSE")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_forward_many_heads(i):
+    # grids of more than two query tiles per CU take the one-group layout (two 4-wave
+    # workgroups per CU); sampled rows against the oracle
+    rng = np.random.default_rng(8500 + i)
+    D, dtype, _, _ = draw_common(rng)
+    Hkv = int(rng.choice([32, 64]))
+    Hq = Hkv * int(rng.choice([2, 4]))
+    B, Nq = 1, int(rng.integers(1100, 1600))      # >= 9 query tiles x >= 64 heads > 2 x 256
+    Nk = Nq if rng.random() < 0.6 else int(rng.integers(300, 2000))
+    causal, left, right, scale = draw_mask(rng, D)
+    print(f"mfa_fwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} D={D} {dtype} causal={causal} "
+          f"win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.dense_inputs(B, Hq, Hkv, Nq, Nk, D, dtype, 8600 + i)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right)
+    sync()
+    assert "groups=1" in ea.mfa_last_dispatch()["kernel"]
+    rows = sorted({(0, int(h), int(r)) for h, r in zip(rng.integers(0, Hq, 200), rng.integers(0, Nq, 200))}
+                  | {(0, 0, 0), (0, Hq - 1, Nq - 1)})
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention(qf, kf, vf, scale, causal, left, right, rows=rows)
+    Oa, _ = oracle.attention(qf, kf, np.abs(vf), scale, causal, left, right, rows=rows)
+    idx = tuple(np.array(rows).T)
+    assert_close_o(to_f64(O, dtype)[idx], Or, dtype, "O", ref_pabs=Oa)
+    assert_close_lse(L.cpu().numpy()[idx], Lr, "LSE")
