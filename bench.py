@@ -14,7 +14,7 @@ of 512..2048 tokens after 1024..16384 cached ones), and the 4-token verification
 (``mfa_decode_paged_multi`` over the decode workload's cache shape, HBM GB/s), and the
 block-sparse causal prefill (``mfa_fwd_ext`` with a 25%-dense 128 x 128 block mask,
 TFLOP/s over the computed visible pairs), and the backward over the dense causal prefill
-shape in bf16 (``mfa_bwd``: prep, dK/dV and dQ launches; TFLOP/s at 10*D FLOP per visible
+shape in bf16 (``mfa_bwd``: dQ and dK/dV launches; TFLOP/s at 10*D FLOP per visible
 pair).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
@@ -426,7 +426,7 @@ def bench_backward(step, steps):
     tf = flop / (ms * 1e-3) / 1e12
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['Nq']} D={c['D']} "
-                    f"{c['dtype']} causal=1 (prep + dK/dV + dQ launches)",
+                    f"{c['dtype']} causal=1 (dQ + dK/dV launches)",
         "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": tf / PEAK_MFMA_F16,

@@ -1,11 +1,12 @@
 // Backward pass of exact attention for gfx950: dQ, dK, dV from Q, K, V, the forward's
-// output O, its row log-sum-exp and the upstream gradient dO, in the three passes of the
-// FlashAttention-2 backward of the mlx-bun flash-attention.ts page:
-//   prep:  D_i = sum_d dO_id O_id per query row, and the LSE in the log2 domain;
-//   dK/dV: per key tile, over the query tiles (and the g query heads of a KV head):
-//          P = exp(scale S - LSE), dP = dO V^T, dS = P (dP - D),
-//          dV += P^T dO, dK += scale dS^T Q;
-//   dQ:    per query tile, over the key tiles: the same P and dS, dQ += scale dS K.
+// output O, its row log-sum-exp and the upstream gradient dO, in the passes of the
+// FlashAttention-2 backward of the mlx-bun flash-attention.ts page (its D-vector pass is
+// folded into the dQ pass, which reads each query row once anyway):
+//   dQ:    per query tile: D_i = sum_d dO_id O_id and the LSE in the log2 domain for its
+//          rows (also written out), then over the key tiles: P = exp(scale S - LSE),
+//          dP = dO V^T, dS = P (dP - D), dQ += scale dS K;
+//   dK/dV: per key tile, over the query tiles (and the g query heads of a KV head), after
+//          the dQ pass: the same P and dS, dV += P^T dO, dK += scale dS^T Q.
 // The probabilities are recomputed from the saved LSE (no running maximum is needed: P <= 1),
 // dQ is accumulated by its own pass rather than with atomics, so every result is
 // deterministic, and every product runs on the 32x32x16 MFMA:
@@ -30,7 +31,6 @@
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves (prep)
 constexpr int kThreads8 = 512;  // 8 waves (dK/dV and dQ)
 
 // The Q / dO (dK/dV pass) and K / V (dQ pass) tiles are read as row operands and
@@ -67,40 +67,6 @@ struct BwdArgs {
     MfaMask mask;
     int chain_q;       // 1: a dQ workgroup runs query tile qt, then nqt - 1 - qt
 };
-
-// ---- prep: D_i and LSE in the log2 domain --------------------------------------------
-// 16 lanes per query row (D / 16 elements each, one 8- or 16-byte load of O and of dO),
-// reduced within the 16-lane DPP row.
-template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void mfa_bwd_prep_kernel(BwdArgs a) {
-    constexpr int PER = D / 16;
-    const long long rows = (long long)a.B * a.Hq * a.Nq;
-    const long long row = (long long)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
-    const int c = threadIdx.x & 15;
-    float acc = 0.f;
-    if (row < rows) {
-        const size_t base = (size_t)row * D + c * PER;
-        if constexpr (PER == 8) {
-            const mfa_u32x4 o4 = *(const mfa_u32x4*)(a.o + base);
-            const mfa_u32x4 d4 = *(const mfa_u32x4*)(a.dout + base);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc += mfa_lo<DT>(o4[e]) * mfa_lo<DT>(d4[e]) + mfa_hi<DT>(o4[e]) * mfa_hi<DT>(d4[e]);
-        } else {
-            const mfa_u32x2 o2 = *(const mfa_u32x2*)(a.o + base);
-            const mfa_u32x2 d2 = *(const mfa_u32x2*)(a.dout + base);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                acc += mfa_lo<DT>(o2[e]) * mfa_lo<DT>(d2[e]) + mfa_hi<DT>(o2[e]) * mfa_hi<DT>(d2[e]);
-        }
-    }
-    acc = mfa_row16_sum(acc);
-    if (row < rows && c == 0) {
-        a.dvec[row] = acc;
-        const float l = a.lse[row];
-        a.lse2[row] = l == -MFA_INF ? MFA_INF : l * 1.4426950408889634f;
-    }
-}
 
 // Visibility of a 32 x 32 block (rows r0 .. r0 + 31 < Nq at least partly, keys
 // c0 .. c0 + 31): any visible pair, and every pair visible.  The row bounds of the mask
@@ -468,21 +434,38 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     const size_t kv_base = (size_t)(b * a.Hkv + kvh) * a.Nk * D;
 
     // Q^T and dO^T operands: lane (query l32, k-group g32) holds row[16 kb + 8 g32 .. +7]
+    // and this row's D_i = sum_d dO_id O_id from the same chunks of O (the other half of
+    // the row is in lane ^ 32); D_i and the LSE in the log2 domain are also written out for
+    // the dK/dV pass, which runs after this one
     mfa_u32x4 qb[NKB], db_op[NKB];
+    float dpart = 0.f;
     {
         const auto rq = mfa_rsrc(a.q + q_base, (uint32_t)a.Nq * D * 2);
         const auto rd = mfa_rsrc(a.dout + q_base, (uint32_t)a.Nq * D * 2);
+        const auto ro = mfa_rsrc(a.o + q_base, (uint32_t)a.Nq * D * 2);
         const uint32_t off = ((uint32_t)qrow * D + g32 * 8) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             qb[kb] = mfa_load16(rq, off + kb * 32);
             db_op[kb] = mfa_load16(rd, off + kb * 32);
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const mfa_u32x4 o4 = mfa_load16(ro, off + kb * 32);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dpart += mfa_lo<DT>(o4[e]) * mfa_lo<DT>(db_op[kb][e]) + mfa_hi<DT>(o4[e]) * mfa_hi<DT>(db_op[kb][e]);
+        }
     }
     const bool qvalid = qrow < a.Nq;
-    const float lse2 = qvalid ? a.lse2[(size_t)bh * a.Nq + qrow] : MFA_INF;
-    const float dvv = qvalid ? a.dvec[(size_t)bh * a.Nq + qrow] : 0.f;
+    const float lraw = qvalid ? a.lse[(size_t)bh * a.Nq + qrow] : -MFA_INF;
     __builtin_amdgcn_s_waitcnt(0x0f70);
+    const float dvv = dpart + mfa_swap_halves(dpart);
+    const float lse2 = lraw == -MFA_INF ? MFA_INF : lraw * 1.4426950408889634f;
+    if (qvalid && kh == 0 && g32 == 0) {
+        a.dvec[(size_t)bh * a.Nq + qrow] = dvv;
+        a.lse2[(size_t)bh * a.Nq + qrow] = lse2;
+    }
     const int64_t rlo64 = mfa_row_lo(m, qrow), rhi64 = mfa_row_hi(m, qrow);
     const int row_lo = rlo64 > a.Nk ? a.Nk : (int)rlo64;
     const int row_hi = rhi64 < -1 ? -1 : (int)rhi64;
@@ -646,15 +629,12 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
 
 template <int D, int DT>
 int launch(const BwdArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
-    const long long rows = (long long)a.B * a.Hq * a.Nq;
-    const dim3 g0((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)));
-    hipLaunchKernelGGL((mfa_bwd_prep_kernel<D, DT>), g0, dim3(kThreads), 0, stream, a);
+    // dQ first: it also writes D_i and the log2-domain LSE that the dK/dV pass reads
+    const dim3 g2((unsigned)((a.Nq + 127) / 128 / (a.chain_q ? 2 : 1)), (unsigned)(a.B * a.Hq));
+    hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     const dim3 g1((unsigned)((a.Nk + 127) / 128), (unsigned)(a.B * a.Hkv));
     hipLaunchKernelGGL((mfa_bwd_dkv_kernel<D, DT>), g1, dim3(kThreads8), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
-    const dim3 g2((unsigned)((a.Nq + 127) / 128 / (a.chain_q ? 2 : 1)), (unsigned)(a.B * a.Hq));
-    hipLaunchKernelGGL((mfa_bwd_dq_kernel<D, DT>), g2, dim3(kThreads8), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MFA_ERR_HIP;
     snprintf(info->kernel, sizeof(info->kernel), "mfa_bwd_dkv_kernel+mfa_bwd_dq_kernel<D=%d,%s%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", a.chain_q ? ",dq chained" : "");
@@ -665,7 +645,7 @@ int launch(const BwdArgs& a, hipStream_t stream, mfa_dispatch_info* info) {
     info->waves = 8;
     info->BM = 32;
     info->BN = 128;
-    info->n_launches = 3;
+    info->n_launches = 2;
     return MFA_OK;
 }
 

@@ -244,7 +244,8 @@ size_t mfa_bwd_workspace_bytes(int B, int Hq, int Nq);
 
 /* Backward pass of mfa_fwd: the gradients of O with respect to Q, K and V for an
  * upstream gradient dO (the FlashAttention-2 backward of the mlx-bun flash-attention.ts
- * page: D-vector, dK/dV and dQ passes recomputing P from the saved LSE).  With P the
+ * page: D-vector, dK/dV and dQ passes recomputing P from the saved LSE; here the D-vector
+ * is formed inside the dQ pass, which runs first).  With P the
  * forward's probabilities (masked keys have P = 0):
  *   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P * (dP - D),
  *   dQ = scale dS K,  dK = scale dS^T Q,
