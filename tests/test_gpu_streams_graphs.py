@@ -116,3 +116,22 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for key, t in got.items():
             assert same(t, ref[key]), (r, key)
+
+
+def test_repeated_calls_bitwise():
+    # 30 back-to-back calls of the chained forward (an even number of query tiles on a
+    # small grid) and of the backward give the first call's result bit for bit
+    import torch
+    x = A.dense_inputs(2, 4, 2, 512, 512, 128, "bf16", 61)
+    q, k, v = (to_dev(t, "bf16") for t in (x.q, x.k, x.v))
+    do = to_dev(A.grad_inputs(2, 4, 512, 128, "bf16", 62), "bf16")
+    scale = 1 / math.sqrt(128)
+    O0, L0 = ea.mfa_fwd(q, k, v, scale=scale, causal=True)
+    assert ",chained" in ea.mfa_last_dispatch()["kernel"]
+    g0 = ea.mfa_bwd(q, k, v, O0, do, L0, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for _ in range(30):
+        O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=True)
+        g = ea.mfa_bwd(q, k, v, O, do, L, scale=scale, causal=True)
+        assert same(O, O0) and same(L, L0)
+        assert all(same(a, b) for a, b in zip(g, g0))
