@@ -376,33 +376,55 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArg
 
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
     const size_t page_elems = (size_t)kPage * a.Hkv * D;
-    int pid_next[kPG];
-#pragma unroll
-    for (int j = 0; j < kPG; ++j) pid_next[j] = w_begin + j < w_end ? mfa_uniform_load(bt + w_begin + j) : -1;
-
-    for (int pg = w_begin; pg < w_end; pg += kPG) {
-        mfa_u32x4 kr[kPG][NKB];
-        int nv[kPG];
+    // page j of the step at page pg: its offset in the pools, and its valid tokens
+    auto page_at = [&](int pg, int j, int pid, int& nvj) {
+        const bool pvalid = pid >= 0 && pid < a.num_pages && pg + j < w_end;
+        nvj = pvalid ? min(kPage, L - (pg + j) * kPage) : 0;
+        return (size_t)(pvalid ? pid : 0) * page_elems + (size_t)kvh * D;
+    };
+    auto issue_k = [&](int pg, const int (&pid)[kPG], mfa_u32x4 (&kr)[kPG][NKB], int (&nv)[kPG]) {
 #pragma unroll
         for (int j = 0; j < kPG; ++j) {
-            const int pid = pid_next[j];
-            const bool pvalid = pid >= 0 && pid < a.num_pages && pg + j < w_end;
-            nv[j] = pvalid ? min(kPage, L - (pg + j) * kPage) : 0;
-            const size_t pbase = (size_t)(pvalid ? pid : 0) * page_elems + (size_t)kvh * D;
-            const uint32_t bytes = (uint32_t)nv[j] * tok_bytes;
-            const auto rk = mfa_rsrc(a.kp + pbase, bytes);
-            const auto rv = mfa_rsrc(a.vp + pbase, bytes);
+            const size_t pbase = page_at(pg, j, pid[j], nv[j]);
+            const auto rk = mfa_rsrc(a.kp + pbase, (uint32_t)nv[j] * tok_bytes);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) kr[j][kb] = mfa_load16(rk, k_off + (4 * kb + G) * 16);
+        }
+    };
+    auto issue_v = [&](int pg, const int (&pid)[kPG]) {
+#pragma unroll
+        for (int j = 0; j < kPG; ++j) {
+            int nvj;
+            const size_t pbase = page_at(pg, j, pid[j], nvj);
+            const auto rv = mfa_rsrc(a.vp + pbase, (uint32_t)nvj * tok_bytes);
 #pragma unroll
             for (int i = 0; i < VLOADS; ++i)
                 mfa_load16_lds(rv, sv + (j * VLOADS + i) * 512, v_off + (uint32_t)(i * TOK_PER_LOAD) * tok_bytes);
         }
+    };
+    auto load_pids = [&](int pg, int (&pid)[kPG]) {
 #pragma unroll
-        for (int j = 0; j < kPG; ++j)
-            pid_next[j] = pg + kPG + j < w_end ? mfa_uniform_load(bt + pg + kPG + j) : -1;
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < kPG; ++j) pid[j] = pg + j < w_end ? mfa_uniform_load(bt + pg + j) : -1;
+    };
 
+    // Pipelined: the next step's K loads are issued once this step's score products have
+    // read the K registers, and its V copies once this step's P V reads have returned, so
+    // both are in flight during this step's softmax and products.  Page ids are read two
+    // steps ahead.
+    int pid_nx[kPG];
+    mfa_u32x4 kr[kPG][NKB];
+    int nv[kPG];
+    {
+        int pid0[kPG];
+        load_pids(w_begin, pid0);
+        load_pids(w_begin + kPG, pid_nx);
+        if (w_begin < w_end) {
+            issue_k(w_begin, pid0, kr, nv);
+            issue_v(w_begin, pid0);
+        }
+    }
+    for (int pg = w_begin; pg < w_end; pg += kPG) {
+        const bool more = pg + kPG < w_end;   // uniform
         // scores (log2 domain), masked: position p visible iff p < L and p <= lim
         float x[kPG][4];
 #pragma unroll
@@ -417,6 +439,8 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArg
                 x[j][i] = vis ? acc[i] * a.scale_log2 : -MFA_INF;
             }
         }
+        int nv_n[kPG];
+        if (more) issue_k(pg + kPG, pid_nx, kr, nv_n);
         float tmax = -MFA_INF;
 #pragma unroll
         for (int j = 0; j < kPG; ++j)
@@ -449,8 +473,17 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArg
                     l_run += p0 + p1;
             }
 
-        // O^T += V^T P^T from the wave's LDS copy of the two pages
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the direct loads have landed
+        // O^T += V^T P^T from the wave's LDS copy of the two pages: this step's V copies
+        // have landed once at most the next step's kPG * NKB K loads are outstanding
+        static_assert(kPG * NKB == 8 || kPG * NKB == 4, "vmcnt immediate");
+        if (more) {
+            if constexpr (kPG * NKB == 8)
+                __builtin_amdgcn_s_waitcnt(0x0f78);   // vmcnt(8)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const mfa_u32x2 lo = mfa_lds_read_tr16(sv + v_rd[db]);
@@ -459,6 +492,12 @@ __global__ __launch_bounds__(kThreads, 2) void mfa_decode_mq_split_kernel(DecArg
         }
         // the next step's copies overwrite the buffer: its reads must have returned
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        if (more) {
+            issue_v(pg + kPG, pid_nx);
+#pragma unroll
+            for (int j = 0; j < kPG; ++j) nv[j] = nv_n[j];
+            load_pids(pg + 2 * kPG, pid_nx);
+        }
     }
 
     // merge the four waves' partial states of each row in LDS (reusing the V buffers)
