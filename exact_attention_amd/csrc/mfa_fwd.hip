@@ -9,15 +9,17 @@
 // contractions run on the CDNA4 matrix cores and the loop is software-pipelined.
 //
 // Work decomposition
-//   One workgroup = 8 waves = one query tile of BM = 128 rows of one (batch, head).
-//   The waves form two groups of 4; in each group a wave owns 32 query rows, and the
-//   two groups split the tile's visited key range in halves, run concurrently (two
-//   waves per SIMD) and merge their (O, m, l) through LDS at the end.  Every
-//   workgroup thus finishes its query tile in about half the serial time, and with
-//   one workgroup per CU and longest tiles dispatched first, short causal tiles fill
-//   the CUs that free up early.  Key tiles of BN = 64 keys stream through LDS: K and
-//   V tiles are copied global -> LDS directly (buffer loads with the LDS bit; the
-//   range check returns zeros past the last key row), double-buffered per group.
+//   A query tile is BM = 128 rows of one (batch, head); a group of 4 waves covers it,
+//   each wave owning 32 rows.  Large grids use one group per workgroup, two workgroups
+//   per CU, which overlap each other's prologue and epilogue; longest tiles go first.
+//   Small grids (at most two tiles per CU) use 8-wave workgroups whose two groups split
+//   the tile's visited key range in halves, run concurrently (two waves per SIMD) and
+//   merge their (O, m, l) through LDS at the end; for dense inputs with an even number
+//   of query tiles such a workgroup then runs a second, complementary tile (T - 1 - r
+//   after r), so every workgroup has the same causal work.  Key tiles of BN = 64 keys
+//   stream through LDS: K and V tiles are copied global -> LDS directly (buffer loads
+//   with the LDS bit; the range check returns zeros past the last key row),
+//   double-buffered per group.
 //
 // Per wave and key tile (32x32x16 MFMA, fp32 accumulate):
 //   S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T held in registers for the whole
