@@ -561,6 +561,76 @@ def pin_backward_masked_keys_and_rows():
     assert np.all(dk[0, 0, 0] == 0) and np.all(dv[0, 0, 0] == 0)
 
 
+def _widen_by_fields(bits, dtype):
+    """Value of 16-bit patterns from the IEEE binary16 / bfloat16 field definitions: sign,
+    exponent (5 bits, bias 15 / 8 bits, bias 127), fraction (10 / 7 bits) with an implicit
+    leading 1 for normal numbers; exponent 0 = subnormal, all ones = inf (fraction 0) or NaN.
+    Integer fields and exact ldexp only."""
+    b = np.asarray(bits, dtype=np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    ebits, fbits, bias = (5, 10, 15) if dtype == "f16" else (8, 7, 127)
+    e = (b >> fbits) & ((1 << ebits) - 1)
+    f = b & ((1 << fbits) - 1)
+    emax = (1 << ebits) - 1
+    normal = sign * np.ldexp((f + (1 << fbits)).astype(np.float64), e - bias - fbits)
+    sub = sign * np.ldexp(f.astype(np.float64), 1 - bias - fbits)
+    val = np.where(e == 0, sub, normal)
+    special = np.where(f == 0, sign * np.inf, np.nan)
+    return np.where(e == emax, special, val)
+
+
+def pin_widen_every_bit_pattern():
+    # widen turns the stored 16-bit patterns into float64 on both sides of every parity
+    # check: all 65,536 patterns of each type against the field definitions and against
+    # torch's own float16 / bfloat16 -> float64 conversions (NaNs compared as NaNs,
+    # zeros by sign), plus fixed values that tell the two types apart
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        got = oracle.widen(bits, dt)
+        ref = _widen_by_fields(bits, dt)
+        ref_t = torch.from_numpy(bits.view(np.int16)).view(tdt).to(torch.float64).numpy()
+        for r in (ref, ref_t):
+            assert np.array_equal(np.isnan(got), np.isnan(r)), dt
+            ok = ~np.isnan(r)
+            assert np.array_equal(got[ok], r[ok]), dt
+            assert np.array_equal(np.signbit(got[ok]), np.signbit(r[ok])), dt
+    fixed = {
+        "f16": {0x3C00: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -24, 0x7BFF: 65504.0, 0x7C00: np.inf,
+                0xFC00: -np.inf, 0x3F80: 1.875, 0x0400: 2.0 ** -14, 0x3555: (1 + 0x155 / 1024) * 2.0 ** -2},
+        "bf16": {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+                 0x7F80: np.inf, 0xFF80: -np.inf, 0x3C00: 2.0 ** -7, 0x0080: 2.0 ** -126},
+    }
+    for dt, table in fixed.items():
+        pats = np.array(list(table), dtype=np.uint16)
+        assert np.array_equal(oracle.widen(pats, dt), np.array(list(table.values()))), dt
+    assert np.signbit(oracle.widen(np.array([0x8000], np.uint16), "f16")[0])
+    assert np.isnan(oracle.widen(np.array([0x7E00], np.uint16), "f16")[0])
+    assert np.isnan(oracle.widen(np.array([0x7FC0], np.uint16), "bf16")[0])
+
+
+def pin_probs_gqa():
+    # attention_probs with grouped query heads (g = 2, two distinct KV heads, Nq != Nk):
+    # equal to the same call on explicitly repeated K heads (consecutive grouping), and
+    # P V equal to the scalar path's output; one row against a brute-force softmax
+    q, k, v = _rand((2, 4, 5, 3), 70), _rand((2, 2, 6, 3), 71), _rand((2, 2, 6, 3), 72)
+    k_rep = np.repeat(k, 2, axis=1)
+    for causal, left, right in [(False, -1, -1), (True, -1, -1), (True, 1, 0), (False, 0, 2)]:
+        P = oracle.attention_probs(q, k, 0.8, causal, left, right)
+        P_rep = oracle.attention_probs(q, k_rep, 0.8, causal, left, right)
+        np.testing.assert_allclose(P, P_rep, atol=1e-15, rtol=0)
+        Os, _ = attention_scalar(q.tolist(), k.tolist(), v.tolist(), 0.8, causal, left, right)
+        for b in range(2):
+            for h in range(4):
+                np.testing.assert_allclose(P[b, h] @ v[b, h // 2], np.array(Os[b][h]), atol=1e-13,
+                                           rtol=0)
+    # row i = 4 of head 3 (KV head 1), non-causal: softmax of all 6 scaled scores
+    P = oracle.attention_probs(q, k, 0.8)
+    sc = [0.8 * _fsum_dot(q[1, 3, 4], k[1, 1, j]) for j in range(6)]
+    z = math.fsum(math.exp(x) for x in sc)
+    np.testing.assert_allclose(P[1, 3, 4], [math.exp(x) / z for x in sc], atol=1e-15, rtol=0)
+
+
 PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_probs_sum_to_one,
         pin_lse_bruteforce, pin_scalar_oracle, pin_wide_window_is_full,
         pin_zero_window_is_identity, pin_gqa_is_repeated_mha, pin_affine_v, pin_torch_sdpa,
@@ -569,7 +639,7 @@ PINS = [pin_golden, pin_single_key, pin_identical_keys, pin_causal_row0, pin_pro
         pin_varlen_window_scalar, pin_varlen_empty_and_isolated, pin_varlen_paged,
         pin_decode_multi, pin_ext_scalar, pin_ext_bias_torch, pin_ext_limits_and_blocks,
         pin_backward_torch_autograd, pin_backward_finite_differences,
-        pin_backward_masked_keys_and_rows]
+        pin_backward_masked_keys_and_rows, pin_widen_every_bit_pattern, pin_probs_gqa]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -754,6 +824,30 @@ def _mut_decode_multi_top_left(q, k_pages, v_pages, block_table, seq_lens, scale
         L[b] = lse[0].T
     return O, L
 
+
+_ORIG_WIDEN = OA.widen
+_ORIG_PROBS = OA.attention_probs
+
+
+def _mut_widen_bf16_shift(bits, dtype):
+    # plausible mistake: the bf16 pattern shifted into the float32 word by the wrong amount
+    if dtype == "bf16":
+        return (np.asarray(bits).astype(np.uint32) << np.uint32(8)).view(np.float32).astype(np.float64)
+    return _ORIG_WIDEN(bits, dtype)
+
+
+def _mut_widen_swapped(bits, dtype):
+    # plausible mistake: the two 16-bit types decoded with each other's layout
+    return _ORIG_WIDEN(bits, "bf16" if dtype == "f16" else "f16")
+
+
+def _mut_probs_gqa_modulo(q, k, scale, causal=False, left=-1, right=-1):
+    # plausible mistake: query head h reads KV head h % Hkv
+    q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    return np.concatenate([_ORIG_PROBS(q[:, h:h + 1], k[:, h % Hkv:h % Hkv + 1], scale, causal,
+                                       left, right) for h in range(Hq)], axis=1)
+
 MUTATIONS = {
     "exclusive_window": ("visible", _mut_exclusive_window),
     "top_left_causal": ("visible", _mut_top_left_causal),
@@ -772,6 +866,9 @@ MUTATIONS = {
     "ext_block_transposed": ("attention_ext", _mut_ext_block_transposed),
     "bwd_no_dvec": ("attention_backward", _mut_bwd_no_dvec),
     "bwd_unscaled_dk": ("attention_backward", _mut_bwd_no_scale_dk),
+    "widen_bf16_wrong_shift": ("widen", _mut_widen_bf16_shift),
+    "widen_types_swapped": ("widen", _mut_widen_swapped),
+    "probs_gqa_modulo": ("attention_probs", _mut_probs_gqa_modulo),
 }
 
 
