@@ -306,7 +306,7 @@ WORKLOADS = {
     # serving-style mix of prompt lengths, GQA heads of the long-context workload
     "packed_varlen_causal_prefill": dict(B=16, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True, left=-1,
                                          right=-1, len_lo=256, len_hi=4096, seed=106),
-    # chunked prefill over the paged cache (mlx-mfa "Paged + packed varlen queries"):
+    # chunked prefill over the paged cache (the mlx-mfa 2.5.2 capability table: packed queries over paged keys):
     # new chunks of 512..2048 tokens after 1024..16384 cached ones, pages of 16
     "paged_chunked_prefill": dict(B=8, Hq=32, Hkv=8, D=128, dtype=BF16, causal=True, left=-1,
                                   right=-1, page_size=16, new_lo=512, new_hi=2048, ctx_lo=1024,

@@ -5,7 +5,8 @@
 // window_size=(left, right) convention of the mlx-mfa 2.5.2 "Sliding window" feature
 // (-1 = unbounded), with both window ends inclusive and bottom-right alignment
 // off = Nk - Nq.  A key tile is visited iff it holds at least one visible pair
-// ("Causal tile-skip: skips upper-triangular K-tiles entirely").  The skip decision is
+// (the "Causal tile-skip" feature: key tiles wholly above the diagonal are never
+// visited).  The skip decision is
 // uniform over the workgroup (a per-lane skip around a barrier is undefined).
 #pragma once
 #include <stdint.h>

@@ -18,14 +18,15 @@
  *                     delimited by cu_seqlens (mlx-mfa "Variable-length"), each
  *                     sequence masked on its own lengths.
  *   mfa_fwd_varlen_paged  packed queries whose keys sit in a paged KV cache (chunked
- *                     prefill; mlx-mfa "Paged + packed varlen queries").
+ *                     prefill; mlx-mfa 2.5.2 capability table, packed queries over paged keys).
  *   mfa_decode_paged_multi  the same for Nq <= 4 new tokens per sequence (speculative
  *                     verification), with the query rows of a KV head packed together.
  *   mfa_decode_paged  single-query decode over a paged KV cache, split across
  *                     workgroups along the keys, with partial (O, LSE) pairs merged in
- *                     a second pass.  Defined by the mlx-mfa 2.5.2 page ("Flash Decode
- *                     — two-phase split-KV", "Paged KV — page-pool KV cache with
- *                     block_table") and the MXFlashAttn 1.5.0 page (M1 paged Split-KV
+ *                     a second pass.  Defined by the mlx-mfa 2.5.2 page (the "Flash Decode"
+ *                     feature, a split-KV decode in two phases, and the "Paged KV"
+ *                     feature, a pool of pages addressed through a block table) and
+ *                     the MXFlashAttn 1.5.0 page (M1 paged Split-KV
  *                     decode; the per-split (m, l) slot race section).
  *
  * Conventions shared by every entry point
@@ -88,7 +89,11 @@ typedef enum {
 typedef struct {
     int BM;               /* query rows per workgroup (one query tile) */
     int BN;               /* keys per key tile */
-    int waves;            /* wavefronts (64 lanes) per workgroup */
+    int waves;            /* wavefronts (64 lanes) per wave group: one group covers the
+                             BM query rows of a tile.  mfa_fwd runs one or two groups per
+                             workgroup, chosen at launch from the grid size (with two, the
+                             groups split the tile's key range); mfa_last_dispatch reports
+                             the workgroup actually launched */
     int n_q_tiles;        /* ceil(Nq / BM) */
     int n_k_tiles;        /* ceil(Nk / BN) */
     long long visited;    /* key tiles visited, summed over the query tiles */
@@ -128,9 +133,10 @@ int mfa_fwd_tilelog(const void* q, const void* k, const void* v, void* out, floa
                     int32_t* tile_log);
 
 /* Score modifiers and block-sparse mask for mfa_fwd_ext (mlx-mfa 2.5.2 feature list:
- * "Softcap — tanh softcapping fused in-kernel", "ALiBi — per-head linear position bias",
- * "Block-sparse attention — block_mask tensor skips entire tiles"; mlx-mfa 2.61.0
- * "Native attn_bias" additive bias on the logits, per key and per head per key).  With
+ * the "Softcap", "ALiBi" and "Block-sparse attention" features, i.e. a tanh cap on the
+ * scores inside the kernel, a linear distance penalty per head, and a mask of blocks whose
+ * tiles are skipped; mlx-mfa 2.61.0 "Native attn_bias" feature, an additive bias on the
+ * logits, per key and per head per key).  With
  * off = Nk - Nq the score of query i and key j of head h in batch b is, in this order:
  *   s = scale * q_i . k_j
  *   s = softcap * tanh(s / softcap)                         if softcap > 0
@@ -207,8 +213,8 @@ int mfa_fwd_varlen_tilelog(const void* q, const void* k, const void* v, void* ou
                            int32_t* tile_log);
 
 /* Packed queries over a paged KV cache: chunked prefill and speculative or
- * multi-token verification (mlx-mfa 2.5.2 capability table, "Paged + packed varlen
- * queries"; the paged-cache addressing of mfa_decode_paged).  Sequence b has
+ * multi-token verification (mlx-mfa 2.5.2 capability table, packed variable-length
+ * queries over paged keys; the paged-cache addressing of mfa_decode_paged).  Sequence b has
  * Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] new query tokens and Lk_b = seq_lens_k[b]
  * cached keys, which include the new tokens' own keys (appended before the call); the
  * visibility rule applies with Nq = Lq_b, Nk = Lk_b, off = Lk_b - Lq_b, so the queries
@@ -264,7 +270,15 @@ int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             int causal, int win_left, int win_right, int dtype, void* stream);
 
 /* Bytes of workspace mfa_decode_paged needs for these sizes (num_splits 0 = auto).
- * Returns 0 if the arguments are invalid. */
+ * The workspace holds the per-split partial results of the split-KV decode: one slot per
+ * (sequence, query head, split), each D fp32 partial outputs plus one fp32 log-sum-exp,
+ * i.e. B * Hq * S * (D + 1) * 4 bytes with S = mfa_decode_num_splits(...).  This follows
+ * the MXFlashAttn 1.5.0 page: its split-KV decode keeps one (m, l) slot per split and
+ * merges them in a second pass (section on the non-deterministic out-of-bounds write in
+ * the split-KV scratch slots), and its roadmap names the scratch lifetime under graph
+ * capture as an open problem, which is why the caller owns this memory here.
+ * Returns 0 if the arguments are invalid (B, Hq < 1, D not 64 / 128, page_size != 16,
+ * max_pages_per_seq < 1 or num_splits < 0); never allocates. */
 size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
                                   int num_splits);
 
@@ -306,8 +320,9 @@ size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_s
                                         int max_pages_per_seq, int num_splits);
 
 /* Paged split-KV decode of Nq <= 4 new tokens per sequence, e.g. the verification step of
- * speculative decoding (mlx-mfa 2.5.2 feature list: "Flash Decode — two-phase split-KV for
- * N_q <= 4"; the packed-GQA verify kernel of the MTPLX verify-attention page).  The new
+ * speculative decoding (mlx-mfa 2.5.2 feature list: the "Flash Decode" feature, a split-KV
+ * decode in two phases for up to four query tokens; the packed-GQA verify kernel of the
+ * MTPLX verify-attention page).  The new
  * tokens' keys are already in the cache: they are its last Nq positions, and new token n
  * sees the keys at positions <= seq_lens[b] - Nq + n (the visibility rule above with
  * Nk = seq_lens[b], causal).  The g * Nq query rows of one KV head are computed together.
@@ -346,7 +361,13 @@ typedef struct {
  * MFA_ERR_ARG if this thread has launched nothing yet. */
 int mfa_last_dispatch(mfa_dispatch_info* out);
 
-/* Static description of a status code. */
+/* Static description of a status code ("unknown status" for a value that is not an
+ * mfa_status).  The status codes follow the mlx-mfa 2.61.0 README: the raw native
+ * entries carry the same guards as the Python wrappers (release notes), malformed inputs
+ * are rejected before dispatch rather than returning silent wrong or NaN output
+ * (input-validation contract), and a disabled fast path reports a reason code instead
+ * of falling back silently ("Verify acceleration is active").  The string is static,
+ * owned by the library; it must not be freed. */
 const char* mfa_status_string(int status);
 
 /* Library ABI version (major * 10000 + minor * 100 + patch). */

@@ -21,14 +21,15 @@ tile by tile:
   token axis and delimited by ``cu_seqlens`` (mlx-mfa "Variable-length" feature),
   each sequence on its own with bottom-right alignment.
 * ``attention_varlen_paged``: packed queries whose keys come from a paged KV cache
-  (chunked prefill; mlx-mfa "Paged + packed varlen queries").
+  (chunked prefill; mlx-mfa 2.5.2 capability table, packed queries over paged keys).
 * ``decode_paged``: single-query attention over a paged KV cache, gathered through
   the block table with its own loop (MXFlashAttn paged Split-KV decode; mlx-mfa
   "Paged KV" feature).
 * ``decode_paged_multi``: decode of up to a few new tokens per sequence (speculative
-  verification), causal among the new tokens (mlx-mfa "Flash Decode ... N_q <= 4").
+  verification), causal among the new tokens (mlx-mfa 2.5.2 "Flash Decode" feature, up to four
+  new tokens).
 * ``lse_merge``: the combination of partial (O, LSE) pairs that a split-KV decode's
-  second pass performs (mlx-mfa "Flash Decode — two-phase split-KV").
+  second pass performs (mlx-mfa 2.5.2 "Flash Decode" feature: split-KV in two phases).
 * ``visited_tiles``: the brute-force set of key tiles holding at least one visible
   (query, key) pair for each query tile (mlx-mfa "Causal tile-skip" and "Sliding
   window" features).

@@ -309,8 +309,8 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
 def attention_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
                            scale: float, page_size: int, causal: bool = False, left: int = -1,
                            right: int = -1, rows=None):
-    """Packed queries over a paged KV cache, float64 (mlx-mfa "Paged + packed varlen
-    queries"; MXFlashAttn paged-cache addressing).
+    """Packed queries over a paged KV cache, float64 (mlx-mfa 2.5.2 capability
+    table, packed variable-length queries over paged keys; MXFlashAttn paged-cache addressing).
 
     q ``[total_q, Hq, D]`` with sequence ``b`` owning query tokens ``cu_seqlens_q[b] ..
     cu_seqlens_q[b+1]-1``; its ``Lk_b = seq_lens_k[b]`` keys are gathered from the
@@ -398,7 +398,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float,
 def decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: float,
                        page_size: int):
     """Decode of ``Nq`` new tokens per sequence over a paged KV cache, float64 (mlx-mfa
-    "Flash Decode — two-phase split-KV for N_q <= 4"; MTPLX verify attention).
+    "Flash Decode" feature, which covers up to four new tokens; MTPLX verify attention).
 
     q ``[B, Nq, Hq, D]``; the ``seq_lens[b]`` cached tokens include the new ones, which are
     the last ``Nq`` positions, so new token ``n`` sees the keys at positions
