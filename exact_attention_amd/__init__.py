@@ -10,7 +10,6 @@ code path.  If the library is missing, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +121,14 @@ def _check(st: int, where: str):
         raise MfaError(st, where)
 
 
+def _scale(scale) -> float:
+    """The softmax scale is an explicit argument with no default (the pages give it as the
+    scalar that multiplies Q K^T before masking); the C ABI checks that it is finite."""
+    if scale is None or isinstance(scale, bool):
+        raise ValueError("scale is required (it multiplies Q K^T; no default is applied)")
+    return float(scale)
+
+
 def mfa_plan_fwd(Nq: int, Nk: int, D: int, dtype: int = MFA_F16, causal: bool = False,
                  win_left: int = -1, win_right: int = -1, with_ranges: bool = True):
     """Host-only tile plan.  Returns (plan dict, list of (kt_lo, kt_hi) per query tile)."""
@@ -209,14 +216,15 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left: int = -1,
+def mfa_fwd(q, k, v, scale: float, causal: bool = False, win_left: int = -1,
             win_right: int = -1, out=None, lse=None, return_lse: bool = True, tile_log=None):
     """Forward pass on torch tensors q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] (fp16 or bf16).
 
-    ``scale`` defaults to 1/sqrt(D) here (the C ABI applies no default).  Returns
+    ``scale`` multiplies Q K^T and has no default.  Returns
     ``(out, lse)``; ``lse`` is None when ``return_lse`` is False and none is given.
     ``tile_log`` (int32 device tensor) selects ``mfa_fwd_tilelog``.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, D]")
@@ -227,8 +235,6 @@ def mfa_fwd(q, k, v, scale: float | None = None, causal: bool = False, win_left:
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     dt = _dtype_code(q)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -254,12 +260,13 @@ def mfa_fwd_tilelog(q, k, v, tile_log, **kw):
     return mfa_fwd(q, k, v, tile_log=tile_log, **kw)
 
 
-def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = False,
+def mfa_bwd(q, k, v, out, dout, lse, scale: float, causal: bool = False,
             win_left: int = -1, win_right: int = -1, dq=None, dk=None, dv=None, workspace=None):
     """Backward pass on torch tensors: the gradients (dq, dk, dv) of ``mfa_fwd``'s output
     for upstream gradient ``dout``.  ``out`` and ``lse`` are the forward's results for the
     same q, k, v, scale and mask arguments.  ``workspace`` is allocated here when absent.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q, k, v must be 4-D [B, H, N, D]")
@@ -275,8 +282,6 @@ def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = 
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
         raise ValueError("lse must be float32 [B, Hq, Nq]")
     dt = _dtype_code(q)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     for t, like, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
         if t is not None:
             _need(t, like.shape, like.dtype, n)
@@ -295,7 +300,7 @@ def mfa_bwd(q, k, v, out, dout, lse, scale: float | None = None, causal: bool = 
     return dq, dk, dv
 
 
-def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_left: int = -1,
+def mfa_fwd_ext(q, k, v, scale: float, causal: bool = False, win_left: int = -1,
                 win_right: int = -1, softcap: float = 0.0, alibi_slopes=None, bias=None,
                 block_mask=None, block_q: int = 0, block_k: int = 0, out=None, lse=None,
                 return_lse: bool = True, tile_log=None):
@@ -307,6 +312,7 @@ def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_l
     [B?, H?, nqb, nkb] (leading dims broadcast through strides) with blocks of
     ``block_q`` x ``block_k`` (multiples of 32).  Returns ``(out, lse)``.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q, k, v must be 4-D [B, H, N, D]")
@@ -317,8 +323,6 @@ def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_l
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     dt = _dtype_code(q)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is not None:
         _need(out, q.shape, q.dtype, "out")
     if lse is not None:
@@ -368,7 +372,7 @@ def mfa_fwd_ext(q, k, v, scale: float | None = None, causal: bool = False, win_l
 
 
 def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                   scale: float | None = None, causal: bool = False, win_left: int = -1,
+                   scale: float, causal: bool = False, win_left: int = -1,
                    win_right: int = -1, out=None, lse=None, return_lse: bool = True,
                    tile_log=None):
     """Packed variable-length forward on torch tensors.
@@ -376,8 +380,9 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     q [total_q, Hq, D], k/v [total_k, Hkv, D] (fp16 or bf16, token-major); cu_seqlens_q /
     cu_seqlens_k int32 [B + 1] device tensors; max_seqlen_q / max_seqlen_k host ints
     bounding every sequence's lengths.  Returns ``(out, lse)`` with lse [Hq, total_q].
-    ``scale`` defaults to 1/sqrt(D) here.  ``tile_log`` selects ``mfa_fwd_varlen_tilelog``.
+    ``tile_log`` selects ``mfa_fwd_varlen_tilelog``.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
         raise ValueError("q must be [total_q, Hq, D] and k, v [total_k, Hkv, D]")
@@ -393,8 +398,6 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
     B = cu_seqlens_q.numel() - 1
     dt = _dtype_code(q)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -419,7 +422,7 @@ def mfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
 
 
 def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlens_q,
-                         max_seqlen_q: int, max_seqlen_k: int, scale: float | None = None,
+                         max_seqlen_q: int, max_seqlen_k: int, scale: float,
                          causal: bool = False,
                          win_left: int = -1, win_right: int = -1, out=None, lse=None,
                          return_lse: bool = True):
@@ -430,6 +433,7 @@ def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlen
     cu_seqlens_q int32 [B + 1]; all on the device; max_seqlen_q / max_seqlen_k host bounds
     of every sequence's query and key counts.  Returns ``(out, lse)``, lse [Hq, total_q].
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
         raise ValueError("q must be [total_q, Hq, D] and the page pools [P, page, Hkv, D]")
@@ -446,8 +450,6 @@ def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlen
     if block_table.dim() != 2 or tuple(seq_lens_k.shape) != (B,) or tuple(cu_seqlens_q.shape) != (B + 1,):
         raise ValueError("block_table must be [B, max_pages], seq_lens_k [B], cu_seqlens_q [B + 1]")
     dt = _dtype_code(q)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -467,7 +469,7 @@ def mfa_fwd_varlen_paged(q, k_pages, v_pages, block_table, seq_lens_k, cu_seqlen
     return out, lse
 
 
-def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
+def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float,
                      num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
                      workspace=None):
     """Paged split-KV decode on torch tensors.
@@ -476,6 +478,7 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
     [B, max_pages_per_seq]; seq_lens int32 [B] (device).  Returns ``(out, lse)``.
     ``workspace`` (any device tensor of enough bytes) is allocated here when absent.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
         raise ValueError("q must be [B, Hq, D] and the page pools [P, page, Hkv, D]")
@@ -491,8 +494,6 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | 
         raise TypeError("q and the page pools must share one dtype")
     dt = _dtype_code(q)
     max_pages = block_table.shape[1]
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is not None:
         _need(out, q.shape, q.dtype, "out")
     if lse is not None:
@@ -522,7 +523,7 @@ def mfa_decode_multi_workspace_bytes(B: int, Nq: int, Hq: int, D: int, page_size
                                                       num_splits))
 
 
-def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
+def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: float,
                            num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
                            workspace=None):
     """Paged split-KV decode of Nq <= 4 new tokens per sequence on torch tensors.
@@ -531,6 +532,7 @@ def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: fl
     [B, max_pages_per_seq]; seq_lens int32 [B] (the new tokens included).  Returns
     ``(out [B, Nq, Hq, D], lse [B, Nq, Hq])``.
     """
+    scale = _scale(scale)
     torch = _torch()
     if q.dim() != 4 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
         raise ValueError("q must be [B, Nq, Hq, D] and the page pools [P, page, Hkv, D]")
@@ -546,8 +548,6 @@ def mfa_decode_paged_multi(q, k_pages, v_pages, block_table, seq_lens, scale: fl
         raise TypeError("q and the page pools must share one dtype")
     dt = _dtype_code(q)
     max_pages = block_table.shape[1]
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if out is not None:
         _need(out, q.shape, q.dtype, "out")
     if lse is not None:

@@ -331,8 +331,31 @@ def _t(*shape, dtype=None):
 
 
 def _binding_error(fn, *args, match, **kw):
+    kw.setdefault("scale", 0.1)
     with pytest.raises((ValueError, TypeError), match=match):
         fn(*args, **kw)
+
+
+def test_binding_requires_scale():
+    # the scale multiplies Q K^T and has no default: omitting it, or passing None, is an error
+    # raised before anything reaches the library
+    import torch
+    q, k = _t(1, 2, 64, 64), _t(1, 2, 64, 64)
+    o, do, lse = _t(1, 2, 64, 64), _t(1, 2, 64, 64), _t(1, 2, 64, dtype=torch.float32)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    kp, bt, sl = _t(4, 16, 2, 64), torch.zeros(1, 4, dtype=torch.int32), torch.ones(1, dtype=torch.int32)
+    calls = [
+        (ea.mfa_fwd, (q, k, k)), (ea.mfa_fwd_ext, (q, k, k)), (ea.mfa_bwd, (q, k, k, o, do, lse)),
+        (ea.mfa_fwd_varlen, (q[0].transpose(0, 1).contiguous(),) * 3 + (cu, cu, 64, 64)),
+        (ea.mfa_fwd_varlen_paged, (q[0].transpose(0, 1).contiguous(), kp, kp, bt, sl, cu, 64, 64)),
+        (ea.mfa_decode_paged, (_t(1, 2, 64), kp, kp, bt, sl)),
+        (ea.mfa_decode_paged_multi, (_t(1, 1, 2, 64), kp, kp, bt, sl)),
+    ]
+    for fn, args in calls:
+        with pytest.raises(TypeError, match="scale"):
+            fn(*args)
+        with pytest.raises(ValueError, match="scale is required"):
+            fn(*args, scale=None)
 
 
 def test_binding_checks_backward_shapes_and_types():
