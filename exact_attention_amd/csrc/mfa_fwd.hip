@@ -165,7 +165,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // Chained tiles (dense inputs, two wave groups): a workgroup runs a long causal
     // query tile and then its complementary short one, so every workgroup has the same
     // work and the second tile starts without a new workgroup launch.
-    constexpr bool CAN_CHAIN = MODE == 0 && GROUPS == 2 && !TILELOG;
+    constexpr bool CAN_CHAIN = MODE == 0 && GROUPS == 2;
     const int n_rep = (CAN_CHAIN && a.chain) ? 2 : 1;
     for (int rep = 0; rep < n_rep; ++rep) {
     // ---- which (query tile, batch, head) -------------------------------------------
@@ -933,7 +933,7 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     long long q_tiles = (long long)a.n_q_tiles * pr.B;
     if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
     const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
-    a.chain = (mode == 0 && groups == 2 && !tl && a.n_q_tiles % 2 == 0) ? 1 : 0;
+    a.chain = (mode == 0 && groups == 2 && a.n_q_tiles % 2 == 0) ? 1 : 0;
     if (mode == 3) return launch_dt<3>(pr, a, stream, groups, tl, neg, info);
     if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
     if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);

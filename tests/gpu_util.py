@@ -93,3 +93,30 @@ def assert_close_grads(names, gots, refs, dtype):
         if err > tol:
             bad.append(f"{name}: max |d| = {err:.3e} > {tol:.3e}")
     assert not bad, "; ".join(bad)
+
+
+def oracle_heads(qf, kf, vf, scale, causal, left, right, heads, workers=None):
+    """``oracle.attention`` over whole heads, several at once.
+
+    ``heads`` lists (b, h) pairs; query head h reads KV head h // (Hq / Hkv) (consecutive
+    grouping), passed to the oracle as a one-head problem.  Threads run the heads side by
+    side (numpy releases the GIL inside its array arithmetic) with BLAS limited to one
+    thread each.  Returns {(b, h): (O [Nq, D], LSE [Nq])}."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    g = qf.shape[1] // kf.shape[1]
+
+    def one(bh):
+        b, h = bh
+        kv = h // g
+        O, L = oracle.attention(qf[b:b + 1, h:h + 1], kf[b:b + 1, kv:kv + 1],
+                                vf[b:b + 1, kv:kv + 1], scale, causal, left, right)
+        return O[0, 0], L[0, 0]
+
+    n = workers or max(1, min(16, os.cpu_count() or 1, len(heads)))
+    with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+        return dict(zip(heads, ex.map(one, heads)))
