@@ -18,10 +18,15 @@ shape in bf16 (``mfa_bwd``: dQ and dK/dV launches; TFLOP/s at 10*D FLOP per visi
 pair).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
-workload first, then K timed steps per workload; ``torch.cuda.synchronize()`` on both
-sides of each timed region.
+workload first, then K timed steps per workload, each call between its own pair of events;
+``torch.cuda.synchronize()`` on both sides of each timed region.  ``ms_per_step`` and
+``value`` cover the whole block of K calls (launch gaps included); the mean, median and min
+of the per-call event times are reported beside it, and ``roofline.achieved`` divides the
+algorithmic work by the mean per-call time (the kernel's average launch duration).
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
-same prefill workload, for about 10 s, and scales to TFLOP/s.
+same prefill workload, for about 10 s, scales to TFLOP/s, names the CPU model, and
+reports the max-abs difference between the GPU's O and LSE and the oracle's on those
+heads.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workloads NAME,...] [--no-cpu-baseline]
 (workload names as in attn_inputs.WORKLOADS; default: all but tiny_dense)
@@ -101,24 +106,30 @@ def to_dev(bits, dtype):
 
 
 def time_calls(fn, steps):
-    """Time `steps` back-to-back calls as one block.
+    """Time `steps` back-to-back calls, each between two HIP events.
 
-    HIP events are recorded on the current stream (the one the library launches on)
-    right before the first and after the last call, with torch.cuda.synchronize() on
-    both sides.  Returns (ms per call, wall ms of the block).
-    """
+    The events are recorded on the current stream (the one the library launches on), with
+    torch.cuda.synchronize() on both sides of the block.  Returns a dict: ms per call over
+    the whole block (launch gaps included), the mean, median and min of the per-call event
+    times, and the wall time of the block."""
     import torch
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    for e0, e1 in ev:
+        e0.record()
         fn()
-    e1.record()
+        e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    return e0.elapsed_time(e1) / steps, wall
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return {"ms_per_call": ev[0][0].elapsed_time(ev[-1][1]) / steps, "mean_ms": float(per.mean()),
+            "median_ms": float(np.median(per)), "min_ms": float(per.min()), "wall_ms": wall}
+
+
+def timing_fields(t):
+    return {k: t[k] for k in ("ms_per_call", "mean_ms", "median_ms", "min_ms", "wall_ms")}
 
 
 def setup_prefill(name):
@@ -136,23 +147,26 @@ def setup_prefill(name):
         ea.mfa_fwd(q, k, v, scale=c["scale"], causal=c["causal"], win_left=c["left"],
                    win_right=c["right"], out=out, lse=lse)
 
+    step.out, step.lse = out, lse
     return step
 
 
 def bench_prefill(name, step, steps):
     import exact_attention_amd as ea
     c = A.workload(name)
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     flop = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], c["left"], c["right"]) \
         * c["B"] * c["Hq"]
     tf = flop / (ms * 1e-3) / 1e12
+    tk = flop / (t["mean_ms"] * 1e-3) / 1e12
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['Nq']} D={c['D']} "
                     f"{c['dtype']} causal={int(c['causal'])} window=({c['left']},{c['right']})",
-        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16,
+        "tflops": tf, **timing_fields(t), "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tk / PEAK_MFMA_F16,
                      "traffic": measured_traffic(name, "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "planned_tiles": info["planned"],
         "dtype": c["dtype"],
@@ -184,19 +198,21 @@ def setup_varlen():
 def bench_varlen(step, steps):
     import exact_attention_amd as ea
     c = A.workload("packed_varlen_causal_prefill")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     lq, lk = step.lens
     pairs = sum(visible_pairs(int(a), int(b), c["causal"], c["left"], c["right"]) for a, b in zip(lq, lk))
     flop = 4.0 * c["D"] * pairs * c["Hq"]
     tf = flop / (ms * 1e-3) / 1e12
+    tk = flop / (t["mean_ms"] * 1e-3) / 1e12
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {c['dtype']} "
                     f"causal={int(c['causal'])} lengths in [{c['len_lo']},{c['len_hi']}] "
                     f"(total {int(lq.sum())} tokens)",
-        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("packed_varlen_causal_prefill", "fwd")},
+        "tflops": tf, **timing_fields(t), "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tk / PEAK_MFMA_F16, "traffic": measured_traffic("packed_varlen_causal_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -230,19 +246,21 @@ def setup_chunked():
 def bench_chunked(step, steps):
     import exact_attention_amd as ea
     c = A.workload("paged_chunked_prefill")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     lq, lk = step.lens
     pairs = sum(visible_pairs(int(a), int(b), c["causal"], c["left"], c["right"]) for a, b in zip(lq, lk))
     flop = 4.0 * c["D"] * pairs * c["Hq"]
     tf = flop / (ms * 1e-3) / 1e12
+    tk = flop / (t["mean_ms"] * 1e-3) / 1e12
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {c['dtype']} "
                     f"page=16 new tokens {int(lq.sum())} in chunks of [{c['new_lo']},{c['new_hi']}], "
                     f"cached keys {int(lk.sum())}",
-        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("paged_chunked_prefill", "fwd")},
+        "tflops": tf, **timing_fields(t), "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tk / PEAK_MFMA_F16, "traffic": measured_traffic("paged_chunked_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -284,16 +302,18 @@ def setup_decode():
 def bench_decode(step, steps):
     import exact_attention_amd as ea
     c = A.workload("paged_splitkv_decode")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"])
     gbs = nb / (ms * 1e-3) / 1e9
+    gk = nb / (t["mean_ms"] * 1e-3) / 1e9
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} bf16 "
                     f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
-        "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("paged_splitkv_decode", "decode")},
+        "gbs": gbs, **timing_fields(t), "bytes": nb,
+        "roofline": {"bound": "hbm", "achieved": gk, "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": gk / PEAK_HBM, "traffic": measured_traffic("paged_splitkv_decode", "decode")},
         "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
         "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
     }
@@ -326,16 +346,18 @@ def setup_multi():
 def bench_multi(step, steps):
     import exact_attention_amd as ea
     c = A.workload("paged_multi_query_decode")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     nb = decode_bytes(step, c["Hkv"], c["D"], c["Hq"], c["Nq"])
     gbs = nb / (ms * 1e-3) / 1e9
+    gk = nb / (t["mean_ms"] * 1e-3) / 1e9
     return {
         "workload": f"{c['name']} B={c['B']} Nq={c['Nq']} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} bf16 "
                     f"page=16 seq_lens in [1024,32768] (sum={int(step.seq_lens.sum())})",
-        "gbs": gbs, "ms_per_call": ms, "wall_ms": wall, "bytes": nb,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM, "traffic": measured_traffic("paged_multi_query_decode", "decode")},
+        "gbs": gbs, **timing_fields(t), "bytes": nb,
+        "roofline": {"bound": "hbm", "achieved": gk, "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": gk / PEAK_HBM, "traffic": measured_traffic("paged_multi_query_decode", "decode")},
         "kernel": info["kernel"], "grid": info["grid"], "num_splits": info["num_splits"],
         "chunk_tokens": info["chunk_tokens"], "dtype": c["dtype"],
     }
@@ -377,18 +399,20 @@ def setup_sparse():
 def bench_sparse(step, steps):
     import exact_attention_amd as ea
     c = A.workload("block_sparse_causal_prefill")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     flop = 4.0 * c["D"] * step.pairs
     tf = flop / (ms * 1e-3) / 1e12
+    tk = flop / (t["mean_ms"] * 1e-3) / 1e12
     dense = 4.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], True, -1, -1) * c["B"] * c["Hq"]
     return {
         "workload": f"{c['name']} B={c['B']} H={c['Hq']} N={c['Nq']} D={c['D']} {c['dtype']} causal, "
                     f"{c['block_q']}x{c['block_k']} block mask, {step.density:.3f} of blocks on "
                     f"({step.pairs / (dense / (4.0 * c['D'])):.3f} of the causal pairs)",
-        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16, "traffic": measured_traffic("block_sparse_causal_prefill", "fwd")},
+        "tflops": tf, **timing_fields(t), "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tk / PEAK_MFMA_F16, "traffic": measured_traffic("block_sparse_causal_prefill", "fwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
@@ -418,56 +442,80 @@ def setup_backward():
 def bench_backward(step, steps):
     import exact_attention_amd as ea
     c = A.workload("dense_causal_backward")
-    ms, wall = time_calls(step, steps)
+    t = time_calls(step, steps)
+    ms = t["ms_per_call"]
     info = ea.mfa_last_dispatch()
     # 10 D FLOP per visible pair: the five products S = Q K^T, dP = dO V^T, dV = P^T dO,
     # dQ = dS K and dK = dS^T Q (2 D each)
     flop = 10.0 * c["D"] * visible_pairs(c["Nq"], c["Nk"], c["causal"], -1, -1) * c["B"] * c["Hq"]
     tf = flop / (ms * 1e-3) / 1e12
+    tk = flop / (t["mean_ms"] * 1e-3) / 1e12
     return {
         "workload": f"{c['name']} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['Nq']} D={c['D']} "
                     f"{c['dtype']} causal=1 (dQ + dK/dV launches)",
-        "tflops": tf, "ms_per_call": ms, "wall_ms": wall, "flop": flop,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_MFMA_F16,
+        "tflops": tf, **timing_fields(t), "flop": flop,
+        "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": tk / PEAK_MFMA_F16,
                      "traffic": measured_traffic("dense_causal_backward", "bwd")},
         "kernel": info["kernel"], "grid": info["grid"], "dtype": c["dtype"],
     }
 
 
-def cpu_baseline(budget_s=10.0):
-    """The float64 oracle on this host over whole heads of the dense causal prefill."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(gpu_out=None, budget_s=10.0):
+    """The float64 oracle on this host over whole heads of the dense causal prefill.
+
+    With gpu_out = (O, LSE) of the GPU run on the same inputs, the heads the oracle
+    finished are also compared with it (max-abs error of O and of LSE)."""
     import oracle
     from threadpoolctl import threadpool_info
     c = A.workload("dense_causal_prefill")
     x = A.workload_inputs("dense_causal_prefill")
     q, k, v = (oracle.widen(t, c["dtype"]) for t in (x.q, x.k, x.v))
     pairs = visible_pairs(c["Nq"], c["Nk"], True, -1, -1)
-    done = 0
+    done = []
     t0 = time.perf_counter()
     for b in range(c["B"]):
         for h in range(c["Hq"]):
-            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                             c["scale"], True)
-            done += 1
+            O, L = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                    c["scale"], True)
+            done.append((b, h, O[0, 0], L[0, 0]))
             if time.perf_counter() - t0 > budget_s:
                 break
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    flop = 4.0 * c["D"] * pairs * done
+    flop = 4.0 * c["D"] * pairs * len(done)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of 16 (b,h) heads of the B=2 H=8 N=4096 D=128 causal workload, "
-                      f"float64 numpy oracle, {dt:.1f} s wall, BLAS threads={threads}, "
-                      f"os.cpu_count()={os.cpu_count()}"}
+    res = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{len(done)} of 16 (b,h) heads of the B=2 H=8 N=4096 D=128 causal workload, "
+                     f"float64 numpy oracle, {dt:.1f} s wall, BLAS threads={threads}, "
+                     f"os.cpu_count()={os.cpu_count()}",
+           "cpu_model": cpu_model()}
+    if gpu_out is not None:
+        Ob, Lg = gpu_out
+        eo = max(float(np.abs(oracle.widen(Ob[b, h], c["dtype"]) - O).max()) for b, h, O, _ in done)
+        el = max(float(np.abs(Lg[b, h] - L).max()) for b, h, _, L in done)
+        res["max_abs_err_vs_gpu"] = {"O": eo, "LSE": el, "heads": len(done),
+                                     "bound": {"O": 2e-3, "LSE": 1e-3}}
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", default=",".join(w for w in A.WORKLOADS if w != "tiny_dense"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -517,6 +565,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_call"], 5),
+        "per_call_ms": {"mean": round(head["mean_ms"], 5), "median": round(head["median_ms"], 5),
+                        "min": round(head["min_ms"], 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -527,7 +577,8 @@ def main():
         "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+        bits = steps[HEAD].out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        line["cpu_baseline"] = cpu_baseline((bits, steps[HEAD].lse.cpu().numpy()))
     line["workloads"] = {
         n: {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
         for n, r in res.items()}

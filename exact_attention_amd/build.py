@@ -37,19 +37,26 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
+    from concurrent.futures import ThreadPoolExecutor
+
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
     cc = hipcc()
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
         cmd = [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE,
-               "-I", CSRC, *lang, "-c",
-               os.path.join(CSRC, src), "-o", obj]
+               "-I", CSRC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return src, obj, cmd, r
+
+    # the sources compile independently (the forward kernel's file takes the longest)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    objs = []
+    for src, obj, cmd, r in results:
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
         if verbose and r.stderr.strip():
