@@ -18,11 +18,12 @@ shape in bf16 (``mfa_bwd``: dQ and dK/dV launches; TFLOP/s at 10*D FLOP per visi
 pair).
 
 Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
-workload first, then K timed steps per workload, each call between its own pair of events;
-``torch.cuda.synchronize()`` on both sides of each timed region.  ``ms_per_step`` and
-``value`` cover the whole block of K calls (launch gaps included); the mean, median and min
-of the per-call event times are reported beside it, and ``roofline.achieved`` divides the
-algorithmic work by the mean per-call time (the kernel's average launch duration).
+workload first, then K timed steps per workload as one block between two events, then K
+more with each call between its own pair of events; ``torch.cuda.synchronize()`` on both
+sides of each timed region.  ``ms_per_step`` and ``value`` cover the block of K calls
+(launch gaps included); the mean, median and min of the per-call event times are reported
+beside it, and ``roofline.achieved`` divides the algorithmic work by the mean per-call
+time (the kernel's average launch duration).
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, scales to TFLOP/s, names the CPU model, and
 reports the max-abs difference between the GPU's O and LSE and the oracle's on those
@@ -106,25 +107,34 @@ def to_dev(bits, dtype):
 
 
 def time_calls(fn, steps):
-    """Time `steps` back-to-back calls, each between two HIP events.
+    """Time `steps` back-to-back calls, twice.
 
-    The events are recorded on the current stream (the one the library launches on), with
-    torch.cuda.synchronize() on both sides of the block.  Returns a dict: ms per call over
-    the whole block (launch gaps included), the mean, median and min of the per-call event
-    times, and the wall time of the block."""
+    First as one block between two HIP events (ms per call with the launch gaps, the
+    whole-job rate), then each call between its own pair of events (mean, median and min of
+    the per-call times: the kernels' own duration).  Events are recorded on the current
+    stream, the one the library launches on, with torch.cuda.synchronize() on both sides of
+    each pass.  An event between every two calls adds a few microseconds of gap on this
+    hardware, which is why the block is timed separately."""
     import torch
     torch.cuda.synchronize()
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    b0.record()
+    for _ in range(steps):
+        fn()
+    b1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for e0, e1 in ev:
         e0.record()
         fn()
         e1.record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3
     per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
-    return {"ms_per_call": ev[0][0].elapsed_time(ev[-1][1]) / steps, "mean_ms": float(per.mean()),
+    return {"ms_per_call": b0.elapsed_time(b1) / steps, "mean_ms": float(per.mean()),
             "median_ms": float(np.median(per)), "min_ms": float(per.min()), "wall_ms": wall}
 
 
@@ -143,10 +153,8 @@ def setup_prefill(name):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     del x
 
-    def step():
-        ea.mfa_fwd(q, k, v, scale=c["scale"], causal=c["causal"], win_left=c["left"],
-                   win_right=c["right"], out=out, lse=lse)
-
+    step = ea.prepare(ea.mfa_fwd, q, k, v, scale=c["scale"], causal=c["causal"], win_left=c["left"],
+                      win_right=c["right"], out=out, lse=lse)
     step.out, step.lse = out, lse
     return step
 
@@ -186,11 +194,9 @@ def setup_varlen():
     out = torch.empty_like(q)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
 
-    def step():
-        ea.mfa_fwd_varlen(q, k, v, cq, ck, int(lq.max()), int(lk.max()), scale=c["scale"],
-                          causal=c["causal"], win_left=c["left"], win_right=c["right"], out=out,
-                          lse=lse)
-
+    step = ea.prepare(ea.mfa_fwd_varlen, q, k, v, cq, ck, int(lq.max()), int(lk.max()),
+                      scale=c["scale"], causal=c["causal"], win_left=c["left"],
+                      win_right=c["right"], out=out, lse=lse)
     step.lens = (lq, lk)
     return step
 
@@ -233,12 +239,9 @@ def setup_chunked():
     out = torch.empty_like(q)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
 
-    def step():
-        ea.mfa_fwd_varlen_paged(q, kp, vp, bt, sl, cq, int(lq.max()), int(p.seq_lens_k.max()),
-                                scale=c["scale"],
-                                causal=c["causal"], win_left=c["left"], win_right=c["right"],
-                                out=out, lse=lse)
-
+    step = ea.prepare(ea.mfa_fwd_varlen_paged, q, kp, vp, bt, sl, cq, int(lq.max()),
+                      int(p.seq_lens_k.max()), scale=c["scale"], causal=c["causal"],
+                      win_left=c["left"], win_right=c["right"], out=out, lse=lse)
     step.lens = (lq, p.seq_lens_k.astype(np.int64))
     return step
 
@@ -291,9 +294,8 @@ def setup_decode():
     nbytes = ea.mfa_decode_workspace_bytes(c["B"], c["Hq"], c["D"], 16, bt.shape[1], 0)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-    def step():
-        ea.mfa_decode_paged(q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse, workspace=ws)
-
+    step = ea.prepare(ea.mfa_decode_paged, q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse,
+                      workspace=ws)
     step.seq_lens = p.seq_lens
     step.page_size = p.page_size
     return step
@@ -335,9 +337,8 @@ def setup_multi():
     nbytes = ea.mfa_decode_multi_workspace_bytes(c["B"], c["Nq"], c["Hq"], c["D"], 16, bt.shape[1], 0)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-    def step():
-        ea.mfa_decode_paged_multi(q, kp, vp, bt, sl, scale=c["scale"], out=out, lse=lse, workspace=ws)
-
+    step = ea.prepare(ea.mfa_decode_paged_multi, q, kp, vp, bt, sl, scale=c["scale"], out=out,
+                      lse=lse, workspace=ws)
     step.seq_lens = p.seq_lens
     step.page_size = p.page_size
     return step
@@ -387,10 +388,8 @@ def setup_sparse():
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
 
-    def step():
-        ea.mfa_fwd_ext(q, k, v, scale=c["scale"], causal=True, block_mask=bmd, block_q=c["block_q"],
-                       block_k=c["block_k"], out=out, lse=lse)
-
+    step = ea.prepare(ea.mfa_fwd_ext, q, k, v, scale=c["scale"], causal=True, block_mask=bmd,
+                      block_q=c["block_q"], block_k=c["block_k"], out=out, lse=lse)
     step.pairs = block_sparse_pairs(bm, c["Nq"], c["Nk"], c["block_q"], c["block_k"])
     step.density = float(bm.mean())
     return step
@@ -432,10 +431,8 @@ def setup_backward():
     ws = torch.empty(int(ea.lib().mfa_bwd_workspace_bytes(c["B"], c["Hq"], c["Nq"])),
                      dtype=torch.uint8, device="cuda")
 
-    def step():
-        ea.mfa_bwd(q, k, v, out, do, lse, scale=c["scale"], causal=c["causal"], dq=dq, dk=dk,
-                   dv=dv, workspace=ws)
-
+    step = ea.prepare(ea.mfa_bwd, q, k, v, out, do, lse, scale=c["scale"], causal=c["causal"],
+                      dq=dq, dk=dk, dv=dv, workspace=ws)
     return step
 
 
