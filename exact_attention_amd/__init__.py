@@ -82,6 +82,8 @@ _SIGS = {
     "mfa_decode_paged_multi": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
                                     _I, _F, _I, _VP, ctypes.c_size_t, _I, _VP]),
     "mfa_decode_num_splits": (_I, [_I, _I, _I]),
+    "mfa_decode_paged_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
+                                      _I, _F, _I, _I, _VP]),
     "mfa_decode_paged": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
                               _I, _VP, ctypes.c_size_t, _I, _VP]),
     "mfa_last_dispatch": (_I, [ctypes.POINTER(mfa_dispatch_info)]),
@@ -553,6 +555,37 @@ def mfa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float,
     return out, lse
 
 
+def mfa_decode_paged_noalloc(q, k_pages, v_pages, block_table, seq_lens, scale: float, out,
+                             lse=None, num_splits: int = 0):
+    """``mfa_decode_paged`` with the split partials in the library's fixed per-GPU scratch
+    (no workspace, nothing allocated by the call): ``out`` [B, Hq, D] and the optional
+    ``lse`` [B, Hq] float32 must be given.  Calls overlapping on one GPU race."""
+    scale = _scale(scale)
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B, Hq, D] and the page pools [P, page, Hkv, D]")
+    B, Hq, D = q.shape
+    P, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError("head dimension mismatch")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share one dtype")
+    _need(out, q.shape, q.dtype, "out")
+    if lse is not None:
+        _need(lse, (B, Hq), torch.float32, "lse")
+    _call("mfa_decode_paged_noalloc", 
+        _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None,
+        B, Hq, Hkv, D, page_size, P, block_table.shape[1], float(scale), int(num_splits),
+        _dtype_code(q), _stream(q))
+    return out, lse
+
+
 def mfa_decode_multi_workspace_bytes(B: int, Nq: int, Hq: int, D: int, page_size: int,
                                      max_pages_per_seq: int, num_splits: int = 0) -> int:
     return int(lib().mfa_decode_multi_workspace_bytes(B, Nq, Hq, D, page_size, max_pages_per_seq,
@@ -612,4 +645,5 @@ __all__ = ["MFA_F16", "MFA_BF16", "MfaError", "EXPORTS", "lib", "mfa_fwd", "mfa_
            "mfa_decode_paged_multi",
            "mfa_decode_multi_workspace_bytes",
            "mfa_decode_paged", "mfa_decode_workspace_bytes", "mfa_decode_num_splits",
+           "mfa_decode_paged_noalloc",
            "mfa_plan_fwd", "mfa_last_dispatch", "mfa_status_string", "mfa_version", "prepare"]

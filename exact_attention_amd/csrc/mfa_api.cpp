@@ -393,6 +393,22 @@ size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_p
     return (size_t)B * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
 }
 
+int mfa_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out,
+                             float* lse, int B, int Hq, int Hkv, int D, int page_size,
+                             int num_pages, int max_pages_per_seq, float scale, int num_splits,
+                             int dtype, void* stream) {
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const int st = mfa_decode_scratch(&ws, &ws_bytes);
+    if (st) return st;
+    // the partials must fit the fixed scratch: decode_common reports MFA_ERR_WORKSPACE
+    // otherwise, after the other argument checks
+    return decode_common(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, 1, Hq, Hkv, D,
+                         page_size, num_pages, max_pages_per_seq, scale, num_splits, ws, ws_bytes,
+                         dtype, stream, 0);
+}
+
 size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
                                         int max_pages_per_seq, int num_splits) {
     if (Nq < 1 || Nq > 4) return 0;

@@ -29,6 +29,8 @@
 // pattern) are never read: each page is addressed through a buffer resource whose
 // range ends at the last valid token, so such loads return zeros, and their scores
 // are set to -inf.
+#include <mutex>
+
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -665,6 +667,31 @@ int launch_mq_hpw(const DecArgs& a, hipStream_t stream, mfa_dispatch_info* info)
 }
 
 }  // namespace
+
+// Fixed scratch for callers that cannot allocate (mfa_decode_paged_noalloc): the split
+// partials live in this file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  On the host the array's
+// name is not a device address: host code uses only the address hipGetSymbolAddress gives
+// for the current device, looked up once per device on its first call.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+int mfa_decode_scratch(void** ptr, size_t* bytes) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MFA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MFA_ERR_HIP;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kDecodeScratchBytes;
+    return MFA_OK;
+}
 
 int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits) {
     // Auto: about 16 splits per sequence of maximal length, between 8 and 32 pages

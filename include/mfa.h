@@ -315,6 +315,27 @@ int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                      int max_pages_per_seq, float scale, int num_splits,
                      void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
+/* mfa_decode_paged without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The split partials live in a fixed scratch array inside the library, one
+ * per GPU, 32 MiB (33,554,432 bytes), held until the process ends; the call itself
+ * allocates nothing.  Arguments, layouts, device-side contract and results are those of
+ * mfa_decode_paged with the same num_splits (the same kernels run).
+ * Limit: the partials take mfa_decode_workspace_bytes(B, Hq, D, page_size,
+ * max_pages_per_seq, num_splits) bytes; above 32 MiB the call returns MFA_ERR_WORKSPACE
+ * (pass a smaller num_splits, or use mfa_decode_paged with a workspace of that size).
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap in time on
+ * the same GPU (concurrent streams or host threads) race and must be serialised by the
+ * caller.  Nothing in the scratch needs clearing between calls.
+ * Errors: those of mfa_decode_paged; MFA_ERR_HIP also if the scratch address cannot be
+ * obtained. */
+int mfa_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             void* out, float* lse,
+                             int B, int Hq, int Hkv, int D, int page_size, int num_pages,
+                             int max_pages_per_seq, float scale, int num_splits, int dtype,
+                             void* stream);
+
 /* Bytes of workspace mfa_decode_paged_multi needs (0 if the arguments are invalid). */
 size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
                                         int max_pages_per_seq, int num_splits);
