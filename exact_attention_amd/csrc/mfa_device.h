@@ -99,6 +99,18 @@ __device__ __forceinline__ void mfa_load16_lds(__amdgpu_buffer_rsrc_t r, void* l
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
 }
 
+// The same loads with the non-temporal cache policy (the nt bit), for data read exactly
+// once (a decode's KV cache): on this chip a plain streaming read of 1 GiB measured
+// 5.9 TB/s with the default policy and 6.7 TB/s with nt.
+constexpr int kMfaNonTemporal = 2;
+__device__ __forceinline__ mfa_u32x4 mfa_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(mfa_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kMfaNonTemporal));
+}
+__device__ __forceinline__ void mfa_load16_lds_nt(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0,
+                                             kMfaNonTemporal);
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes, lane i
 // names 4 consecutive 16-bit values (row i/4, columns 4*(i%4) .. +3 of a 4 x 16 block)
 // and receives column i of the block (rows 0..3), packed low to high.

@@ -69,6 +69,25 @@ def test_decode_vs_oracle(case):
     assert info["num_splits"] == ea.mfa_decode_num_splits(16, p.block_table.shape[1], 0)
 
 
+@pytest.mark.parametrize("B", [256, 257])
+def test_both_grids(B):
+    # up to 256 sequences the split kernel's grid lists only the non-empty chunks (each
+    # workgroup finds its item from seq_lens); above, the grid is (chunk, head group,
+    # sequence) and empty chunks return at once.  Both against the oracle, with zero-length
+    # and single-token sequences among them.
+    lens = np.random.default_rng(B).integers(0, 400, size=B)
+    lens[:3] = [0, 1, 16]
+    p = A.paged_inputs(B, 4, 1, 64, "bf16", 60 + B, len_lo=0, len_hi=400, seq_lens=lens,
+                       extra_pages=1)
+    d = Dev(p)
+    O, L = run(d, 0.11)
+    info = ea.mfa_last_dispatch()
+    assert (",flat" in info["kernel"]) == (B <= 256), info["kernel"]
+    Or, Lr = ref(p, 0.11)
+    assert_close_o(to_f64(O, "bf16"), Or, "bf16", f"decode O B={B}")
+    assert_close_lse(L.cpu().numpy(), Lr, f"decode LSE B={B}")
+
+
 def test_empty_sequence():
     import torch
     p = A.paged_inputs(3, 8, 2, 128, "bf16", 9, len_lo=1, len_hi=200, seq_lens=[0, 33, 200])

@@ -71,6 +71,22 @@ def test_multi_decode_vs_oracle(case):
     print(f"multi {case}: max|dO|={eo:.2e} max|dLSE|={el:.2e} {info['kernel']}")
 
 
+@pytest.mark.parametrize("B", [256, 257])
+def test_both_grids(B):
+    # the flattened grid of non-empty chunks (B <= 256) and the (chunk, head group, sequence)
+    # grid, with sequences shorter than the new tokens among them
+    lens = np.random.default_rng(B).integers(0, 300, size=B)
+    lens[:3] = [0, 2, 17]
+    p = A.paged_multi_inputs(B, 3, 4, 2, 64, "f16", 80 + B, len_lo=0, len_hi=300, seq_lens=lens,
+                             extra_pages=1)
+    O, L = run(Dev(p), 0.12)
+    info = ea.mfa_last_dispatch()
+    assert (",flat" in info["kernel"]) == (B <= 256), info["kernel"]
+    Or, Lr = ref(p, 0.12)
+    assert_close_o(to_f64(O, "f16"), Or, "f16", f"multi decode O B={B}")
+    assert_close_lse(L.cpu().numpy(), Lr, f"multi decode LSE B={B}")
+
+
 def test_fully_masked_rows():
     # with 2 cached tokens and 4 new ones, tokens 0 and 1 see nothing: O = 0, LSE = -inf
     import torch
