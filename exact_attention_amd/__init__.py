@@ -124,6 +124,7 @@ def _check(st: int, where: str):
 
 
 _RECORD = None   # list collecting (name, args) of library calls while prepare() runs
+_HELD = None     # list collecting the tensors behind those calls' pointers
 
 
 def _call(name: str, *args):
@@ -139,14 +140,15 @@ def prepare(fn, *args, **kw):
     """Run binding function ``fn(*args, **kw)`` once and return a callable that repeats its
     library call with the same marshalled arguments (the same tensors, outputs and stream),
     skipping the Python-side checks: for timing loops, where per-call marshalling would
-    otherwise set the pace.  The tensors must stay alive while the callable is used."""
-    global _RECORD
-    _RECORD = []
+    otherwise set the pace.  The callable holds references to every argument, so the
+    device memory its pointers name stays allocated while it exists."""
+    global _RECORD, _HELD
+    _RECORD, _HELD = [], []
     try:
         fn(*args, **kw)
-        calls = _RECORD
+        calls, held = _RECORD, _HELD
     finally:
-        _RECORD = None
+        _RECORD, _HELD = None, None
     if len(calls) != 1:
         raise RuntimeError(f"expected one library call, got {len(calls)}")
     name, cargs = calls[0]
@@ -157,6 +159,7 @@ def prepare(fn, *args, **kw):
         if st != 0:
             raise MfaError(st, name)
 
+    again.keep = (args, kw, held)   # the tensors behind the raw pointers in cargs
     return again
 
 
@@ -223,12 +226,19 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float16 / bfloat16)")
 
 
+def _hold(t):
+    """Note a tensor whose pointer is passed to the library (kept alive by prepare())."""
+    if _HELD is not None:
+        _HELD.append(t)
+    return t
+
+
 def _dev(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device (HIP) tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr()
+    return _hold(t).data_ptr()
 
 
 def _need(t, shape, dtype, name):
@@ -385,7 +395,7 @@ def mfa_fwd_ext(q, k, v, scale: float, causal: bool = False, win_left: int = -1,
             raise ValueError("bias must broadcast to [B, Hq, Nk]")
         if not bias.is_cuda:
             raise ValueError("bias must be a device tensor")
-        ext.bias = bias.data_ptr()
+        ext.bias = _hold(bias).data_ptr()
         ext.bias_stride_b, ext.bias_stride_h = b3.stride(0), b3.stride(1)
         keep.append(bias)
     if block_mask is not None:
@@ -395,7 +405,7 @@ def mfa_fwd_ext(q, k, v, scale: float, causal: bool = False, win_left: int = -1,
         b4 = bm.expand(B, Hq, bm.shape[2], bm.shape[3])
         if b4.stride(2) != bm.shape[3]:
             raise ValueError("block_mask rows must be contiguous")
-        ext.block_mask = bm.data_ptr()
+        ext.block_mask = _hold(bm).data_ptr()
         ext.mask_stride_b, ext.mask_stride_h = b4.stride(0), b4.stride(1)
         ext.mask_q_blocks, ext.mask_k_blocks = bm.shape[2], bm.shape[3]
         ext.block_q, ext.block_k = int(block_q), int(block_k)

@@ -209,3 +209,27 @@ def test_deterministic():
     O0, L0 = run(q, k, v, 0.08, causal=True)
     O1, L1 = run(q, k, v, 0.08, causal=True)
     assert torch.equal(O0.view(torch.int16), O1.view(torch.int16)) and torch.equal(L0, L1)
+
+
+def test_prepared_call_holds_its_tensors():
+    # ea.prepare() repeats a call with marshalled raw pointers; the callable must keep the
+    # tensors behind them (inputs, and outputs the binding allocated itself) alive after the
+    # caller drops its references, or their memory would be handed to other tensors
+    import torch
+
+    def make():
+        x = A.dense_inputs(1, 4, 2, 300, 300, 128, "f16", 41)
+        q, k, v = (to_dev(t, "f16") for t in (x.q, x.k, x.v))
+        return ea.prepare(ea.mfa_fwd, q, k, v, scale=0.09, causal=True), x
+
+    step, x = make()
+    junk = [torch.full((1 << 20,), 7.0, dtype=torch.float16, device="cuda") for _ in range(8)]
+    step()
+    torch.cuda.synchronize()
+    out, lse = step.keep[2][3], step.keep[2][4]   # held in marshalling order: q, k, v, out, lse
+    assert tuple(out.shape) == (1, 4, 300, 128) and tuple(lse.shape) == (1, 4, 300)
+    qf, kf, vf = (oracle.widen(t, "f16") for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention(qf, kf, vf, 0.09, True)
+    assert_close_o(to_f64(out, "f16"), Or, "f16", "prepared O")
+    assert_close_lse(lse.cpu().numpy(), Lr, "prepared LSE")
+    del junk
