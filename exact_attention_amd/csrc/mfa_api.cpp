@@ -195,8 +195,8 @@ int varlen_paged_common(const void* q, const void* k_pages, const void* v_pages,
     return MFA_OK;
 }
 
-int decode_splits(int max_pages, int num_splits, int* chunk_pages) {
-    const int c = mfa_decode_chunk_pages(max_pages, num_splits);
+int decode_splits(int max_pages, int num_splits, int nq, int* chunk_pages) {
+    const int c = mfa_decode_chunk_pages(max_pages, num_splits, nq);
     if (chunk_pages) *chunk_pages = c;
     return (max_pages + c - 1) / c;
 }
@@ -221,7 +221,7 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
         return MFA_ERR_ALIGN;
     if ((double)num_pages * page_size * Hkv * D > 4e18) return MFA_ERR_OVERFLOW;
     int chunk_pages = 0;
-    const int S = decode_splits(max_pages_per_seq, num_splits, &chunk_pages);
+    const int S = decode_splits(max_pages_per_seq, num_splits, Nq, &chunk_pages);
     const size_t need = (size_t)B * (size_t)Nq * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
     if (!workspace || workspace_bytes < need) return MFA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MFA_ERR_ALIGN;
@@ -382,7 +382,7 @@ int mfa_fwd_varlen_paged(const void* q, const void* k_pages, const void* v_pages
 int mfa_decode_num_splits(int page_size, int max_pages_per_seq, int num_splits) {
     if (page_size != 16 || max_pages_per_seq < 1) return MFA_ERR_PAGED;
     if (num_splits < 0) return MFA_ERR_ARG;
-    return decode_splits(max_pages_per_seq, num_splits, nullptr);
+    return decode_splits(max_pages_per_seq, num_splits, 1, nullptr);
 }
 
 size_t mfa_decode_workspace_bytes(int B, int Hq, int D, int page_size, int max_pages_per_seq,
@@ -411,9 +411,10 @@ int mfa_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_p
 
 size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
                                         int max_pages_per_seq, int num_splits) {
-    if (Nq < 1 || Nq > 4) return 0;
-    const size_t one = mfa_decode_workspace_bytes(B, Hq, D, page_size, max_pages_per_seq, num_splits);
-    return one * (size_t)Nq;
+    if (Nq < 1 || Nq > 4 || B < 1 || Hq < 1 || (D != 64 && D != 128)) return 0;
+    if (page_size != 16 || max_pages_per_seq < 1 || num_splits < 0) return 0;
+    const int S = decode_splits(max_pages_per_seq, num_splits, Nq, nullptr);
+    return (size_t)B * (size_t)Nq * (size_t)Hq * (size_t)S * (size_t)(D + 1) * sizeof(float);
 }
 
 int mfa_decode_paged(const void* q, const void* k_pages, const void* v_pages,

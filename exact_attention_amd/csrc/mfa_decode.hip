@@ -764,17 +764,22 @@ int mfa_decode_scratch(void** ptr, size_t* bytes) {
     return MFA_OK;
 }
 
-int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits) {
-    // Auto: about 16 splits per sequence of maximal length, between 8 and 32 pages
-    // (128 .. 512 tokens) per split.  Chunks are a multiple of 8 pages (2 per wave).
+int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits, int nq) {
+    // Auto, one new token: about 32 splits per sequence of maximal length, between 8 and
+    // 64 pages (128 .. 1024 tokens) per split (on the decode workload 1024-token chunks
+    // measured 199 us per call against 204 us with 512-token ones).  Several new tokens:
+    // about 24 splits, up to 128 pages each; their partials are nq times larger, and on
+    // the 4-token decode workload 1408-token chunks measured 182 us against 198 us with
+    // 512-token ones.  Chunks are a multiple of 8 pages (2 per wave).
     int want;
     if (num_splits > 0)
         want = (max_pages_per_seq + num_splits - 1) / num_splits;
     else
-        want = max_pages_per_seq / 16;
+        want = nq > 1 ? max_pages_per_seq / 24 : max_pages_per_seq / 32;
     int c = ((want + 7) / 8) * 8;
     if (c < 8) c = 8;
-    if (num_splits == 0 && c > 32) c = 32;
+    const int cap = nq > 1 ? 128 : 64;
+    if (num_splits == 0 && c > cap) c = cap;
     return c;
 }
 

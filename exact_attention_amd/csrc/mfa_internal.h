@@ -77,7 +77,8 @@ int mfa_fwd_launch(const MfaFwdProblem& p, hipStream_t stream, mfa_dispatch_info
 
 int mfa_bwd_launch(const MfaBwdProblem& p, hipStream_t stream, mfa_dispatch_info* info);
 
-int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits);
+// Pages per split of the decode kernels for nq new tokens per sequence.
+int mfa_decode_chunk_pages(int max_pages_per_seq, int num_splits, int nq);
 // Device address and size of the current device's fixed decode scratch (looked up once per
 // device); MFA_ERR_HIP if the lookup fails.
 int mfa_decode_scratch(void** ptr, size_t* bytes);

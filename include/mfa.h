@@ -336,7 +336,8 @@ int mfa_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_p
                              int max_pages_per_seq, float scale, int num_splits, int dtype,
                              void* stream);
 
-/* Bytes of workspace mfa_decode_paged_multi needs (0 if the arguments are invalid). */
+/* Bytes of workspace mfa_decode_paged_multi needs: B * Nq * Hq * S * (D + 1) * 4, with S the
+ * number of key splits it uses for these sizes (0 if the arguments are invalid). */
 size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_size,
                                         int max_pages_per_seq, int num_splits);
 
@@ -349,7 +350,9 @@ size_t mfa_decode_multi_workspace_bytes(int B, int Nq, int Hq, int D, int page_s
  * Nk = seq_lens[b], causal).  The g * Nq query rows of one KV head are computed together.
  *   q    [B, Nq, Hq, D] dtype        out [B, Nq, Hq, D] dtype    lse [B, Nq, Hq] float32 or NULL
  *   k_pages, v_pages, block_table, seq_lens, page_size, num_pages, max_pages_per_seq,
- *   num_splits: as for mfa_decode_paged, with the same device-side contract.
+ *   num_splits: as for mfa_decode_paged, with the same device-side contract; the automatic
+ *   split count (num_splits 0) is lower than mfa_decode_paged's when Nq > 1 (longer
+ *   chunks, since each split's partials are Nq times larger).
  *   workspace: at least mfa_decode_multi_workspace_bytes(...) bytes of device memory.
  * A row with no visible key (seq_lens[b] < Nq - n) gets O = 0 and LSE = -inf.
  * Errors: MFA_ERR_NULL, _DTYPE, _HEAD_DIM, _SHAPE (also Nq outside 1..4), _GQA, _PAGED,

@@ -285,9 +285,17 @@ def test_decode_multi_validation(kw, code):
 
 
 def test_multi_workspace_bytes():
+    # B * Nq * Hq * S * (D + 1) floats.  One token: the single-token decode's split count;
+    # with explicit num_splits the same count for every Nq; auto with Nq > 1: 2048 pages in
+    # chunks of 88 (24 splits)
     one = ea.mfa_decode_workspace_bytes(16, 32, 128, 16, 2048, 0)
+    assert ea.mfa_decode_multi_workspace_bytes(16, 1, 32, 128, 16, 2048, 0) == one
     for nq in (1, 2, 3, 4):
-        assert ea.mfa_decode_multi_workspace_bytes(16, nq, 32, 128, 16, 2048, 0) == nq * one
+        assert ea.mfa_decode_multi_workspace_bytes(16, nq, 32, 128, 16, 2048, 7) == \
+            nq * ea.mfa_decode_workspace_bytes(16, 32, 128, 16, 2048, 7)
+    for nq in (2, 3, 4):
+        assert ea.mfa_decode_multi_workspace_bytes(16, nq, 32, 128, 16, 2048, 0) == \
+            16 * nq * 32 * 24 * 129 * 4
     assert ea.mfa_decode_multi_workspace_bytes(16, 5, 32, 128, 16, 2048, 0) == 0
     assert ea.mfa_decode_multi_workspace_bytes(16, 0, 32, 128, 16, 2048, 0) == 0
 
@@ -299,7 +307,7 @@ def test_workspace_and_splits():
         if ns > 0:
             assert S <= ns
         assert ea.mfa_decode_workspace_bytes(16, 32, 128, 16, max_pages, ns) == 16 * 32 * S * 129 * 4
-    assert ea.mfa_decode_num_splits(16, 2048, 0) == 64
+    assert ea.mfa_decode_num_splits(16, 2048, 0) == 32   # auto: 64-page chunks
     assert ea.mfa_decode_workspace_bytes(16, 32, 128, 8, 2048, 0) == 0
     with pytest.raises(ea.MfaError):
         ea.mfa_decode_num_splits(16, 0, 0)
