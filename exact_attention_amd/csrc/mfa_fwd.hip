@@ -608,13 +608,20 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
 
         const bool full = use_list ? ((ent >> 28) & 1) != 0 : mfa_tile_full(mask, kBM, BN, qt, kt);
         if (!full) {
-            const int k0 = kt * BN;
+            // element r of key block nb holds key base + c with c = 32 nb + 16 (r / 8) + r % 8
+            // (a constant), base = kt * BN + 8 g32; it is visible iff lo <= c <= lo + span with
+            // the row's bounds rebased to base: one unsigned compare per element.  A row that
+            // sees no key gets lo far below every c, so every compare fails.
+            const int base = kt * BN + 8 * g32;
+            const bool any = row_hi >= row_lo;
+            const int lo = any ? row_lo - base : -(1 << 30);
+            const uint32_t span = any ? (uint32_t)(row_hi - row_lo) : 0u;
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + nb * 32 + 16 * (r >> 3) + 8 * g32 + (r & 7);
-                    const bool vis = key >= row_lo && key <= row_hi &&
+                    const int c = nb * 32 + 16 * (r >> 3) + (r & 7);
+                    const bool vis = (uint32_t)(c - lo) <= span &&
                                      (!use_list || ((ent >> (20 + 2 * wave + nb)) & 1) != 0);
                     s_cur[nb][r] = vis ? s_cur[nb][r] : (NEG ? MFA_INF : -MFA_INF);
                 }
