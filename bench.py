@@ -17,9 +17,10 @@ TFLOP/s over the computed visible pairs), and the backward over the dense causal
 shape in bf16 (``mfa_bwd``: dQ and dK/dV launches; TFLOP/s at 10*D FLOP per visible
 pair).
 
-Timing: HIP events on the stream the kernels run on; W untimed warm-up steps of every
-workload first, then K timed steps per workload as one block between two events, then K
-more with each call between its own pair of events; ``torch.cuda.synchronize()`` on both
+Timing: HIP events on the stream the kernels run on; per workload, W untimed warm-up
+steps (continued until at least 30 ms of back-to-back calls have run, so that the clock
+has settled), then K timed steps as one block between two events, then K more with each
+call between its own pair of events; ``torch.cuda.synchronize()`` on both
 sides of each timed region.  ``ms_per_step`` and ``value`` cover the block of K calls
 (launch gaps included); the mean, median and min of the per-call event times are reported
 beside it, and ``roofline.achieved`` divides the algorithmic work by the mean per-call
@@ -136,6 +137,26 @@ def time_calls(fn, steps):
     per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
     return {"ms_per_call": b0.elapsed_time(b1) / steps, "mean_ms": float(per.mean()),
             "median_ms": float(np.median(per)), "min_ms": float(per.min()), "wall_ms": wall}
+
+
+WARM_MS = 30.0   # back-to-back work that brings the clock up after an idle gap
+
+
+def warm_up(fn, n):
+    """n untimed calls right before a workload's timed calls, continued (in groups of four)
+    until at least WARM_MS of back-to-back calls have run: after an idle gap the clock
+    takes some 20 ms of load to settle, which would otherwise show in the first timed
+    calls of a long kernel."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
 
 
 def timing_fields(t):
@@ -542,14 +563,9 @@ def main():
              "paged_chunked_prefill": bench_chunked, "paged_multi_query_decode": bench_multi,
              "block_sparse_causal_prefill": bench_sparse, "dense_causal_backward": bench_backward}
     steps = {n: (setup[n]() if n in setup else setup_prefill(n)) for n in wl}
-    # the W untimed warm-up steps of every workload run first, so that the first timed
-    # workload does not meet a GPU still ramping its clocks
-    for n in wl:
-        for _ in range(args.warmup):
-            steps[n]()
-    torch.cuda.synchronize()
     res = {}
     for n in wl:
+        warm_up(steps[n], args.warmup)
         res[n] = timed[n](steps[n], args.steps) if n in timed else bench_prefill(n, steps[n], args.steps)
         print(f"# workload {n}: " + json.dumps(res[n]), file=sys.stderr, flush=True)
 

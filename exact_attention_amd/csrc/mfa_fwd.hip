@@ -83,6 +83,7 @@ struct FwdArgs {
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
     int chain;       // 1: each workgroup runs query tile n_q_tiles - 1 - r, then tile r
+    int pair;        // 1: the two wave groups take two query heads of one KV head
     float scale_log2_abs;  // |scale| * log2(e)
     MfaMask mask;    // dense layout only (packed sequences build theirs per sequence)
     // packed sequences ([total, H, D] token-major, delimited by cu_seqlens)
@@ -141,7 +142,7 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int total, 
 //   and an optional block-sparse mask: the workgroup first lists the key tiles of its
 //   causal / window range that hold a computed block (a compacted list in LDS, with
 //   per-(wave, 32-key block) visibility bits and a no-mask flag), then walks the list.
-template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, int MODE>
+template <int D, int DT, int GROUPS, bool TILELOG, bool NEG, int MODE, bool PAIR>
 __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdArgs a) {
     constexpr bool VAR = MODE == 1 || MODE == 2;   // packed sequences
     constexpr bool PAGED = MODE == 2;
@@ -151,21 +152,22 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NNB = BN / 32;  // 32-key blocks of a tile
 
-    // per wave group: K buffers 0, 1 then V buffers 0, 1
-    __shared__ __attribute__((aligned(1024))) uint16_t smem_all[GROUPS * 4 * T::ELEMS];
+    // per wave group: K buffers 0, 1 then V buffers 0, 1 (one set for head pairs)
+    static_assert(!PAIR || (MODE == 0 && GROUPS == 2), "head pairs: dense inputs, two groups");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem_all[(PAIR ? 1 : GROUPS) * 4 * T::ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int grp = GROUPS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);   // wave group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);    // wave within its group
-    uint16_t* smem = smem_all + grp * 4 * T::ELEMS;
+    uint16_t* smem = smem_all + (PAIR ? 0 : grp * 4 * T::ELEMS);
     const int g32 = lane >> 5;
     const int l32 = lane & 31;
 
     // Chained tiles (dense inputs, two wave groups): a workgroup runs a long causal
     // query tile and then its complementary short one, so every workgroup has the same
     // work and the second tile starts without a new workgroup launch.
-    constexpr bool CAN_CHAIN = MODE == 0 && GROUPS == 2;
+    constexpr bool CAN_CHAIN = MODE == 0 && GROUPS == 2 && !PAIR;
     const int n_rep = (CAN_CHAIN && a.chain) ? 2 : 1;
     for (int rep = 0; rep < n_rep; ++rep) {
     // ---- which (query tile, batch, head) -------------------------------------------
@@ -182,13 +184,17 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
         // of one (batch, KV head) on the same XCD so its K/V stay in that L2
         const int x = w & 7, j = w >> 3;
-        const int pair = x + 8 * (j / a.g);
+        const int gg = PAIR ? a.g >> 1 : a.g;   // workgroups per (batch, KV head) and tile
+        const int pair = x + 8 * (j / gg);
         b = pair / a.Hkv;
-        h = (pair - b * a.Hkv) * a.g + (j % a.g);
+        h = (pair - b * a.Hkv) * gg + (j % gg);
     } else {
-        b = w / a.Hq;
-        h = w - b * a.Hq;
+        const int hq = PAIR ? a.Hq >> 1 : a.Hq;
+        b = w / hq;
+        h = w - b * hq;
     }
+    // head pairs: the workgroup's two groups take query heads 2h' and 2h' + 1 (one KV head)
+    if (PAIR) h = 2 * h + grp;
     const int kvh = h / a.g;
 
     // this (batch, head)'s sequence: lengths, first tokens and mask
@@ -230,7 +236,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int SK = VAR ? a.Hkv * D : D;
 
     // with two wave groups the visited key tiles [t_lo, t_hi) are split between them:
-    // group 0 takes the first ceil(n/2), group 1 the rest
+    // group 0 takes the first ceil(n/2), group 1 the rest (head pairs: each group walks all
+    // of them, over the one K/V stream the workgroup shares)
     int t_lo, t_hi;
     mfa_tile_range(mask, Nq, kBM, BN, qt, &t_lo, &t_hi);
     int n_all = t_hi - t_lo;
@@ -290,10 +297,11 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             n_all = tcount;
         }
     }
-    const int n0 = GROUPS == 1 ? n_all : (n_all + 1) >> 1;
-    const int kt_lo = grp == 0 ? t_lo : t_lo + n0;
-    const int n = grp == 0 ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
-    const int lbase = grp == 0 ? 0 : n0;        // this group's first list entry
+    const bool first = grp == 0 || PAIR;
+    const int n0 = (GROUPS == 1 || PAIR) ? n_all : (n_all + 1) >> 1;
+    const int kt_lo = first ? t_lo : t_lo + n0;
+    const int n = first ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
+    const int lbase = first ? 0 : n0;        // this group's first list entry
     // key tile of this group's idx-th visited tile
     auto tile_at = [&](int idx) {
         if constexpr (MODE == 3) {
@@ -342,16 +350,21 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     float l_run = 0.f;        // this lane's half of the row sum
 
     // ---- direct global -> LDS tile loads ------------------------------------------
-    // Load i of wave w fills the 1 KiB block b = 4*i + w of the tile (rows
-    // b*RPB .. b*RPB + RPB - 1, RPB = 64 / KCH rows per block); lane l writes 16 bytes at
-    // LDS slot b*64 + l, i.e. (row, physical chunk), fetching the logical chunk the
-    // swizzle maps there.  Blocks of one wave are 256 / KCH rows apart, which leaves the
-    // swizzle unchanged, so one per-lane offset serves every load of the thread and each
-    // load only moves the buffer base (scalar).
+    // The CW waves that share a tile's copies each make CL of them (head pairs: the
+    // workgroup's eight waves, half as many copies each).  Copy i of copying wave w fills
+    // the 1 KiB block b = CW*i + w of the tile (rows b*RPB .. b*RPB + RPB - 1, RPB = 64 / KCH
+    // rows per block); lane l writes 16 bytes at LDS slot b*64 + l, i.e. (row, physical
+    // chunk), fetching the logical chunk the swizzle maps there.  Blocks of one wave are
+    // CW * RPB rows apart, a multiple of 16, which leaves the swizzles unchanged, so one
+    // per-lane offset serves every copy of the thread and each copy only moves the buffer
+    // base (scalar).
     constexpr int RPB = 64 / T::KCH;
+    constexpr int CW = PAIR ? 8 : 4;
+    constexpr int CL = T::LOADS * 4 / CW;
+    const int cwave = PAIR ? grp * 4 + wave : wave;
     uint32_t kld_off, vld_off;
     {
-        const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
+        const int row = cwave * RPB + lane / T::KCH, phys = lane % T::KCH;
         kld_off = (uint32_t)(row * SK + T::k_phys(row, phys) * 8) * 2;
         vld_off = (uint32_t)(row * SK + T::v_phys(row, phys) * 8) * 2;
     }
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             return mfa_rsrc(src + (size_t)k0 * SK, (uint32_t)bytes);
         }
     };
-    const uint32_t copy_step = (uint32_t)(4 * RPB * SK * 2);
+    const uint32_t copy_step = (uint32_t)(CW * RPB * SK * 2);
     uint32_t kpg_off = 0, vpg_off = 0;
     if constexpr (PAGED) {
         const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
@@ -410,7 +423,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             mfa_load16_lds(page_rsrc(kg, r.kt, i, r.need ? kpid[i] : -1),
                            smem + buf * T::ELEMS + (4 * i + wave) * 512, kpg_off);
         else
-            mfa_load16_lds(r, smem + buf * T::ELEMS + (4 * i + wave) * 512, kld_off + i * copy_step);
+            mfa_load16_lds(r, smem + buf * T::ELEMS + (CW * i + cwave) * 512, kld_off + i * copy_step);
     };
     auto copy_v = [&](const auto& r, auto buf_c, int i) {
         constexpr int buf = decltype(buf_c)::value;
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             mfa_load16_lds(page_rsrc(vg, r.kt, i, r.need ? vpid[i] : -1),
                            smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vpg_off);
         else
-            mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vld_off + i * copy_step);
+            mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (CW * i + cwave) * 512, vld_off + i * copy_step);
     };
     auto issue_k = [&](int kt, auto buf_c) {
         if constexpr (PAGED) {
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         } else {
             const auto r = tile_rsrc(kg, kt, true);
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i) copy_k(r, buf_c, i);
+            for (int i = 0; i < CL; ++i) copy_k(r, buf_c, i);
         }
     };
     auto issue_v = [&](int kt, auto buf_c) {
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         } else {
             const auto r = tile_rsrc(vg, kt, true);
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i) copy_v(r, buf_c, i);
+            for (int i = 0; i < CL; ++i) copy_v(r, buf_c, i);
         }
     };
 
@@ -670,9 +683,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             }
 #pragma unroll
             for (int step = 0; step < NKB; ++step) {
-                // K copies: LOADS per stage, LOADS / 2 per phase, at evenly spaced steps
-                if ((step % (2 * NKB / T::LOADS)) == 1)
-                    copy_k(rk, MfaInt<P>{}, ph * (T::LOADS / 2) + step / (2 * NKB / T::LOADS));
+                // K copies: CL per stage, at evenly spaced steps of the two phases
+                constexpr int every = 2 * NKB / CL;
+                if ((ph * NKB + step) % every == 1) copy_k(rk, MfaInt<P>{}, (ph * NKB + step) / every);
                 if (step + 2 < NKB)
                     kop[(step + 2) % 3] = lds_read16(kbase + k_rd[step + 2] + nbm * 32 * D);
                 acc = mfa_mfma32<DT>(kop[step % 3], qreg[step], acc);
@@ -699,8 +712,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
 
         // O += V(j)^T P(j)^T
         pv_mfma(MfaInt<P>{}, pop, [&](int q) {
-            // V copies: LOADS per stage over the 2 * NNB PV steps
-            if (q % (2 * NNB / T::LOADS) == 0) copy_v(rv, MfaInt<P ^ 1>{}, q / (2 * NNB / T::LOADS));
+            // V copies: CL per stage over the 2 * NNB PV steps
+            if (q % (2 * NNB / CL) == 0) copy_v(rv, MfaInt<P ^ 1>{}, q / (2 * NNB / CL));
         });
 
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's direct loads landed
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // ---- merge the two groups' partial states (same rows, disjoint keys) ---------
     // Group 1 leaves (m, l, o) of each lane in LDS (struct-of-arrays, conflict-free);
     // group 0 combines them with its own: M = max(m0, m1), f_i = exp2(m_i - M).
-    if constexpr (GROUPS == 2) {
+    if constexpr (GROUPS == 2 && !PAIR) {
         constexpr int NC = NDB * 16 + 2;   // o values, m, l per lane
         float* xch = reinterpret_cast<float*>(smem_all);
         __shared__ int edge_cnt;
@@ -789,8 +802,20 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // ---- epilogue: O = o / l, LSE = (m + log2 l) * ln 2 --------------------------
     const float l_tot = l_run + mfa_swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qvalid) {
-        uint16_t* op = a.o + q_base + (size_t)qrow * SQ + 4 * g32;
+    // O leaves through LDS: the wave writes its 32 x D block row-major (16-byte chunks
+    // XOR-swizzled by row) into free tile memory and reads it back so that each store
+    // instruction covers 64 / KCH whole rows.  The tile buffers are free here: the last
+    // stage ended with every copy landed and every read done.  After the two groups'
+    // merge, group 0 uses group 1's V buffers, which the exchange does not reach; the two
+    // groups of a head pair use K buffers 0, 1 and V buffers 0, 1 respectively.
+    {
+        uint16_t* stg = (PAIR ? smem_all + grp * 2 * T::ELEMS : GROUPS == 2 ? smem_all + 6 * T::ELEMS : smem) +
+                        wave * 32 * D;
+        // (the lane index is made opaque here so that the staging addresses are formed
+        // now rather than hoisted out of the tile loop, where they would hold registers)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lr = ln & 31, lh = ln >> 5;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -798,15 +823,25 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
                 mfa_u32x2 w2;
                 w2[0] = mfa_pack2<DT>(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
                 w2[1] = mfa_pack2<DT>(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-                *(mfa_u32x2*)(op + db * 32 + 8 * j) = w2;
+                const int c = db * 4 + j;   // 16-byte chunk of the row: columns 8c .. 8c + 7
+                *(mfa_u32x2*)(stg + lr * D + (c ^ (lr & (T::KCH - 1))) * 8 + 4 * lh) = w2;
             }
         }
-        if (a.lse != nullptr && g32 == 0) {
-            const size_t li = VAR ? (size_t)h * a.total_q + qs + qrow : (size_t)(b * a.Hq + h) * a.Nq + qrow;
-            a.lse[li] = l_tot > 0.f ? (m_run + mfa_log2(l_tot)) * MFA_LN2 : -MFA_INF;
+        constexpr int RPS = 64 / T::KCH;   // rows per store instruction
+        const int rr = ln / T::KCH, ch = ln % T::KCH;
+#pragma unroll
+        for (int k = 0; k < 32 / RPS; ++k) {
+            const int row = k * RPS + rr;
+            const mfa_u32x4 val = *(const mfa_u32x4*)(stg + row * D + (ch ^ (row & (T::KCH - 1))) * 8);
+            const int srow = q0 + wave * 32 + row;
+            if (srow < Nq) *(mfa_u32x4*)(a.o + q_base + (size_t)srow * SQ + ch * 8) = val;
         }
     }
-    if (TILELOG && tid == 0) {
+    if (qvalid && a.lse != nullptr && g32 == 0) {
+        const size_t li = VAR ? (size_t)h * a.total_q + qs + qrow : (size_t)(b * a.Hq + h) * a.Nq + qrow;
+        a.lse[li] = l_tot > 0.f ? (m_run + mfa_log2(l_tot)) * MFA_LN2 : -MFA_INF;
+    }
+    if (TILELOG && (PAIR ? (tid & 255) : tid) == 0) {
         int32_t* t = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + qt) * 4;
         int first = t_lo, last = t_hi;
         if (use_list && n_all > 0) {
@@ -822,20 +857,25 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }   // rep
 }
 
-template <int D, int DT, int G, bool TL, int MODE>
+template <int D, int DT, int G, bool TL, int MODE, bool PAIR = false>
 void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
     const dim3 block(G * kGroupThreads);
     if (neg)
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true, MODE>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, true, MODE, PAIR>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false, MODE>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((mfa_fwd_kernel<D, DT, G, TL, false, MODE, PAIR>), grid, block, 0, stream, a);
 }
 
 template <int D, int DT, int MODE>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
     const dim3 grid((unsigned)(a.chain ? a.n_rounds / 2 : a.n_rounds) * (unsigned)a.HB);
-    if (groups == 2) {
+    if (a.pair) {
+        if constexpr (MODE == 0) {
+            if (tilelog) launch_sign<D, DT, 2, true, MODE, true>(a, grid, stream, neg);
+            else launch_sign<D, DT, 2, false, MODE, true>(a, grid, stream, neg);
+        }
+    } else if (groups == 2) {
         if (tilelog) launch_sign<D, DT, 2, true, MODE>(a, grid, stream, neg);
         else launch_sign<D, DT, 2, false, MODE>(a, grid, stream, neg);
     } else {
@@ -845,7 +885,7 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
     snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
              MODE == 3 ? ",ext" : MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
-             tilelog ? ",tilelog" : "", neg ? ",neg" : "", a.chain ? ",chained" : "");
+             tilelog ? ",tilelog" : "", neg ? ",neg" : "", a.chain ? ",chained" : a.pair ? ",head-pairs" : "");
     info->BM = kBM;
     info->BN = kBN;
     info->waves = groups * kGroupThreads / 64;
@@ -939,8 +979,16 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     // sequences at most total_q / BM + B of the grid's B * ceil(max_seqlen_q / BM)
     long long q_tiles = (long long)a.n_q_tiles * pr.B;
     if (var && (long long)pr.total_q / kBM + pr.B < q_tiles) q_tiles = (long long)pr.total_q / kBM + pr.B;
-    const int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
+    int groups = mfa_fwd_groups(q_tiles, pr.Hq, mfa_num_cus());
     a.chain = (mode == 0 && groups == 2 && a.n_q_tiles % 2 == 0) ? 1 : 0;
+    // Dense GQA with many tiles: one 8-wave workgroup per pair of query heads that share a
+    // KV head instead of two 4-wave workgroups, so that each K/V tile is copied to LDS once
+    // for both heads (half the copies per FLOP).
+    a.pair = (mode == 0 && groups == 1 && a.g % 2 == 0) ? 1 : 0;
+    if (a.pair) {
+        groups = 2;
+        a.HB = pr.B * pr.Hq / 2;
+    }
     if (mode == 3) return launch_dt<3>(pr, a, stream, groups, tl, neg, info);
     if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
     if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);

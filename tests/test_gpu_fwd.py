@@ -233,3 +233,51 @@ def test_prepared_call_holds_its_tensors():
     assert_close_o(to_f64(out, "f16"), Or, "f16", "prepared O")
     assert_close_lse(lse.cpu().numpy(), Lr, "prepared LSE")
     del junk
+
+
+# Dense GQA on a large grid (more than two query tiles per CU) runs one 8-wave workgroup
+# per pair of query heads that share a KV head (both groups walk the same key tiles from one K/V stream in LDS); an odd group
+# size keeps the 4-wave layout.  Hq, Hkv, Nq, Nk, D, dtype, causal, left, right, scale, pairs
+PAIR_CASES = [
+    (128, 64, 520, 520, 128, "f16", True, -1, -1, None, True),      # g = 2, ragged last tile
+    (96, 16, 700, 800, 64, "bf16", False, 40, 17, None, True),      # g = 6, window, Nk > Nq
+    (128, 32, 600, 600, 128, "f16", True, -1, -1, -0.1, True),      # g = 4, negative scale
+    (64, 16, 1100, 1100, 128, "bf16", True, 300, 0, None, True),    # g = 4, causal window
+    (192, 64, 300, 300, 128, "bf16", True, -1, -1, None, False),    # g = 3: 4-wave groups
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[str(i) for i in range(len(PAIR_CASES))])
+def test_head_pairs(case):
+    import torch
+    Hq, Hkv, Nq, Nk, D, dtype, causal, left, right, scale, pairs = case
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    x = A.dense_inputs(1, Hq, Hkv, Nq, Nk, D, dtype, 900 + Hq + Nq)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = run(q, k, v, scale, causal, left, right)
+    kern = ea.mfa_last_dispatch()["kernel"]
+    assert (",head-pairs" in kern) == pairs and ("groups=2" in kern) == pairs, kern
+    # both heads of the first and the last pair, and one pair in the middle
+    g = Hq // Hkv
+    heads = sorted({0, 1, Hq // 2, Hq // 2 + 1, Hq - 2, Hq - 1})
+    for h in heads:
+        kv = h // g
+        qf = oracle.widen(x.q[:, h:h + 1], dtype)
+        kf, vf = (oracle.widen(t[:, kv:kv + 1], dtype) for t in (x.k, x.v))
+        Or, Lr = oracle.attention(qf, kf, vf, scale, causal, left, right)
+        assert_close_o(to_f64(O[:, h:h + 1], dtype), Or, dtype, f"O h={h}")
+        assert_close_lse(L[:, h:h + 1].cpu().numpy(), Lr, f"LSE h={h}")
+    # the per-tile visit record: each group writes its own head's records
+    plan, ranges = ea.mfa_plan_fwd(Nq, Nk, D, ea.MFA_F16 if dtype == "f16" else ea.MFA_BF16,
+                                   causal, left, right)
+    log = torch.full((Hq * plan["n_q_tiles"] * 4,), -7, dtype=torch.int32, device="cuda")
+    ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right, tile_log=log)
+    torch.cuda.synchronize()
+    assert (",head-pairs" in ea.mfa_last_dispatch()["kernel"]) == pairs
+    log = log.view(Hq, plan["n_q_tiles"], 4).cpu().numpy()
+    ref = oracle.visited_tiles(Nq, Nk, plan["BM"], plan["BN"], causal, left, right)
+    for t in range(plan["n_q_tiles"]):
+        want = (ref[t][0], len(ref[t]), ref[t][-1] + 1) if ref[t] else (-1, 0, -1)
+        assert np.all(log[:, t, 0] == want[0]) and np.all(log[:, t, 1] == want[1]), (t, log[:, t])
+        assert np.all(log[:, t, 3] == want[2]), (t, log[:, t])
+    assert int(log[..., 2].sum()) == Hq * plan["edge"]

@@ -60,6 +60,8 @@ DENSE = [
     (1, 240, 240, 259, 259, 128, "bf16", True, -1, -1),  # many heads: one wave group
     (1, 4, 4, 512, 512, 128, "f16", True, -1, -1),      # chained complementary tiles
     (1, 2, 1, 1, 777, 128, "f16", True, -1, -1),        # one query row
+    (1, 128, 32, 520, 520, 64, "bf16", True, -1, -1),   # head pairs, D = 64, partial tile
+    (1, 128, 64, 650, 600, 128, "f16", True, -1, -1),   # head pairs, Nk < Nq
 ]
 
 

@@ -244,8 +244,8 @@ def test_random_ext(i):
 
 @pytest.mark.parametrize("i", range(8))
 def test_random_forward_many_heads(i):
-    # grids of more than two query tiles per CU take the one-group layout (two 4-wave
-    # workgroups per CU); sampled rows against the oracle
+    # grids of more than two query tiles per CU with an even group size take one 8-wave
+    # workgroup per pair of query heads sharing a KV head; sampled rows against the oracle
     rng = np.random.default_rng(8500 + i)
     D, dtype, _, _ = draw_common(rng)
     Hkv = int(rng.choice([32, 64]))
@@ -259,7 +259,8 @@ def test_random_forward_many_heads(i):
     q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
     O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right)
     sync()
-    assert "groups=1" in ea.mfa_last_dispatch()["kernel"]
+    # (an even group size: one 8-wave workgroup per pair of query heads)
+    assert "groups=2" in ea.mfa_last_dispatch()["kernel"] and ",head-pairs" in ea.mfa_last_dispatch()["kernel"]
     rows = sorted({(0, int(h), int(r)) for h, r in zip(rng.integers(0, Hq, 200), rng.integers(0, Nq, 200))}
                   | {(0, 0, 0), (0, Hq - 1, Nq - 1)})
     qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
