@@ -219,7 +219,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         qt = a.n_rounds - 1 - round - c;
         // the records of tiles past this sequence's last one are written by the workgroup
         // of its last tile (by round 0's if it has none)
-        if (TILELOG && tid == 0 && (n_tiles > 0 ? qt == n_tiles - 1 : round == 0)) {
+        if (TILELOG && (PAIR ? (tid & 255) : tid) == 0 && (n_tiles > 0 ? qt == n_tiles - 1 : round == 0)) {
             for (int t = n_tiles; t < a.n_q_tiles; ++t) {
                 int32_t* r = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + t) * 4;
                 r[0] = -1;
@@ -374,8 +374,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // own (the range check applies to it).  Packed rows are SK apart, so there the range
     // ends with the last row's D elements.
     //
-    // Paged keys: a key tile is BN / 16 pages, and the rows of copy i of this wave all lie in
-    // page ((4 * i + wave) * RPB) / 16 of the tile, at row (row & 15) of that page; the copy
+    // Paged keys: a key tile is BN / 16 pages, and the rows of copy i of copying wave w all lie
+    // in page ((CW * i + w) * RPB) / 16 of the tile, at row (row & 15) of that page; the copy
     // gets a range over the page's valid rows of this head (empty for an unused or invalid
     // page).  The page ids of the tiles a stage copies are read one stage ahead.
     constexpr int PAGE = 16;
@@ -396,15 +396,15 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const uint32_t copy_step = (uint32_t)(CW * RPB * SK * 2);
     uint32_t kpg_off = 0, vpg_off = 0;
     if constexpr (PAGED) {
-        const int row = wave * RPB + lane / T::KCH, phys = lane % T::KCH;
+        const int row = cwave * RPB + lane / T::KCH, phys = lane % T::KCH;
         kpg_off = (uint32_t)((row & (PAGE - 1)) * SK + T::k_phys(row, phys) * 8) * 2;
         vpg_off = (uint32_t)((row & (PAGE - 1)) * SK + T::v_phys(row, phys) * 8) * 2;
     }
     const int32_t* bt_row = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
-    auto page_slot = [&](int kt, int i) { return kt * (BN / PAGE) + ((4 * i + wave) * RPB) / PAGE; };
+    auto page_slot = [&](int kt, int i) { return kt * (BN / PAGE) + ((CW * i + cwave) * RPB) / PAGE; };
     auto load_ids = [&](int kt, bool need, int(&ids)[T::LOADS]) {
 #pragma unroll
-        for (int i = 0; i < T::LOADS; ++i) {
+        for (int i = 0; i < CL; ++i) {
             const int slot = page_slot(kt, i);
             ids[i] = (need && slot * PAGE < Nk) ? mfa_uniform_load(bt_row + slot) : -1;
         }
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         constexpr int buf = decltype(buf_c)::value;
         if constexpr (PAGED)
             mfa_load16_lds(page_rsrc(kg, r.kt, i, r.need ? kpid[i] : -1),
-                           smem + buf * T::ELEMS + (4 * i + wave) * 512, kpg_off);
+                           smem + buf * T::ELEMS + (CW * i + cwave) * 512, kpg_off);
         else
             mfa_load16_lds(r, smem + buf * T::ELEMS + (CW * i + cwave) * 512, kld_off + i * copy_step);
     };
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         constexpr int buf = decltype(buf_c)::value;
         if constexpr (PAGED)
             mfa_load16_lds(page_rsrc(vg, r.kt, i, r.need ? vpid[i] : -1),
-                           smem + (2 + buf) * T::ELEMS + (4 * i + wave) * 512, vpg_off);
+                           smem + (2 + buf) * T::ELEMS + (CW * i + cwave) * 512, vpg_off);
         else
             mfa_load16_lds(r, smem + (2 + buf) * T::ELEMS + (CW * i + cwave) * 512, vld_off + i * copy_step);
     };
@@ -438,8 +438,8 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             int ids[T::LOADS];
             load_ids(kt, true, ids);
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i)
-                mfa_load16_lds(page_rsrc(kg, kt, i, ids[i]), smem + decltype(buf_c)::value * T::ELEMS + (4 * i + wave) * 512,
+            for (int i = 0; i < CL; ++i)
+                mfa_load16_lds(page_rsrc(kg, kt, i, ids[i]), smem + decltype(buf_c)::value * T::ELEMS + (CW * i + cwave) * 512,
                                kpg_off);
         } else {
             const auto r = tile_rsrc(kg, kt, true);
@@ -452,9 +452,9 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             int ids[T::LOADS];
             load_ids(kt, true, ids);
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i)
+            for (int i = 0; i < CL; ++i)
                 mfa_load16_lds(page_rsrc(vg, kt, i, ids[i]),
-                               smem + (2 + decltype(buf_c)::value) * T::ELEMS + (4 * i + wave) * 512, vpg_off);
+                               smem + (2 + decltype(buf_c)::value) * T::ELEMS + (CW * i + cwave) * 512, vpg_off);
         } else {
             const auto r = tile_rsrc(vg, kt, true);
 #pragma unroll
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         block_barrier();
         if constexpr (PAGED) {
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i) {
+            for (int i = 0; i < CL; ++i) {
                 kpid[i] = kpid_n[i];
                 vpid[i] = vpid_n[i];
             }
@@ -983,7 +983,8 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
     a.chain = (mode == 0 && groups == 2 && a.n_q_tiles % 2 == 0) ? 1 : 0;
     // Dense GQA with many tiles: one 8-wave workgroup per pair of query heads that share a
     // KV head instead of two 4-wave workgroups, so that each K/V tile is copied to LDS once
-    // for both heads (half the copies per FLOP).
+    // for both heads (half the copies per FLOP).  Packed sequences keep two 4-wave
+    // workgroups per CU: there the pairs measured 11-19% slower.
     a.pair = (mode == 0 && groups == 1 && a.g % 2 == 0) ? 1 : 0;
     if (a.pair) {
         groups = 2;

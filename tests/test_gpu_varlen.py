@@ -97,16 +97,18 @@ def test_keyless_rows_and_padding_untouched():
 
 
 def test_both_workgroup_layouts():
-    # few query tiles: two key-splitting wave groups per workgroup; many: one group
-    for Hq, groups in ((2, 2), (64, 1)):
-        x = A.varlen_inputs(Hq, 2, 128, "bf16", 40 + Hq, seqlens_q=[900, 1, 640, 459])
+    # few query tiles: two key-splitting wave groups per workgroup; many: one group (packed
+    # sequences take no head pairs, whatever the group size)
+    for Hq, Hkv, layout in ((2, 2, "groups=2"), (64, 2, "groups=1"), (72, 24, "groups=1")):
+        x = A.varlen_inputs(Hq, Hkv, 128, "bf16", 40 + Hq, seqlens_q=[900, 1, 640, 459])
         O, L = run(x, 0.09, True)
         info = ea.mfa_last_dispatch()
-        assert f"groups={groups}" in info["kernel"], info["kernel"]
-        for h in (0, Hq - 1):
-            sub = A.VarlenInputs(x.q[:, h:h + 1], x.k[:, h * 2 // Hq:h * 2 // Hq + 1],
-                                 x.v[:, h * 2 // Hq:h * 2 // Hq + 1], x.cu_seqlens_q,
-                                 x.cu_seqlens_k, "bf16")
+        assert layout in info["kernel"], info["kernel"]
+        g = Hq // Hkv
+        for h in sorted({0, 1, Hq - 2, Hq - 1}):
+            kv = h // g
+            sub = A.VarlenInputs(x.q[:, h:h + 1], x.k[:, kv:kv + 1], x.v[:, kv:kv + 1],
+                                 x.cu_seqlens_q, x.cu_seqlens_k, "bf16")
             Or, Lr = oracle_of(sub, 0.09, True)
             assert_close_o(to_f64(O[:, h:h + 1], "bf16"), Or, "bf16", f"Hq={Hq} h={h}")
             assert_close_lse(L[h:h + 1].cpu().numpy(), Lr, f"Hq={Hq} h={h}")

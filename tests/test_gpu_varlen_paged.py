@@ -62,6 +62,9 @@ CASES = [
     (4, 4, 128, "f16", [200, 333], [500, 64], True, 100, 0),                    # window
     (2, 2, 64, "bf16", [90, 257], [10, 300], False, -1, -1),                    # non-causal
     (6, 2, 128, "bf16", [640], [0], True, -1, -1),                              # no context
+    # many tiles: one 4-wave group per workgroup
+    (64, 16, 128, "bf16", [300, 5, 700, 129], [700, 90, 0, 1500], True, -1, -1),
+    (96, 48, 64, "f16", [129, 250, 7, 400], [3, 640, 33, 900], True, 200, 0),
 ]
 
 
@@ -79,12 +82,15 @@ def test_paged_packs_match_oracle(case):
     print(f"paged {case}: max|dO|={eo:.2e} max|dLSE|={el:.2e} {info['kernel']}")
 
 
-def test_paged_equals_contiguous_packed_bitwise():
+@pytest.mark.parametrize("Hq,Hkv,layout", [(8, 2, "groups=2"), (96, 8, "groups=1")])
+def test_paged_equals_contiguous_packed_bitwise(Hq, Hkv, layout):
     # the same tokens through pages or packed back to back: same tiles, same order, same
-    # values (zeros past each sequence's end), hence bit-identical results
+    # values (zeros past each sequence's end), hence bit-identical results (in both the
+    # key-splitting and the one-group layout)
     import torch
-    p = A.paged_varlen_inputs(8, 2, 128, "bf16", 17, seqlens_q=[300, 5, 129], ctx_lens=[700, 90, 0])
+    p = A.paged_varlen_inputs(Hq, Hkv, 128, "bf16", 17, seqlens_q=[300, 5, 129], ctx_lens=[700, 90, 0])
     O, L = run(p, 0.09)
+    assert layout in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
     k, v = contiguous_tokens(p)
     lk = p.seq_lens_k
     cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
@@ -92,6 +98,7 @@ def test_paged_equals_contiguous_packed_bitwise():
                                dev_i32(p.cu_seqlens_q), dev_i32(cu_k), 300, int(lk.max()),
                                scale=0.09, causal=True)
     torch.cuda.synchronize()
+    assert layout in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
     assert np.array_equal(to_bits(O), to_bits(Oc))
     assert torch.equal(L, Lc)
 
