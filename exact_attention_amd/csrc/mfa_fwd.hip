@@ -761,6 +761,28 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         }
     }
 
+    // Global stores of a wave's 32 x D output block staged row-major in LDS (16-byte chunks
+    // XOR-swizzled by row): each store instruction covers 64 / KCH whole rows.  (The lane
+    // index is made opaque so that the addresses are formed here rather than hoisted out of
+    // the tile loop, where they would hold registers.)
+    auto store_block = [&](const uint16_t* stg) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        constexpr int RPS = 64 / T::KCH;   // rows per store instruction
+        const int rr = ln / T::KCH, ch = ln % T::KCH;
+#pragma unroll
+        for (int k = 0; k < 32 / RPS; ++k) {
+            const int row = k * RPS + rr;
+            const mfa_u32x4 val = *(const mfa_u32x4*)(stg + row * D + (ch ^ (row & (T::KCH - 1))) * 8);
+            const int srow = q0 + wave * 32 + row;
+            if (srow < Nq) *(mfa_u32x4*)(a.o + q_base + (size_t)srow * SQ + ch * 8) = val;
+        }
+    };
+    // With two key-splitting groups, group 0 merges and stages its block in group 1's V
+    // buffers (which the exchange below does not reach), and group 1, idle by then, stores it.
+    constexpr bool SPLIT_STORE = GROUPS == 2 && !PAIR;
+    uint16_t* const stg_all = PAIR ? smem_all + grp * 2 * T::ELEMS : GROUPS == 2 ? smem_all + 6 * T::ELEMS : smem;
+
     // ---- merge the two groups' partial states (same rows, disjoint keys) ---------
     // Group 1 leaves (m, l, o) of each lane in LDS (struct-of-arrays, conflict-free);
     // group 0 combines them with its own: M = max(m0, m1), f_i = exp2(m_i - M).
@@ -781,8 +803,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         static_assert(NC * 256 * 4 <= GROUPS * 4 * T::ELEMS * 2, "exchange fits in the tile buffers");
         __syncthreads();
         if (grp == 1) {
+            __syncthreads();   // group 0 has staged its block
+            store_block(stg_all + wave * 32 * D);
             if (n_rep == 1) return;
-            __syncthreads();   // group 0 has read the exchange before the next tile's copies
+            __syncthreads();   // the block is read before the next tile's copies
             continue;
         }
         const float m1 = xch[0 * 256 + slot];
@@ -803,16 +827,11 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const float l_tot = l_run + mfa_swap_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // O leaves through LDS: the wave writes its 32 x D block row-major (16-byte chunks
-    // XOR-swizzled by row) into free tile memory and reads it back so that each store
-    // instruction covers 64 / KCH whole rows.  The tile buffers are free here: the last
-    // stage ended with every copy landed and every read done.  After the two groups'
-    // merge, group 0 uses group 1's V buffers, which the exchange does not reach; the two
-    // groups of a head pair use K buffers 0, 1 and V buffers 0, 1 respectively.
+    // XOR-swizzled by row) into free tile memory, from where whole rows are stored.  The
+    // tile buffers are free here: the last stage ended with every copy landed and every
+    // read done.  The two groups of a head pair use K buffers 0, 1 and V buffers 0, 1.
     {
-        uint16_t* stg = (PAIR ? smem_all + grp * 2 * T::ELEMS : GROUPS == 2 ? smem_all + 6 * T::ELEMS : smem) +
-                        wave * 32 * D;
-        // (the lane index is made opaque here so that the staging addresses are formed
-        // now rather than hoisted out of the tile loop, where they would hold registers)
+        uint16_t* stg = stg_all + wave * 32 * D;
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lr = ln & 31, lh = ln >> 5;
@@ -827,15 +846,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
                 *(mfa_u32x2*)(stg + lr * D + (c ^ (lr & (T::KCH - 1))) * 8 + 4 * lh) = w2;
             }
         }
-        constexpr int RPS = 64 / T::KCH;   // rows per store instruction
-        const int rr = ln / T::KCH, ch = ln % T::KCH;
-#pragma unroll
-        for (int k = 0; k < 32 / RPS; ++k) {
-            const int row = k * RPS + rr;
-            const mfa_u32x4 val = *(const mfa_u32x4*)(stg + row * D + (ch ^ (row & (T::KCH - 1))) * 8);
-            const int srow = q0 + wave * 32 + row;
-            if (srow < Nq) *(mfa_u32x4*)(a.o + q_base + (size_t)srow * SQ + ch * 8) = val;
-        }
+        if (!SPLIT_STORE) store_block(stg);
     }
     if (qvalid && a.lse != nullptr && g32 == 0) {
         const size_t li = VAR ? (size_t)h * a.total_q + qs + qrow : (size_t)(b * a.Hq + h) * a.Nq + qrow;
@@ -853,6 +864,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         t[2] = n_edge;
         t[3] = n_all ? last : -1;
     }
+    if (SPLIT_STORE) __syncthreads();   // the block is staged: group 1 stores it
     if (n_rep > 1) __syncthreads();
     }   // rep
 }
