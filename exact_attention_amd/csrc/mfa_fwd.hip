@@ -83,6 +83,8 @@ struct FwdArgs {
     int HB;          // B * Hq
     int xcd_group;   // 1: group the query heads of one KV head on one XCD
     int chain;       // 1: each workgroup runs query tile n_q_tiles - 1 - r, then tile r
+    int seqmajor;    // 1: packed sequences in sequence-major order per XCD (seq_major_item)
+    int grid;        // workgroups of the launch
     int pair;        // 1: the two wave groups take two query heads of one KV head
     float scale_log2_abs;  // |scale| * log2(e)
     MfaMask mask;    // dense layout only (packed sequences build theirs per sequence)
@@ -129,6 +131,63 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int total, 
     s1 = s1 < s0 ? s0 : (s1 > total ? total : s1);
     *start = s0;
     *len = (s1 - s0) > max_len ? max_len : (s1 - s0);
+}
+
+// Sequence-major order of packed sequences (B <= 64, Hkv a multiple of 8).  The
+// workgroups of XCD x = id % 8 (dispatch goes round-robin over the 8 XCDs) take the KV
+// heads x, x + 8, ...; they run sequence after sequence, longest key range first, and
+// within a sequence all query tiles of one KV head back to back (longest tile first, its
+// g query heads side by side).  The workgroups that stream one sequence's K/V through the
+// XCD's L2 then start together and read the same tiles at about the same time.  Lane i of
+// every wave holds sequence i; k = id / 8 indexes the XCD's items.  Returns false past the
+// XCD's last item.  (Uniform over the workgroup.)
+template <bool PAGED>
+__device__ __forceinline__ bool seq_major_item(const FwdArgs& a, int lane, int* b, int* h, int* qt,
+                                               int* n_seq_tiles) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    int ni = 0, key = -1;
+    if (lane < a.B) {
+        int s0 = a.cu_q[lane], s1 = a.cu_q[lane + 1];
+        s0 = s0 < 0 ? 0 : (s0 > a.total_q ? a.total_q : s0);
+        s1 = s1 < s0 ? s0 : (s1 > a.total_q ? a.total_q : s1);
+        const int len = (s1 - s0) > a.Nq ? a.Nq : (s1 - s0);
+        ni = (len + kBM - 1) / kBM;
+        if constexpr (PAGED) {
+            const int L = a.seq_lens_k[lane];
+            key = L < 0 ? 0 : (L > a.Nk ? a.Nk : L);
+        } else {
+            int k0 = a.cu_k[lane], k1 = a.cu_k[lane + 1];
+            k0 = k0 < 0 ? 0 : (k0 > a.total_k ? a.total_k : k0);
+            k1 = k1 < k0 ? k0 : (k1 > a.total_k ? a.total_k : k1);
+            key = (k1 - k0) > a.Nk ? a.Nk : (k1 - k0);
+        }
+    }
+    // rank of this lane's sequence: longer key ranges first, ties by index
+    int rank = 0;
+    for (int j = 0; j < a.B; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+    }
+    // items of this XCD before the sequence: (KV heads of the XCD) x g x tiles
+    const int cnt = (a.Hkv >> 3) * a.g * ni;
+    int excl = 0;
+    for (int j = 0; j < a.B; ++j) {
+        const int rj = __builtin_amdgcn_readlane(rank, j);
+        const int cj = __builtin_amdgcn_readlane(cnt, j);
+        excl += rj < rank ? cj : 0;
+    }
+    *n_seq_tiles = ni;   // (per lane: this lane's sequence)
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.B && k >= excl && k < excl + cnt);
+    if (hit == 0) return false;
+    const int sb = (int)__builtin_ctzll(hit);
+    const int local = k - __builtin_amdgcn_readlane(excl, sb);
+    const int nb = __builtin_amdgcn_readlane(ni, sb);
+    const int per_kv = a.g * nb;
+    const int mi = local / per_kv, rest = local - mi * per_kv;
+    *b = sb;
+    *qt = nb - 1 - rest / a.g;
+    *h = (x + 8 * mi) * a.g + rest % a.g;
+    return true;
 }
 
 // MODE 0: dense [B, H, N, D] tensors.
@@ -180,7 +239,26 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     // orders the tiles of all sequences by causal work, whatever their lengths.
     int qt = rep == 0 ? a.n_q_tiles - 1 - round : round;
     int b, h;
-    if (a.xcd_group) {
+    const bool sm = VAR && a.seqmajor;
+    if (sm) {
+        int ni = 0;
+        const bool have = seq_major_item<PAGED>(a, lane, &b, &h, &qt, &ni);
+        // the records of sequences with no query tile are written by the XCD's first
+        // workgroup, for the query heads of the XCD's KV heads (lane i: sequence i)
+        if (TILELOG && tid < 64 && (blockIdx.x >> 3) == 0 && lane < a.B && ni == 0) {
+            for (int hh = 0; hh < a.Hq; ++hh) {
+                if (((hh / a.g) & 7) != (int)(blockIdx.x & 7)) continue;
+                for (int t = 0; t < a.n_q_tiles; ++t) {
+                    int32_t* r = a.tile_log + ((size_t)(lane * a.Hq + hh) * a.n_q_tiles + t) * 4;
+                    r[0] = -1;
+                    r[1] = 0;
+                    r[2] = 0;
+                    r[3] = -1;
+                }
+            }
+        }
+        if (!have) return;   // past the XCD's last item (uniform)
+    } else if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
         // of one (batch, KV head) on the same XCD so its K/V stay in that L2
         const int x = w & 7, j = w >> 3;
@@ -216,10 +294,10 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         // n_rounds >= ceil(Nq / BM) + c for every sequence, so each tile has one round
         const int n_tiles = (Nq + kBM - 1) / kBM;
         const int c = Nk > Nq ? (Nk - Nq) / kBM : 0;
-        qt = a.n_rounds - 1 - round - c;
+        if (!sm) qt = a.n_rounds - 1 - round - c;
         // the records of tiles past this sequence's last one are written by the workgroup
-        // of its last tile (by round 0's if it has none)
-        if (TILELOG && (PAIR ? (tid & 255) : tid) == 0 && (n_tiles > 0 ? qt == n_tiles - 1 : round == 0)) {
+        // of its last tile (in round order: by round 0's if it has none)
+        if (TILELOG && (PAIR ? (tid & 255) : tid) == 0 && (n_tiles > 0 ? qt == n_tiles - 1 : !sm && round == 0)) {
             for (int t = n_tiles; t < a.n_q_tiles; ++t) {
                 int32_t* r = a.tile_log + ((size_t)(b * a.Hq + h) * a.n_q_tiles + t) * 4;
                 r[0] = -1;
@@ -881,7 +959,7 @@ void launch_sign(const FwdArgs& a, dim3 grid, hipStream_t stream, bool neg) {
 template <int D, int DT, int MODE>
 int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool neg,
            mfa_dispatch_info* info) {
-    const dim3 grid((unsigned)(a.chain ? a.n_rounds / 2 : a.n_rounds) * (unsigned)a.HB);
+    const dim3 grid((unsigned)a.grid);
     if (a.pair) {
         if constexpr (MODE == 0) {
             if (tilelog) launch_sign<D, DT, 2, true, MODE, true>(a, grid, stream, neg);
@@ -897,7 +975,8 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
     snprintf(info->kernel, sizeof(info->kernel), "mfa_fwd_kernel<D=%d,%s,BM=%d,BN=%d,groups=%d%s%s%s%s>", D,
              DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
              MODE == 3 ? ",ext" : MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
-             tilelog ? ",tilelog" : "", neg ? ",neg" : "", a.chain ? ",chained" : a.pair ? ",head-pairs" : "");
+             tilelog ? ",tilelog" : "", neg ? ",neg" : "",
+             a.chain ? ",chained" : a.pair ? ",head-pairs" : a.seqmajor ? ",seq-major" : "");
     info->BM = kBM;
     info->BN = kBN;
     info->waves = groups * kGroupThreads / 64;
@@ -1002,6 +1081,14 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
         groups = 2;
         a.HB = pr.B * pr.Hq / 2;
     }
+    // packed sequences: sequence-major order per XCD when each XCD can own whole KV heads;
+    // the grid covers at most floor(total_q / BM) + B query tiles per (head) and the
+    // workgroups past an XCD's last item exit at once
+    a.seqmajor = (var && mode != 3 && pr.B <= 64 && pr.Hkv % 8 == 0) ? 1 : 0;
+    if (a.seqmajor)
+        a.grid = 8 * (pr.Hkv / 8) * a.g * (pr.total_q / kBM + pr.B);
+    else
+        a.grid = (a.chain ? a.n_rounds / 2 : a.n_rounds) * a.HB;
     if (mode == 3) return launch_dt<3>(pr, a, stream, groups, tl, neg, info);
     if (mode == 2) return launch_dt<2>(pr, a, stream, groups, tl, neg, info);
     if (mode == 1) return launch_dt<1>(pr, a, stream, groups, tl, neg, info);
