@@ -203,3 +203,58 @@ def test_full_size_packed_workload_sampled():
     eo = assert_close_o(Og, Or, c["dtype"], "packed workload")
     el = assert_close_lse(Lg, Lr, "packed workload")
     print(f"packed workload: max|dO|={eo:.2e} max|dLSE|={el:.2e} kernel={ea.mfa_last_dispatch()['kernel']}")
+
+
+# Sequence-major order (at most 64 sequences, Hkv a multiple of 8): each XCD takes whole KV
+# heads and runs the sequences longest first, a sequence's tiles of one KV head back to
+# back; every (sequence, head, tile) must still be computed exactly once, and the tile
+# records of empty sequences are written by each XCD's first workgroup.
+# Hq, Hkv, lq, lk, causal, left, right, dtype
+SEQ_MAJOR = [
+    (16, 8, [700, 1, 300, 129, 0, 1000], [700, 900, 1000, 5, 3, 1200], True, -1, -1, "bf16"),
+    (32, 16, [257, 513, 0, 40], [257, 600, 7, 40], True, 100, 0, "f16"),
+    (8, 8, [200] * 64, [300] * 64, False, -1, -1, "bf16"),    # 64 sequences: the limit
+    (24, 8, [0, 0, 129], [10, 0, 129], True, -1, -1, "f16"),   # mostly empty, g = 3
+]
+
+
+@pytest.mark.parametrize("case", SEQ_MAJOR, ids=[str(i) for i in range(len(SEQ_MAJOR))])
+def test_sequence_major_order(case):
+    import torch
+    Hq, Hkv, lq, lk, causal, left, right, dt = case
+    x = A.varlen_inputs(Hq, Hkv, 128, dt, 60 + Hq + len(lq), seqlens_q=lq, seqlens_k=lk)
+    O, L = run(x, 0.09, causal, left, right)
+    assert ",seq-major" in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
+    Or, Lr = oracle_of(x, 0.09, causal, left, right)
+    T = in_seq_tokens(x)
+    assert_close_o(to_f64(O, dt)[:T], Or[:T], dt, "seq-major O")
+    assert_close_lse(L.cpu().numpy()[:, :T], Lr[:, :T], "seq-major LSE")
+    # per-tile visit records of every (sequence, head)
+    plan, _ = ea.mfa_plan_fwd(max(max(lq), 1), max(max(lk), 1), 128,
+                              ea.MFA_F16 if dt == "f16" else ea.MFA_BF16, causal, left, right, False)
+    BM, BN = plan["BM"], plan["BN"]
+    nqt = max(1, math.ceil(max(lq) / BM))
+    log = torch.full((len(lq) * Hq * nqt * 4,), -7, dtype=torch.int32, device="cuda")
+    run(x, 0.09, causal, left, right, tile_log=log)
+    assert ",seq-major" in ea.mfa_last_dispatch()["kernel"]
+    log = log.view(len(lq), Hq, nqt, 4).cpu().numpy()
+    for b in range(len(lq)):
+        ref = oracle.visited_tiles(lq[b], lk[b], BM, BN, causal, left, right) if lq[b] else []
+        for t in range(nqt):
+            tiles = ref[t] if t < len(ref) else []
+            want = (tiles[0], len(tiles), tiles[-1] + 1) if tiles else (-1, 0, -1)
+            got = log[b, :, t]
+            assert np.all(got[:, 0] == want[0]) and np.all(got[:, 1] == want[1]), (b, t, got, want)
+            assert np.all(got[:, 3] == want[2]), (b, t, got, want)
+
+
+def test_sequence_major_limits():
+    # more than 64 sequences, or Hkv not a multiple of 8: the round order
+    for Hq, Hkv, B in ((8, 8, 65), (8, 4, 10)):
+        x = A.varlen_inputs(Hq, Hkv, 64, "f16", 70 + B, seqlens_q=[33] * B, seqlens_k=[40] * B)
+        O, L = run(x, 0.125, True)
+        assert ",seq-major" not in ea.mfa_last_dispatch()["kernel"]
+        Or, Lr = oracle_of(x, 0.125, True)
+        T = in_seq_tokens(x)
+        assert_close_o(to_f64(O, "f16")[:T], Or[:T], "f16", f"B={B} Hkv={Hkv}")
+        assert_close_lse(L.cpu().numpy()[:, :T], Lr[:, :T], f"B={B} Hkv={Hkv}")

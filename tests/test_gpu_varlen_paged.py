@@ -79,6 +79,8 @@ def test_paged_packs_match_oracle(case):
     el = assert_close_lse(L.cpu().numpy(), Lr, str(case))
     info = ea.mfa_last_dispatch()
     assert info["op"] == 4 and ",varlen,paged" in info["kernel"]
+    # (at most 64 sequences and Hkv a multiple of 8: sequence-major order)
+    assert (",seq-major" in info["kernel"]) == (Hkv % 8 == 0 and len(lq) <= 64), info["kernel"]
     print(f"paged {case}: max|dO|={eo:.2e} max|dLSE|={el:.2e} {info['kernel']}")
 
 
