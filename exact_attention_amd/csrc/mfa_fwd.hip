@@ -258,6 +258,18 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
             }
         }
         if (!have) return;   // past the XCD's last item (uniform)
+    } else if (!VAR && !PAIR && GROUPS == 1 && a.seqmajor) {
+        // head-major order per XCD (dense layout): XCD x takes KV heads x, x + 8, ...; for
+        // each batch element it runs each KV head's query tiles longest first, the g query
+        // heads of a tile side by side
+        const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+        const int per_kv = a.g * a.n_q_tiles;
+        const int per_b = (a.Hkv >> 3) * per_kv;
+        b = k / per_b;
+        const int r1 = k - b * per_b;
+        const int mi = r1 / per_kv, r2 = r1 - mi * per_kv;
+        qt = a.n_q_tiles - 1 - r2 / a.g;
+        h = (x + 8 * mi) * a.g + r2 % a.g;
     } else if (a.xcd_group) {
         // consecutive workgroups go to different XCDs (id % 8); keep every query head
         // of one (batch, KV head) on the same XCD so its K/V stay in that L2
@@ -976,7 +988,7 @@ int launch(const FwdArgs& a, hipStream_t stream, int groups, bool tilelog, bool 
              DT == MFA_DT_F16 ? "f16" : "bf16", kBM, kBN, groups,
              MODE == 3 ? ",ext" : MODE == 2 ? ",varlen,paged" : MODE == 1 ? ",varlen" : "",
              tilelog ? ",tilelog" : "", neg ? ",neg" : "",
-             a.chain ? ",chained" : a.pair ? ",head-pairs" : a.seqmajor ? ",seq-major" : "");
+             a.chain ? ",chained" : a.pair ? ",head-pairs" : !a.seqmajor ? "" : (MODE == 1 || MODE == 2) ? ",seq-major" : ",head-major");
     info->BM = kBM;
     info->BN = kBN;
     info->waves = groups * kGroupThreads / 64;
@@ -1081,11 +1093,15 @@ int mfa_fwd_launch(const MfaFwdProblem& pr, hipStream_t stream, mfa_dispatch_inf
         groups = 2;
         a.HB = pr.B * pr.Hq / 2;
     }
-    // packed sequences: sequence-major order per XCD when each XCD can own whole KV heads;
-    // the grid covers at most floor(total_q / BM) + B query tiles per (head) and the
-    // workgroups past an XCD's last item exit at once
-    a.seqmajor = (var && mode != 3 && pr.B <= 64 && pr.Hkv % 8 == 0) ? 1 : 0;
-    if (a.seqmajor)
+    // Each XCD owns whole KV heads when Hkv is a multiple of 8.  Packed sequences (at most
+    // 64) then run in sequence-major order per XCD; the grid covers at most
+    // floor(total_q / BM) + B query tiles per head, and the workgroups past an XCD's last
+    // item exit at once.  Dense layouts with one 4-wave group per workgroup run in
+    // head-major order per XCD (same grid).  Both keep the workgroups that stream one K/V
+    // through an XCD's L2 running together.
+    a.seqmajor = (pr.Hkv % 8 == 0 && ((var && mode != 3 && pr.B <= 64) ||
+                                      (!var && groups == 1 && !a.pair))) ? 1 : 0;
+    if (a.seqmajor && var)
         a.grid = 8 * (pr.Hkv / 8) * a.g * (pr.total_q / kBM + pr.B);
     else
         a.grid = (a.chain ? a.n_rounds / 2 : a.n_rounds) * a.HB;

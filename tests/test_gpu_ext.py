@@ -93,6 +93,9 @@ BLOCK_CASES = [
     (2, 2, 2, 700, 700, 64, "bf16", False, -1, -1, 64, 64, 0.4, False),
     (1, 2, 1, 333, 900, 128, "bf16", True, -1, -1, 32, 64, 0.6, True),
     (1, 4, 4, 640, 640, 128, "f16", True, 200, 0, 128, 32, 0.7, True),
+    # more than two query tiles per CU with Hkv a multiple of 8: head-major order per XCD
+    (1, 64, 16, 1100, 1100, 128, "f16", True, -1, -1, 128, 128, 0.3, True),
+    (1, 48, 48, 1500, 1500, 64, "bf16", True, 200, 0, 64, 32, 0.5, False),
 ]
 
 
@@ -120,6 +123,9 @@ def test_block_sparse(c):
     log = torch.full((B * Hq * nqt * 4,), -7, dtype=torch.int32, device="cuda")
     eo, el, _, _ = case(B, Hq, Hkv, Nq, Nk, D, dt, 50 + Nq, causal, left, right, bmask=bm, bq=bq,
                         bk=bk, tile_log=log)
+    kern = ea.mfa_last_dispatch()["kernel"]
+    one_group = B * Hq * nqt > 2 * 256
+    assert (",head-major" in kern) == (one_group and Hkv % 8 == 0), kern
     log = log.view(B, Hq, nqt, 4).cpu().numpy()
     for b in range(B):
         for h in range(Hq):

@@ -257,6 +257,8 @@ def test_head_pairs(case):
     O, L = run(q, k, v, scale, causal, left, right)
     kern = ea.mfa_last_dispatch()["kernel"]
     assert (",head-pairs" in kern) == pairs and ("groups=2" in kern) == pairs, kern
+    # (one 4-wave group with Hkv a multiple of 8: head-major order per XCD)
+    assert (",head-major" in kern) == (not pairs and Hkv % 8 == 0), kern
     # both heads of the first and the last pair, and one pair in the middle
     g = Hq // Hkv
     heads = sorted({0, 1, Hq // 2, Hq // 2 + 1, Hq - 2, Hq - 1})
