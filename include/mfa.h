@@ -92,8 +92,10 @@ typedef struct {
     int waves;            /* wavefronts (64 lanes) per wave group: one group covers the
                              BM query rows of a tile.  mfa_fwd runs one or two groups per
                              workgroup, chosen at launch from the grid size (with two, the
-                             groups split the tile's key range); mfa_last_dispatch reports
-                             the workgroup actually launched */
+                             groups split the tile's key range, or on large dense GQA
+                             grids take the same tile of two query heads that share a KV
+                             head); mfa_last_dispatch reports the workgroup actually
+                             launched */
     int n_q_tiles;        /* ceil(Nq / BM) */
     int n_k_tiles;        /* ceil(Nk / BN) */
     long long visited;    /* key tiles visited, summed over the query tiles */
@@ -367,7 +369,11 @@ int mfa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pag
 /* What the last successful launch on this host thread ran (MXFlashAttn's per-dispatch
  * record: backend, operation, selection and split fields). */
 typedef struct {
-    char kernel[96];      /* kernel name of the main launch */
+    char kernel[96];      /* kernel name of the main launch; forward names end with the
+                             workgroup layout and order: groups=1|2, then ",chained"
+                             (two complementary query tiles per workgroup), ",head-pairs",
+                             ",seq-major" (packed sequences) or ",head-major" (dense),
+                             when taken */
     int op;               /* 1 = forward, 2 = paged decode, 3 = packed varlen forward,
                              4 = packed queries over a paged cache, 5 = multi-token decode,
                              6 = forward with modifiers / block mask, 7 = backward */
