@@ -269,3 +269,115 @@ def test_random_forward_many_heads(i):
     idx = tuple(np.array(rows).T)
     assert_close_o(to_f64(O, dtype)[idx], Or, dtype, "O", ref_pabs=Oa)
     assert_close_lse(L.cpu().numpy()[idx], Lr, "LSE")
+
+
+# Workgroup orders that pin KV heads to XCDs (Hkv a multiple of 8): sequence-major for
+# packed and paged sequences, head-major for dense layouts with one 4-wave group.
+def draw_xcd_heads(rng, gs=(1, 2, 3)):
+    D = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    Hkv = int(rng.choice([8, 16]))
+    return D, dtype, Hkv * int(rng.choice(gs)), Hkv
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_varlen_seq_major(i):
+    rng = np.random.default_rng(9100 + i)
+    D, dtype, Hq, Hkv = draw_xcd_heads(rng)
+    B = int(rng.integers(1, 25))
+    lq = rng.integers(0, 300, size=B)
+    lk = lq + (rng.integers(0, 300, size=B) if rng.random() < 0.5 else 0)
+    causal, left, right, scale = draw_mask(rng, D)
+    print(f"mfa_fwd_varlen (seq-major) B={B} Hq={Hq} Hkv={Hkv} D={D} {dtype} lq={lq.tolist()} "
+          f"lk={lk.tolist()} causal={causal} win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.varlen_inputs(Hq, Hkv, D, dtype, 9200 + i, seqlens_q=lq, seqlens_k=lk)
+    if x.q.shape[0] == 0 or x.k.shape[0] == 0:
+        pytest.skip("drew no tokens")
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    O, L = ea.mfa_fwd_varlen(q, k, v, dev_i32(x.cu_seqlens_q), dev_i32(x.cu_seqlens_k),
+                             int(max(1, lq.max())), int(max(1, lk.max())), scale=scale,
+                             causal=causal, win_left=left, win_right=right)
+    sync()
+    assert ",seq-major" in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (x.q, x.k, x.v))
+    Or, Lr = oracle.attention_varlen(qf, kf, vf, x.cu_seqlens_q, x.cu_seqlens_k, scale, causal,
+                                     left, right)
+    Oa, _ = oracle.attention_varlen(qf, kf, np.abs(vf), x.cu_seqlens_q, x.cu_seqlens_k, scale, causal,
+                                    left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "varlen O", ref_pabs=Oa)
+    assert_close_lse(L.cpu().numpy(), Lr, "varlen LSE")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_paged_seq_major(i):
+    rng = np.random.default_rng(9300 + i)
+    D, dtype, Hq, Hkv = draw_xcd_heads(rng)
+    B = int(rng.integers(1, 17))
+    lq = rng.integers(1, 200, size=B)
+    ctx = rng.integers(0, 800, size=B)
+    causal, left, right, scale = draw_mask(rng, D)
+    causal = True if rng.random() < 0.7 else causal
+    print(f"mfa_fwd_varlen_paged (seq-major) B={B} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
+          f"lq={lq.tolist()} ctx={ctx.tolist()} causal={causal} win=({left},{right}) "
+          f"scale={scale:.4f}", flush=True)
+    p = A.paged_varlen_inputs(Hq, Hkv, D, dtype, 9400 + i, seqlens_q=lq, ctx_lens=ctx,
+                              extra_pages=int(rng.integers(0, 4)))
+    O, L = ea.mfa_fwd_varlen_paged(to_dev(p.q, dtype), to_dev(p.k_pages, dtype), to_dev(p.v_pages, dtype),
+                                   dev_i32(p.block_table), dev_i32(p.seq_lens_k),
+                                   dev_i32(p.cu_seqlens_q), int(lq.max()), int(p.seq_lens_k.max()),
+                                   scale=scale, causal=causal, win_left=left, win_right=right)
+    sync()
+    assert ",seq-major" in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
+    qf, kf, vf = (oracle.widen(t, dtype) for t in (p.q, p.k_pages, p.v_pages))
+    Or, Lr = oracle.attention_varlen_paged(qf, kf, vf, p.block_table, p.seq_lens_k, p.cu_seqlens_q,
+                                           scale, p.page_size, causal, left, right)
+    Oa, _ = oracle.attention_varlen_paged(qf, kf, np.abs(vf), p.block_table, p.seq_lens_k,
+                                          p.cu_seqlens_q, scale, p.page_size, causal, left, right)
+    assert_close_o(to_f64(O, dtype), Or, dtype, "paged prefill O", ref_pabs=Oa)
+    assert_close_lse(L.cpu().numpy(), Lr, "paged prefill LSE")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_head_major(i):
+    # dense layouts with one 4-wave group (odd group sizes, more than two query tiles per
+    # CU), with score modifiers and a block mask on every other draw; four heads checked
+    rng = np.random.default_rng(9500 + i)
+    D, dtype, Hq, Hkv = draw_xcd_heads(rng, gs=(1, 3))
+    B = int(rng.integers(1, 3))
+    tiles = 512 // (B * Hq) + 1
+    Nq = int(rng.integers(128 * tiles - 100, 128 * tiles + 300))
+    Nk = Nq if rng.random() < 0.6 else int(rng.integers(max(1, Nq // 2), Nq + 400))
+    causal, left, right, scale = draw_mask(rng, D)
+    ext = i % 2 == 1
+    print(f"{'mfa_fwd_ext' if ext else 'mfa_fwd'} (head-major) B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} "
+          f"Nk={Nk} D={D} {dtype} causal={causal} win=({left},{right}) scale={scale:.4f}", flush=True)
+    x = A.dense_inputs(B, Hq, Hkv, Nq, Nk, D, dtype, 9600 + i)
+    q, k, v = (to_dev(t, dtype) for t in (x.q, x.k, x.v))
+    kw = {}
+    if ext:
+        bq, bk = 64, 64
+        bm = (rng.random((B, Hq, math.ceil(Nq / bq), math.ceil(Nk / bk))) < 0.5).astype(np.uint8)
+        kw = dict(softcap=float(rng.uniform(5, 40)), block_mask=bm, block_q=bq, block_k=bk)
+        O, L = ea.mfa_fwd_ext(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right,
+                              softcap=kw["softcap"], block_mask=dev_u8(bm), block_q=bq, block_k=bk)
+    else:
+        O, L = ea.mfa_fwd(q, k, v, scale=scale, causal=causal, win_left=left, win_right=right)
+    sync()
+    assert ",head-major" in ea.mfa_last_dispatch()["kernel"], ea.mfa_last_dispatch()["kernel"]
+    g = Hq // Hkv
+    heads = sorted({0, Hq - 1} | {int(h) for h in rng.integers(0, Hq, 2)})
+    for b in range(B):
+        for h in heads:
+            qf = oracle.widen(x.q[b:b + 1, h:h + 1], dtype)
+            kf, vf = (oracle.widen(t[b:b + 1, h // g:h // g + 1], dtype) for t in (x.k, x.v))
+            if ext:
+                bmh = kw["block_mask"][b:b + 1, h:h + 1]
+                Or, Lr = oracle.attention_ext(qf, kf, vf, scale, causal, left, right,
+                                              softcap=kw["softcap"], block_mask=bmh, block_q=64, block_k=64)
+                Oa, _ = oracle.attention_ext(qf, kf, np.abs(vf), scale, causal, left, right,
+                                             softcap=kw["softcap"], block_mask=bmh, block_q=64, block_k=64)
+            else:
+                Or, Lr = oracle.attention(qf, kf, vf, scale, causal, left, right)
+                Oa, _ = oracle.attention(qf, kf, np.abs(vf), scale, causal, left, right)
+            assert_close_o(to_f64(O[b:b + 1, h:h + 1], dtype), Or, dtype, f"O b={b} h={h}", ref_pabs=Oa)
+            assert_close_lse(L[b:b + 1, h:h + 1].cpu().numpy(), Lr, f"LSE b={b} h={h}")
