@@ -16,10 +16,15 @@
 //   the tile's visited key range in halves, run concurrently (two waves per SIMD) and
 //   merge their (O, m, l) through LDS at the end; for dense inputs with an even number
 //   of query tiles such a workgroup then runs a second, complementary tile (T - 1 - r
-//   after r), so every workgroup has the same causal work.  Key tiles of BN = 64 keys
+//   after r), so every workgroup has the same causal work.  Large dense GQA grids with an
+//   even group size use 8-wave workgroups too, whose two groups take the same tile of two
+//   query heads that share a KV head, over one K/V stream.  Key tiles of BN = 64 keys
 //   stream through LDS: K and V tiles are copied global -> LDS directly (buffer loads
 //   with the LDS bit; the range check returns zeros past the last key row),
-//   double-buffered per group.
+//   double-buffered per group.  Workgroups are ordered so that those reading one KV
+//   head's K/V run on one XCD and share its L2: the query heads of a KV head on one XCD,
+//   and with Hkv a multiple of 8 whole KV heads per XCD, run head by head (dense layouts)
+//   or sequence by sequence (packed sequences).  O leaves through LDS as whole rows.
 //
 // Per wave and key tile (32x32x16 MFMA, fp32 accumulate):
 //   S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T held in registers for the whole
