@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mfa_bwd_dq_kernel(BwdArgs a) {
     const bool qvalid = qrow < a.Nq;
     const float lraw = qvalid ? a.lse[(size_t)bh * a.Nq + qrow] : -MFA_INF;
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    const float dvv = dpart + mfa_swap_halves(dpart);
+    const float dvv = mfa_pair_sum(dpart);
     const float lse2 = lraw == -MFA_INF ? MFA_INF : lraw * 1.4426950408889634f;
     if (qvalid && kh == 0 && g32 == 0) {
         a.dvec[(size_t)bh * a.Nq + qrow] = dvv;

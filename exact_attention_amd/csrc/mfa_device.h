@@ -9,6 +9,7 @@ typedef float mfa_f32x16 __attribute__((ext_vector_type(16)));
 typedef float mfa_f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mfa_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mfa_u32x2 __attribute__((ext_vector_type(2)));
+typedef float mfa_f32x2 __attribute__((ext_vector_type(2)));
 
 #define MFA_DT_F16 0
 #define MFA_DT_BF16 1
@@ -134,9 +135,24 @@ __device__ __forceinline__ int32_t mfa_uniform_load(const int32_t* p) {
     return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
-// Value of x held by lane (lane ^ 32).
-__device__ __forceinline__ float mfa_swap_halves(float x) {
-    return __shfl_xor(x, 32, 64);
+// The two values of x held by lanes i and i + 32 (i = lane & 31), in that order, in every
+// lane: v_permlane32_swap exchanges the upper half of its first operand with the lower
+// half of its second, with no trip through LDS.  Written as inline asm because the
+// compiler's own folding of the builtin takes its two results for one value; the leading
+// s_nop covers the wait a permlane needs after a VALU write of its operands.
+__device__ __forceinline__ mfa_f32x2 mfa_halves(float x) {
+    float lo = x, hi = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+    return mfa_f32x2{lo, hi};
+}
+// Sum and maximum of x over the lane pair (i, i + 32); every lane gets the same bits.
+__device__ __forceinline__ float mfa_pair_sum(float x) {
+    const mfa_f32x2 h = mfa_halves(x);
+    return h[0] + h[1];
+}
+__device__ __forceinline__ float mfa_pair_max(float x) {
+    const mfa_f32x2 h = mfa_halves(x);
+    return fmaxf(h[0], h[1]);
 }
 
 // Value of x held by lane src (any lane of the wave).

@@ -742,7 +742,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, NEG ? -s_cur[nb][r] : s_cur[nb][r]);
-        tmax = fmaxf(tmax, mfa_swap_halves(tmax));
+        tmax = mfa_pair_max(tmax);
         const float tmax_s = (tmax == -MFA_INF) ? -MFA_INF : tmax * sl2;
         const bool raise = tmax_s > m_run + kLazy;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     }
 
     // ---- epilogue: O = o / l, LSE = (m + log2 l) * ln 2 --------------------------
-    const float l_tot = l_run + mfa_swap_halves(l_run);
+    const float l_tot = mfa_pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // O leaves through LDS: the wave writes its 32 x D block row-major (16-byte chunks
     // XOR-swizzled by row) into free tile memory, from where whole rows are stored.  The
