@@ -397,10 +397,16 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
     const int kt_lo = first ? t_lo : t_lo + n0;
     const int n = first ? n0 : n_all - n0;   // this group's tiles (n0 or n0 - 1)
     const int lbase = first ? 0 : n0;        // this group's first list entry
+    // list entry of this group's idx-th visited tile.  Block-sparse lists are walked from
+    // the diagonal down: the workgroups of a head that run together then sit at nearby key
+    // tiles all along (each starts at its own diagonal, one tile below the next), where
+    // from key 0 up the late starters re-read the head's first keys long after the L2 has
+    // dropped them.
+    auto list_at = [&](int idx) { return lbase + n - 1 - idx; };
     // key tile of this group's idx-th visited tile
     auto tile_at = [&](int idx) {
         if constexpr (MODE == 3) {
-            if (use_list) return __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + lbase + idx) & 0xfffff);
+            if (use_list) return __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + list_at(idx)) & 0xfffff);
         }
         return kt_lo + idx;
     };
@@ -688,7 +694,7 @@ __global__ __launch_bounds__(GROUPS * kGroupThreads, 2) void mfa_fwd_kernel(FwdA
         int kt_k = kt + 2, kt_v = kt + 1;
         if constexpr (MODE == 3) {
             if (use_list) {
-                ent = __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + lbase + j));
+                ent = __builtin_amdgcn_readfirstlane(lds_read_i32(tlist + list_at(j)));
                 kt = ent & 0xfffff;
                 kt_k = j + 2 < n ? tile_at(j + 2) : 0;
                 kt_v = j + 1 < n ? tile_at(j + 1) : 0;
