@@ -180,6 +180,23 @@ def setup_prefill(name):
     return step
 
 
+def prefill_bytes(c) -> int:
+    """Algorithmic bytes of a dense prefill: q, k, v and out once each (2 bytes per element)
+    and the fp32 LSE."""
+    rows_q = c["B"] * c["Hq"] * c["Nq"]
+    return 2 * c["D"] * (2 * rows_q + 2 * c["B"] * c["Hkv"] * c["Nk"]) + 4 * rows_q
+
+
+def roofline_model(flop, nbytes, tflops):
+    """The roofline at this workload's arithmetic intensity: attainable TFLOP/s is the lesser
+    of the MFMA peak and intensity x peak HBM bandwidth (ridge 312.5 FLOP/B)."""
+    inten = flop / nbytes
+    att = min(PEAK_MFMA_F16, inten * PEAK_HBM / 1e3)
+    return {"flop_per_byte": inten, "ridge_flop_per_byte": PEAK_MFMA_F16 * 1e3 / PEAK_HBM,
+            "bound": "mfma" if att >= PEAK_MFMA_F16 else "hbm", "attainable_tflops": att,
+            "frac_of_attainable": tflops / att}
+
+
 def bench_prefill(name, step, steps):
     import exact_attention_amd as ea
     c = A.workload(name)
@@ -197,6 +214,7 @@ def bench_prefill(name, step, steps):
         "roofline": {"bound": "mfma", "achieved": tk, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": tk / PEAK_MFMA_F16,
                      "traffic": measured_traffic(name, "fwd")},
+        "roofline_model": roofline_model(flop, prefill_bytes(c), tk),
         "kernel": info["kernel"], "grid": info["grid"], "planned_tiles": info["planned"],
         "dtype": c["dtype"],
     }
