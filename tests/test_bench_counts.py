@@ -32,3 +32,18 @@ def test_decode_bytes_counts_every_cached_token_once():
     L = p.seq_lens.astype(np.int64)
     expect = int(L.sum()) * 2 * 64 * 2 * 2 + 2 * 3 * 8 * 64 * 2 + 3 * 8 * 4 + 4 * int(np.ceil(L / 16).sum()) + 12
     assert bench.decode_bytes(p, 2, 64, 8) == expect
+
+
+def test_prefill_bytes_and_roofline_model():
+    # bytes of the seeded arrays themselves: q, k, v, out (2 bytes per element) and fp32 LSE
+    c = dict(B=1, Hq=4, Hkv=2, Nq=96, Nk=160, D=64)
+    x = A.dense_inputs(c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"], "f16", 5)
+    expect = x.q.nbytes * 2 + x.k.nbytes + x.v.nbytes + c["B"] * c["Hq"] * c["Nq"] * 4
+    assert bench.prefill_bytes(c) == expect
+    # below the ridge the attainable rate is intensity x bandwidth, above it the MFMA peak
+    lo = bench.roofline_model(flop=100e9, nbytes=1e9, tflops=200.0)
+    assert lo["bound"] == "hbm" and abs(lo["attainable_tflops"] - 800.0) < 1e-9
+    assert abs(lo["frac_of_attainable"] - 0.25) < 1e-12
+    hi = bench.roofline_model(flop=1000e9, nbytes=1e9, tflops=500.0)
+    assert hi["bound"] == "mfma" and hi["attainable_tflops"] == bench.PEAK_MFMA_F16
+    assert abs(hi["frac_of_attainable"] - 0.2) < 1e-12
