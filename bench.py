@@ -24,7 +24,9 @@ call between its own pair of events; ``torch.cuda.synchronize()`` on both
 sides of each timed region.  ``ms_per_step`` and ``value`` cover the block of K calls
 (launch gaps included); the mean, median and min of the per-call event times are reported
 beside it, and ``roofline.achieved`` divides the algorithmic work by the mean per-call
-time (the kernel's average launch duration).
+time (the kernel's average launch duration).  The dense-layout prefill entries also
+carry ``roofline_model``: FLOP per algorithmic byte, the attainable TFLOP/s at that
+intensity (the lesser of the MFMA peak and intensity x 8 TB/s) and the fraction reached.
 ``cpu_baseline`` times the float64 CPU oracle on this host over whole heads of the
 same prefill workload, for about 10 s, scales to TFLOP/s, names the CPU model, and
 reports the max-abs difference between the GPU's O and LSE and the oracle's on those
