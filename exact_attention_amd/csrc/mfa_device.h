@@ -121,12 +121,6 @@ __device__ __forceinline__ mfa_u32x2 mfa_lds_read_tr16(const void* p) {
     return __builtin_bit_cast(mfa_u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<void*>(p))));
 }
 
-__device__ __forceinline__ uint32_t mfa_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ mfa_u32x2 mfa_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(mfa_u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
 __device__ __forceinline__ float mfa_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Wave-uniform read of an int32 the kernel never writes, through the scalar data cache
@@ -153,37 +147,4 @@ __device__ __forceinline__ float mfa_pair_sum(float x) {
 __device__ __forceinline__ float mfa_pair_max(float x) {
     const mfa_f32x2 h = mfa_halves(x);
     return fmaxf(h[0], h[1]);
-}
-
-// Value of x held by lane src (any lane of the wave).
-__device__ __forceinline__ float mfa_lane(float x, int src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
-}
-
-// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r + 15); every lane of the
-// row receives the result.
-__device__ __forceinline__ float mfa_dpp_f(float x, int ctrl_sel) {
-    int v = __builtin_bit_cast(int, x);
-    int r;
-    switch (ctrl_sel) {
-        case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false); break;  // row_ror:8
-        case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false); break;  // row_ror:4
-        case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false); break;   // quad_perm 2,3,0,1
-        default: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false); break;  // quad_perm 1,0,3,2
-    }
-    return __builtin_bit_cast(float, r);
-}
-__device__ __forceinline__ float mfa_row16_sum(float x) {
-    x += mfa_dpp_f(x, 0);
-    x += mfa_dpp_f(x, 1);
-    x += mfa_dpp_f(x, 2);
-    x += mfa_dpp_f(x, 3);
-    return x;
-}
-__device__ __forceinline__ float mfa_row16_max(float x) {
-    x = fmaxf(x, mfa_dpp_f(x, 0));
-    x = fmaxf(x, mfa_dpp_f(x, 1));
-    x = fmaxf(x, mfa_dpp_f(x, 2));
-    x = fmaxf(x, mfa_dpp_f(x, 3));
-    return x;
 }

@@ -22,14 +22,10 @@ __device__ __forceinline__ int key_perm(int i) {
 // XOR swizzles on the 16-byte chunks of an LDS tile with KCH chunks per row (rows are not
 // padded, so that a wave's direct load fills 1 KiB of consecutive LDS).  Row reads: the
 // 16 rows one MFMA operand read touches at a logical chunk land in 16 distinct bank
-// groups.  Transposing reads: the 4 rows x 32 bytes of one read land in distinct banks.
+// groups.
 template <int KCH>
 __device__ __forceinline__ int swz_rows(int row, int ch) {
     return (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
-}
-template <int KCH>
-__device__ __forceinline__ int swz_tr(int row, int ch) {
-    return (KCH == 16) ? (ch ^ ((row & 3) << 1)) : (ch ^ (((row >> 1) & 1) << 1));
 }
 
 // A layout for tiles read both ways, and for transposing reads by 32 lanes at once:
@@ -39,8 +35,8 @@ __device__ __forceinline__ int swz_tr(int row, int ch) {
 // chunk bits above bit 1.  With 16 chunks a row (a row spans the 64 banks)
 // x(r) = ((r & 3) << 2) | ((r >> 2) & 3) meets both; with 8 chunks (two rows per 64 banks)
 // x = h((r >> 1) & 7), h(s) = ((s & 1) << 2) | (s >> 1).  (swz_rows puts rows 4k and
-// 4k + 1 of a transposing read on the same banks; swz_tr separates them within 16 lanes
-// but not across 32.)  x depends on row % 16 only.  Between a transposing read and the
+// 4k + 1 of a transposing read on the same banks; XOR-ing the chunk with (r & 3) << 1
+// separates them within 16 lanes but not across 32.)  x depends on row % 16 only.  Between a transposing read and the
 // one 4 rows below it the layout flips chunk bit 0, so the second read is
 // tr4_delta elements further, by the lane's chunk parity.
 template <int KCH>
